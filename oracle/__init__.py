@@ -1,0 +1,28 @@
+"""CPU oracle for paged decode attention and its two cache kernels.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
+package. The product path (``paged_kv_cache_165_amd``) never imports it, and
+this package imports nothing from the product path: the two share no code.
+
+Everything here is plain numpy in float64 and follows the definitions on the
+pages cited in ``paged_attention.py``. See that module's header for the list of
+pinned and unpinned functions.
+"""
+
+from .paged_attention import (  # noqa: F401
+    BF16,
+    F16,
+    F32,
+    block_layout,
+    translate,
+    gather_rows,
+    attend_contiguous,
+    paged_decode,
+    partition_stats,
+    lse_merge,
+    paged_decode_partitioned,
+    write_cache,
+    copy_blocks,
+    to_float64,
+)
