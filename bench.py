@@ -1,0 +1,204 @@
+"""Paged decode attention benchmark on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the copy-on-write block copies (if the workload has any), the cache writes of
+the step's new tokens, then paged decode (partition kernel + log-sum-exp
+merge). Inputs are resident in HBM before the timed region starts.
+
+Prints ONE JSON line. `value` is K+V GB/s: the algorithmic bytes one decode
+must read (2 * ctx * Hkv * D * element size, summed over the batch) divided
+by the measured time per step. `roofline` reports the partition kernel alone
+(its average duration from HIP events recorded around it on the launch stream
+in every timed step) against the 8 TB/s MI355X HBM peak. `cpu_baseline` is the
+float64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "paged decode attention: KV GB/s read (% of HBM peak), seqs/sec"
+HBM_PEAK_GBS = 8000.0
+
+
+def progress(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa8b",
+                    choices=["tiny", "layout", "mha7b", "gqa8b", "prefix", "long"])
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target duration of the CPU oracle sample")
+    ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "profiles", "traffic.json"),
+                    help="counter-derived HBM bytes per partition-kernel launch, if measured")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q_h, kc_h, vc_h, seconds: float):
+    """Time the oracle on the first sequences of the batch until about
+    `seconds` of CPU work has been done; single BLAS thread."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover - threadpoolctl is installed on this image
+        limiter = None
+    dt = {"f32": oracle.F32, "bf16": oracle.BF16}[w.dtype]
+    done, t_used, kv = 0, 0.0, 0
+    e = 4 if w.dtype == "f32" else 2
+    t0 = time.perf_counter()
+    while done < w.num_seqs and t_used < seconds:
+        i = done
+        ts = time.perf_counter()
+        oracle.paged_decode(q_h[i:i + 1], kc_h, vc_h, w.block_tables[i:i + 1], w.context_lens[i:i + 1],
+                            w.scale, w.block_size, dt)
+        t_used += time.perf_counter() - ts
+        kv += 2 * int(w.context_lens[i]) * w.num_kv_heads * w.head_dim * e
+        done += 1
+    wall = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.restore_original_limits()
+    return {
+        "value": round(kv / t_used / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "seqs_per_s": round(done / t_used, 3),
+        "sample": f"first {done} of {w.num_seqs} sequences of {w.name} ({kv / 1e6:.1f} MB of K+V), "
+                  f"float64 numpy oracle, 1 BLAS thread, {wall:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    progress("importing torch")
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_165_amd as pa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    lib = pa.library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    progress(f"device {torch.cuda.get_device_name(dev)}; building workload {args.workload}")
+    w = W.build(args.workload)
+    if args.partition_size:
+        w.partition_size = args.partition_size
+    vals = W.make_values(w, device=dev, poison=True)
+    q, kc, vc = vals["q"], vals["k_cache"], vals["v_cache"]
+    tables = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    pairs = torch.from_numpy(w.cow_pairs.astype(np.int32)).to(dev)
+    slots = [torch.from_numpy(op.slots.astype(np.int32)).to(dev) for op in w.writes]
+    out = torch.empty_like(q)
+    ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.head_dim, w.max_context_len, w.partition_size,
+                            device=dev)
+    dargs = (out, q, kc, vc, tables, lens, w.scale, w.max_context_len, w.partition_size, ws)
+
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(i=None):
+        if len(w.cow_pairs):
+            pa.copy_blocks(kc, vc, pairs)
+        for sl, (k, v) in zip(slots, vals["writes"]):
+            pa.write_cache(k, v, kc, vc, sl)
+        if i is not None:
+            ev_a[i].record()
+        pa.decode_partitions(*dargs)
+        if i is not None:
+            ev_b[i].record()
+        pa.decode_merge(*dargs)
+
+    progress(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    progress(f"timing {args.steps} steps")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+    part_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
+    part_us = 1e3 * float(np.mean(part_ms))
+    part_us_med = 1e3 * float(np.median(part_ms))
+    kv = w.kv_bytes()
+    value = kv / (ms_step * 1e-3) / 1e9
+    achieved = kv / (part_us * 1e-6) / 1e9
+    progress(f"step {ms_step * 1e3:.1f} us, partition kernel mean {part_us:.1f} us (median {part_us_med:.1f})")
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                tj = json.load(f).get(w.name)
+            if tj:
+                traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        progress("cpu baseline (oracle) on a bounded sample")
+
+        def host(t):
+            t = t.detach().cpu().contiguous()
+            return t.view(torch.uint16).numpy() if t.dtype == torch.bfloat16 else t.numpy()
+
+        cpu = cpu_baseline(w, host(q), host(kc), host(vc), args.cpu_seconds)
+        progress(f"cpu baseline: {cpu}")
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "partition_size": w.partition_size, "ctx": w.ctx_recipe, "tokens": int(w.context_lens.sum()),
+                   "kv_bytes": kv, "seed": w.seed, "parallelism": "none (1 GPU)"},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "wall_ms_per_step": round(1e3 * t_wall / args.steps, 5),
+        "roofline": {"bound": "hbm", "kernel": "pa_partition_valu", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel_us_mean": round(part_us, 2),
+                     "kernel_us_median": round(part_us_med, 2), "bytes_per_launch": kv},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

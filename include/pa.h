@@ -1,0 +1,185 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged KV-cache decode library.
+ *
+ * Three device operations, each enqueued on the caller's HIP stream:
+ *   pa_decode       single-query attention of every sequence over its KV
+ *                   cache, read through its block table;
+ *   pa_write_cache  write each new token's K and V rows into the slot given by
+ *                   a slot mapping;
+ *   pa_copy_blocks  whole-block copies, the copy half of copy-on-write.
+ *
+ * Pages the operations are defined by (cited below by short name):
+ *   [aiqz]     aiqz.cc/article/paged-attention-mechanism.html (PagedAttention
+ *              tutorial: block table equation, prefix sharing, copy-on-write)
+ *   [lihaoran] lihaoran.work/auto-20261007-1900 (mechanism note: the
+ *              [5, 1, 7] example, tail-slot count)
+ *   [cf-1]     cf-1.com/news/5879632 (engineering blog: block table in shared
+ *              memory, prefetch, copy-on-write steps)
+ *   [ipipp]    ipipp.com/html/20260817/41684.html ("PagedAttention原理是什么？")
+ *
+ * Memory layout (all arrays dense, row-major, in device memory owned by the
+ * caller; the library never allocates, frees or synchronizes):
+ *   k_cache, v_cache  [num_blocks][num_kv_heads][block_size][head_dim]  elements of `dtype`
+ *   q, out            [num_seqs][num_heads][head_dim]                   elements of `dtype`
+ *   k, v (new tokens) [num_tokens][num_kv_heads][head_dim]              elements of `dtype`
+ *   block_tables      int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens      int32 [num_seqs]
+ *   slot_mapping      int32 [num_tokens]; slot = physical_block * block_size + offset
+ *   src_dst_pairs     int32 [num_pairs][2]
+ * Every data pointer must be 16-byte aligned. `stream` is a hipStream_t
+ * (NULL = the null stream) passed as void* so this header needs no HIP header.
+ *
+ * Errors: every check below is made on the host before anything is launched;
+ * a failing call launches nothing and returns a status, and pa_last_error()
+ * gives a message for the calling thread. A launch failure returns
+ * PA_ERR_HIP. Index contents live in device memory and are not checked on the
+ * host; the kernels clamp what they read so that a bad index can never make
+ * them touch memory outside the arrays (see each call).
+ *
+ * Thread safety: the library keeps no state besides a per-device cache of the
+ * compute-unit count and kernel occupancy, filled under a lock. Calls that
+ * share a workspace must not overlap.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_dtype {
+    PA_F32 = 0,  /* IEEE binary32 */
+    PA_BF16 = 1, /* bfloat16 */
+    PA_F16 = 2   /* IEEE binary16 */
+} pa_dtype_t;
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size, misalignment */
+    PA_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for */
+    PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than pa_decode_workspace_size */
+    PA_ERR_HIP = 4          /* the HIP runtime reported an error */
+} pa_status_t;
+
+/* ABI version of the loaded library (PA_ABI_VERSION it was built with). */
+int pa_abi_version(void);
+
+/* Static description of a status code. */
+const char* pa_status_string(pa_status_t status);
+
+/* Message of the last failed call on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * Tokens per context partition when the caller passes partition_size = 0.
+ */
+int pa_default_partition_size(void);
+
+/*
+ * Bytes of device workspace pa_decode needs: per sequence, per query head and
+ * per context partition one (max, sum, output row) record in float32. Returns
+ * 0 for invalid arguments. partition_size = 0 selects the default.
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
+                                int max_context_len, int partition_size);
+
+/*
+ * Paged decode attention.
+ *
+ * For sequence s with L = context_lens[s] and query head h (KV head
+ * kv = h / (num_heads / num_kv_heads)), token t in [0, L) lives at physical
+ * block pid = block_tables[s][t / block_size], offset off = t % block_size
+ * ([aiqz] section 块表映射机制, equation pid/off; [lihaoran] section
+ * 块表把逻辑顺序映射到物理位置). With x_t = scale * <q[s][h], k_cache[pid][kv][off]>,
+ *     out[s][h] = sum_t exp(x_t - max x) v_cache[pid][kv][off] / sum_t exp(x_t - max x),
+ * i.e. ordinary softmax attention over all L visible tokens: the paging
+ * changes where the rows live, not the value ([aiqz] 常见误区; [ipipp]
+ * 分页式KV缓存的底层设计). L = 0 gives a zero row. Slots at or past L in the
+ * last block and table entries past ceil(L / block_size) are never read.
+ * Arithmetic is float32; out is rounded to `dtype` (round to nearest even).
+ *
+ * The context is split into partitions of partition_size tokens that are
+ * reduced separately and merged by log-sum-exp; the split changes rounding
+ * only. A sequence with a single partition is written directly.
+ *
+ * Arguments: num_heads must be a multiple of num_kv_heads; num_heads /
+ * num_kv_heads must be 1, 2, 4 or 8; head_dim 64, 128 or 256; block_size a
+ * power of two from 4 to 256 and at least 1024 / (head_dim * sizeof(dtype));
+ * partition_size (0 = default) a multiple of 16 and of block_size with
+ * partition_size / block_size <= 256; num_seqs <= 8192;
+ * max_blocks_per_seq * block_size >= max_context_len. workspace must hold
+ * pa_decode_workspace_size(...) bytes for the same arguments.
+ * max_context_len must be >= every context_lens[s]; a longer sequence is
+ * clamped to max_context_len tokens. Table entries outside [0, num_blocks)
+ * are clamped into that range (wrong values, no fault). q/out must not alias.
+ */
+pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int block_size, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                      int num_blocks, int max_blocks_per_seq, int max_context_len,
+                      int partition_size, pa_dtype_t dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * The two stages pa_decode runs, exposed with the same arguments so a caller
+ * can time them apart: pa_decode == pa_decode_partitions then
+ * pa_decode_merge on the same stream. The merge combines per-partition
+ * records (m_p, l_p, o_p) of a sequence as M = max m_p, w_p = l_p e^(m_p - M),
+ * out = sum w_p o_p / sum w_p, and does nothing for single-partition
+ * sequences. Calling pa_decode_merge without a preceding
+ * pa_decode_partitions on the same workspace leaves `out` undefined.
+ */
+pa_status_t pa_decode_partitions(void* out, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, float scale, int block_size,
+                                 int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                 int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                 int partition_size, pa_dtype_t dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+pa_status_t pa_decode_merge(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            float scale, int block_size, int num_seqs, int num_heads,
+                            int num_kv_heads, int head_dim, int num_blocks,
+                            int max_blocks_per_seq, int max_context_len, int partition_size,
+                            pa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * Cache write: for every token i with 0 <= slot_mapping[i] < num_blocks *
+ * block_size, with pid = slot / block_size and off = slot % block_size,
+ *     k_cache[pid][kv][off][:] = k[i][kv][:]  and  v_cache[pid][kv][off][:] = v[i][kv][:]
+ * for every KV head kv -- the "write the new token" step of [aiqz] 前缀共享机制,
+ * addressed as in [aiqz] 块表映射机制. Elements are copied as raw bits (NaN
+ * payloads included). A negative slot skips the token; a slot past the pool
+ * is skipped too. Slots must be distinct (two tokens writing one slot leave
+ * either value). num_tokens = 0 is a no-op.
+ */
+pa_status_t pa_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                           const int32_t* slot_mapping, int num_tokens, int num_kv_heads,
+                           int head_dim, int block_size, int num_blocks, pa_dtype_t dtype,
+                           void* stream);
+
+/*
+ * Block copy: for every pair (src, dst) = src_dst_pairs[i], copy the whole
+ * block -- all KV heads, all block_size slots (stale ones too) -- of both
+ * caches: k_cache[dst] = k_cache[src], v_cache[dst] = v_cache[src], as raw
+ * bits. This is the copy of copy-on-write ([aiqz] 前缀共享机制: allocate, copy
+ * the old block, then write; [cf-1] 4.2). Pairs act as if applied at once:
+ * every dst must be distinct and no dst may also be a src (otherwise the
+ * result is unspecified). A pair with an id outside [0, num_blocks) is
+ * skipped. num_pairs = 0 is a no-op.
+ */
+pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
+                           int num_pairs, int num_kv_heads, int block_size, int head_dim,
+                           int num_blocks, pa_dtype_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,178 @@
+"""Paged KV-cache decode attention for MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libpa.so`` (include/pa.h). Every
+function checks tensor devices, dtypes, shapes and contiguity, then passes raw
+device pointers and the current torch stream to the library; all computation
+runs in the library's HIP kernels. PyTorch supplies device memory and
+streams only. There is no fallback path: a missing library raises.
+
+Layouts (see include/pa.h):
+  k_cache, v_cache  [num_blocks, num_kv_heads, block_size, head_dim]
+  q, out            [num_seqs, num_heads, head_dim]
+  k, v              [num_tokens, num_kv_heads, head_dim]
+  block_tables      int32 [num_seqs, max_blocks_per_seq]
+  context_lens      int32 [num_seqs]
+  slot_mapping      int32 [num_tokens]
+  src_dst_pairs     int32 [num_pairs, 2]
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "PaError", "library", "default_partition_size", "workspace_size", "alloc_workspace",
+    "decode", "decode_partitions", "decode_merge", "write_cache", "copy_blocks",
+]
+
+_DTYPES = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16, torch.float16: _lib.PA_F16}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"pa status {status}: {message}")
+
+
+def library() -> ctypes.CDLL:
+    return _lib.load()
+
+
+def _check(status: int) -> None:
+    if status != _lib.PA_OK:
+        lib = library()
+        raise PaError(status, f"{lib.pa_status_string(status).decode()}: {lib.pa_last_error().decode()}")
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtype=None, ndim=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def default_partition_size() -> int:
+    return int(library().pa_default_partition_size())
+
+
+def workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                   partition_size: int = 0) -> int:
+    return int(library().pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                                  partition_size))
+
+
+def alloc_workspace(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                    partition_size: int = 0, device="cuda") -> torch.Tensor:
+    """Caller-owned workspace tensor (uint8) for ``decode``."""
+    n = workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                 partition_size, workspace):
+    _dev_tensor(q, "q", ndim=3)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _dev_tensor(out, "out", dtype=q.dtype, ndim=3)
+    _dev_tensor(k_cache, "k_cache", dtype=q.dtype, ndim=4)
+    _dev_tensor(v_cache, "v_cache", dtype=q.dtype, ndim=4)
+    _dev_tensor(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev_tensor(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    s, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if tuple(out.shape) != (s, hq, d):
+        raise ValueError("out must have the shape of q")
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or d2 != d:
+        raise ValueError("k_cache and v_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    if block_tables.shape[0] != s or context_lens.shape[0] != s:
+        raise ValueError("one block table row and one context length per sequence")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if s else 0  # device -> host read
+    if workspace is None:
+        workspace = alloc_workspace(s, hq, d, max_context_len, partition_size, device=q.device)
+    else:
+        _dev_tensor(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), float(scale), bs, s, hq, hkv, d, nb,
+            block_tables.shape[1], int(max_context_len), int(partition_size), _DTYPES[q.dtype],
+            workspace.data_ptr(), ws_bytes, _stream(q))
+
+
+def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len=None,
+           partition_size=0, workspace=None):
+    """Paged decode attention into ``out`` (see ``pa_decode`` in include/pa.h).
+
+    ``max_context_len`` should be passed by callers that know it; when None it
+    is read from the device, which synchronizes the stream.
+    """
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                        max_context_len, partition_size, workspace)
+    _check(library().pa_decode(*args))
+    return out
+
+
+def decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      max_context_len, partition_size=0, workspace=None):
+    """First stage of ``decode`` (partition kernel) on the current stream."""
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                        max_context_len, partition_size, workspace)
+    _check(library().pa_decode_partitions(*args))
+
+
+def decode_merge(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                 partition_size=0, workspace=None):
+    """Second stage of ``decode`` (log-sum-exp merge) on the current stream."""
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                        max_context_len, partition_size, workspace)
+    _check(library().pa_decode_merge(*args))
+
+
+def write_cache(k, v, k_cache, v_cache, slot_mapping):
+    """Write new tokens' K/V rows into their slots (``pa_write_cache``)."""
+    _dev_tensor(k_cache, "k_cache", ndim=4)
+    if k_cache.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {k_cache.dtype}")
+    _dev_tensor(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+    _dev_tensor(k, "k", dtype=k_cache.dtype, ndim=3)
+    _dev_tensor(v, "v", dtype=k_cache.dtype, ndim=3)
+    _dev_tensor(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
+    nb, hkv, bs, d = k_cache.shape
+    n = slot_mapping.shape[0]
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache shapes differ")
+    if tuple(k.shape) != (n, hkv, d) or tuple(v.shape) != (n, hkv, d):
+        raise ValueError("k and v must be [num_tokens, num_kv_heads, head_dim]")
+    _check(library().pa_write_cache(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                    slot_mapping.data_ptr(), n, hkv, d, bs, nb, _DTYPES[k_cache.dtype],
+                                    _stream(k_cache)))
+
+
+def copy_blocks(k_cache, v_cache, src_dst_pairs):
+    """Copy whole blocks src -> dst in both caches (``pa_copy_blocks``)."""
+    _dev_tensor(k_cache, "k_cache", ndim=4)
+    if k_cache.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {k_cache.dtype}")
+    _dev_tensor(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+    _dev_tensor(src_dst_pairs, "src_dst_pairs", dtype=torch.int32, ndim=2)
+    if src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be [num_pairs, 2]")
+    nb, hkv, bs, d = k_cache.shape
+    _check(library().pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src_dst_pairs.data_ptr(),
+                                    src_dst_pairs.shape[0], hkv, bs, d, nb, _DTYPES[k_cache.dtype],
+                                    _stream(k_cache)))

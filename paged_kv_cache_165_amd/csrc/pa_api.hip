@@ -1,0 +1,304 @@
+// C-ABI entry points: argument validation, workspace layout and dispatch.
+// Every check happens before any launch; a failing call launches nothing.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kDefaultPartition = 512;
+constexpr int kMaxSeqs = 8192;
+constexpr int kMaxTableSlice = 256;
+
+thread_local std::string g_last_error;
+
+pa_status_t fail(pa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pa_status_t fail(pa_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+pa_status_t hip_fail(hipError_t e, const char* what) {
+    return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(pa_dtype_t dt) { return dt == PA_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == PA_F32 || dt == PA_BF16 || dt == PA_F16; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int x) {
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
+}
+
+// Compute-unit count of the current device, cached per device.
+pa_status_t num_cus(int* out) {
+    static std::mutex mu;
+    static std::unordered_map<int, int> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) {
+        *out = it->second;
+        return PA_OK;
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    cache[dev] = n;
+    *out = n;
+    return PA_OK;
+}
+
+int resolve_partition(int partition_size) {
+    return partition_size == 0 ? kDefaultPartition : partition_size;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct WsLayout {
+    size_t m_off, l_off, o_off, total;
+};
+
+WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int pmax) {
+    WsLayout w{};
+    if (pmax <= 1) return w;  // single-partition sequences never touch the workspace
+    const size_t recs = static_cast<size_t>(num_seqs) * num_heads * pmax;
+    w.m_off = 0;
+    w.l_off = align256(recs * sizeof(float));
+    w.o_off = w.l_off + align256(recs * sizeof(float));
+    w.total = w.o_off + align256(recs * head_dim * sizeof(float));
+    return w;
+}
+
+int pmax_of(int max_context_len, int part) {
+    const int p = (max_context_len + part - 1) / part;
+    return p < 1 ? 1 : p;
+}
+
+// Shared validation of the decode entry points; fills `p`.
+pa_status_t prepare_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           int block_size, int num_seqs, int num_heads, int num_kv_heads,
+                           int head_dim, int num_blocks, int max_blocks_per_seq,
+                           int max_context_len, int partition_size, pa_dtype_t dtype,
+                           void* workspace, size_t workspace_bytes, pa::DecodeParams* p) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
+        max_blocks_per_seq <= 0 || max_context_len < 0 || block_size <= 0 || partition_size < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_seqs=%d num_heads=%d num_kv_heads=%d "
+                    "head_dim=%d num_blocks=%d max_blocks_per_seq=%d max_context_len=%d block_size=%d "
+                    "partition_size=%d)", num_seqs, num_heads, num_kv_heads, head_dim, num_blocks,
+                    max_blocks_per_seq, max_context_len, block_size, partition_size);
+    if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if (num_heads % num_kv_heads != 0)
+        return fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    const int group = num_heads / num_kv_heads;
+    if (!pa::decode_supported(dtype, head_dim, group))
+        return fail(PA_ERR_UNSUPPORTED, "no kernel for dtype=%d head_dim=%d group=%d "
+                    "(head_dim 64/128/256, group 1/2/4/8)", static_cast<int>(dtype), head_dim, group);
+    if (num_seqs > kMaxSeqs) return fail(PA_ERR_UNSUPPORTED, "num_seqs %d > %d", num_seqs, kMaxSeqs);
+    if (!is_pow2(block_size) || block_size < 4 || block_size > 256)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two in [4, 256]", block_size);
+    const int rpi = pa::rows_per_wave_load(dtype, head_dim);
+    if (block_size < rpi)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d < %d rows per wave load for this dtype/head_dim", block_size, rpi);
+    const int part = resolve_partition(partition_size);
+    if (part % 16 != 0 || part % block_size != 0 || part / block_size > kMaxTableSlice)
+        return fail(PA_ERR_INVALID_ARG, "partition_size %d must be a multiple of 16 and of block_size %d "
+                    "spanning at most %d blocks", part, block_size, kMaxTableSlice);
+    if (static_cast<long long>(max_blocks_per_seq) * block_size < max_context_len)
+        return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size = %lld < max_context_len %d",
+                    static_cast<long long>(max_blocks_per_seq) * block_size, max_context_len);
+    if (num_seqs > 0) {
+        if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+            return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+        if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+            return fail(PA_ERR_INVALID_ARG, "q, out, k_cache and v_cache must be 16-byte aligned");
+        if (out == q) return fail(PA_ERR_INVALID_ARG, "out aliases q");
+    }
+    const int pmax = pmax_of(max_context_len, part);
+    const WsLayout ws = ws_layout(num_seqs, num_heads, head_dim, pmax);
+    if (ws.total > 0 && num_seqs > 0) {
+        if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes required", ws.total);
+        if (workspace_bytes < ws.total)
+            return fail(PA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, ws.total);
+        if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    }
+    char* wsb = static_cast<char*>(workspace);
+    p->out = out;
+    p->q = q;
+    p->k_cache = k_cache;
+    p->v_cache = v_cache;
+    p->block_tables = block_tables;
+    p->context_lens = context_lens;
+    p->ws_m = ws.total ? reinterpret_cast<float*>(wsb + ws.m_off) : nullptr;
+    p->ws_l = ws.total ? reinterpret_cast<float*>(wsb + ws.l_off) : nullptr;
+    p->ws_o = ws.total ? reinterpret_cast<float*>(wsb + ws.o_off) : nullptr;
+    p->scale_log2 = scale * 1.4426950408889634f;
+    p->num_seqs = num_seqs;
+    p->num_heads = num_heads;
+    p->num_kv_heads = num_kv_heads;
+    p->group = group;
+    p->num_blocks = num_blocks;
+    p->max_blocks = max_blocks_per_seq;
+    p->max_ctx = max_context_len;
+    p->part = part;
+    p->pmax = pmax;
+    p->log2_bs = log2i(block_size);
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(pa_status_t status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_INVALID_ARG: return "invalid argument";
+        case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case PA_ERR_WORKSPACE: return "workspace missing or too small";
+        case PA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_default_partition_size(void) { return kDefaultPartition; }
+
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                                int partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_size < 0)
+        return 0;
+    const int part = resolve_partition(partition_size);
+    return ws_layout(num_seqs, num_heads, head_dim, pmax_of(max_context_len, part)).total;
+}
+
+#define PA_DECODE_ARGS                                                                              \
+    out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, num_seqs, num_heads, \
+        num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, partition_size,  \
+        dtype, workspace, workspace_bytes
+
+pa_status_t pa_decode_partitions(void* out, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, float scale, int block_size,
+                                 int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                 int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                 int partition_size, pa_dtype_t dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    pa::DecodeParams p;
+    pa_status_t st = prepare_decode(PA_DECODE_ARGS, &p);
+    if (st != PA_OK) return st;
+    if (num_seqs == 0) return PA_OK;
+    int cus = 0;
+    st = num_cus(&cus);
+    if (st != PA_OK) return st;
+    hipError_t e = pa::launch_decode_partitions(p, dtype, head_dim, cus, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode partition kernel launch");
+    return PA_OK;
+}
+
+pa_status_t pa_decode_merge(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            float scale, int block_size, int num_seqs, int num_heads,
+                            int num_kv_heads, int head_dim, int num_blocks,
+                            int max_blocks_per_seq, int max_context_len, int partition_size,
+                            pa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    pa::DecodeParams p;
+    pa_status_t st = prepare_decode(PA_DECODE_ARGS, &p);
+    if (st != PA_OK) return st;
+    if (num_seqs == 0) return PA_OK;
+    hipError_t e = pa::launch_decode_merge(p, dtype, head_dim, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode merge kernel launch");
+    return PA_OK;
+}
+
+pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int block_size, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                      int num_blocks, int max_blocks_per_seq, int max_context_len,
+                      int partition_size, pa_dtype_t dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    pa::DecodeParams p;
+    pa_status_t st = prepare_decode(PA_DECODE_ARGS, &p);
+    if (st != PA_OK) return st;
+    if (num_seqs == 0) return PA_OK;
+    int cus = 0;
+    st = num_cus(&cus);
+    if (st != PA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = pa::launch_decode_partitions(p, dtype, head_dim, cus, s);
+    if (e != hipSuccess) return hip_fail(e, "decode partition kernel launch");
+    e = pa::launch_decode_merge(p, dtype, head_dim, s);
+    if (e != hipSuccess) return hip_fail(e, "decode merge kernel launch");
+    return PA_OK;
+}
+
+pa_status_t pa_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                           const int32_t* slot_mapping, int num_tokens, int num_kv_heads,
+                           int head_dim, int block_size, int num_blocks, pa_dtype_t dtype,
+                           void* stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_tokens=%d num_kv_heads=%d head_dim=%d "
+                    "block_size=%d num_blocks=%d)", num_tokens, num_kv_heads, head_dim, block_size, num_blocks);
+    if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    const int row_bytes = head_dim * elem_bytes(dtype);
+    if (row_bytes % 16 != 0)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim * element size = %d bytes is not a multiple of 16", row_bytes);
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PA_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
+    hipError_t e = pa::launch_write_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+                                          row_bytes, block_size, num_blocks, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "cache write kernel launch");
+    return PA_OK;
+}
+
+pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
+                           int num_pairs, int num_kv_heads, int block_size, int head_dim,
+                           int num_blocks, pa_dtype_t dtype, void* stream) {
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_pairs=%d num_kv_heads=%d block_size=%d "
+                    "head_dim=%d num_blocks=%d)", num_pairs, num_kv_heads, block_size, head_dim, num_blocks);
+    if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    const size_t block_bytes = static_cast<size_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
+    if (block_bytes % 16 != 0)
+        return fail(PA_ERR_UNSUPPORTED, "block of %zu bytes is not a multiple of 16", block_bytes);
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !src_dst_pairs) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PA_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+    hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, src_dst_pairs, num_pairs, block_bytes, num_blocks,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "block copy kernel launch");
+    return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Cache maintenance kernels for gfx950: the per-token write through a slot
+// mapping and the whole-block copy of copy-on-write.
+//
+// Both move raw 16-byte vectors, so the result is bit-exact whatever the
+// element type. The write is the "write the new token" step and the copy the
+// "allocate a new block and copy the old one into it" step of copy-on-write
+// (aiqz.cc tutorial, section 前缀共享机制; cf-1.com blog, 4.2). The slot of a
+// token is its (physical block, offset) pair of the block-table equation
+// (aiqz.cc, section 块表映射机制) flattened as pid * B + off.
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+// One workgroup per new token. Thread c moves 16-byte chunk c of the token's
+// [Hkv][D] row set into k_cache[pid][kv][off][:] (and the same for V).
+__global__ __launch_bounds__(256) void pa_write_kernel(const u32x4* __restrict__ k,
+                                                       const u32x4* __restrict__ v,
+                                                       u32x4* __restrict__ kc,
+                                                       u32x4* __restrict__ vc,
+                                                       const int32_t* __restrict__ slots,
+                                                       int num_kv_heads, int row16,
+                                                       int block_size, long long pool_slots) {
+    const int i = blockIdx.x;
+    const int slot = slots[i];
+    if (slot < 0 || static_cast<long long>(slot) >= pool_slots) return;
+    const int pid = slot / block_size;
+    const int off = slot - pid * block_size;
+    const int chunks = num_kv_heads * row16;
+    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+        const int kvh = c / row16;
+        const int r = c - kvh * row16;
+        const size_t dst = ((static_cast<size_t>(pid) * num_kv_heads + kvh) * block_size + off) * row16 + r;
+        const size_t src = static_cast<size_t>(i) * chunks + c;
+        kc[dst] = k[src];
+        vc[dst] = v[src];
+    }
+}
+
+// grid (pairs, 2): y = 0 copies K, y = 1 copies V. A block is contiguous
+// ([Hkv][B][D]), so the copy is one linear run of block16 vectors.
+__global__ __launch_bounds__(256) void pa_copy_kernel(u32x4* __restrict__ kc, u32x4* __restrict__ vc,
+                                                      const int32_t* __restrict__ pairs,
+                                                      size_t block16, int num_blocks) {
+    const int i = blockIdx.x;
+    const int src = pairs[2 * i];
+    const int dst = pairs[2 * i + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+    u32x4* c = blockIdx.y == 0 ? kc : vc;
+    const u32x4* from = c + static_cast<size_t>(src) * block16;
+    u32x4* to = c + static_cast<size_t>(dst) * block16;
+    size_t x = threadIdx.x;
+    for (; x + 3 * 256 < block16; x += 4 * 256) {
+        const u32x4 a0 = from[x], a1 = from[x + 256], a2 = from[x + 512], a3 = from[x + 768];
+        to[x] = a0; to[x + 256] = a1; to[x + 512] = a2; to[x + 768] = a3;
+    }
+    for (; x < block16; x += 256) to[x] = from[x];
+}
+
+hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int32_t* slots, int num_tokens, int num_kv_heads,
+                              int row_bytes, int block_size, int num_blocks, hipStream_t stream) {
+    if (num_tokens == 0) return hipSuccess;
+    const int row16 = row_bytes / 16;
+    const int chunks = num_kv_heads * row16;
+    int threads = chunks < 256 ? ((chunks + 63) / 64) * 64 : 256;
+    hipLaunchKernelGGL(pa_write_kernel, dim3(static_cast<unsigned>(num_tokens)), dim3(threads), 0, stream,
+                       static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
+                       static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), slots,
+                       num_kv_heads, row16, block_size,
+                       static_cast<long long>(num_blocks) * block_size);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
+                              size_t block_bytes, int num_blocks, hipStream_t stream) {
+    if (num_pairs == 0) return hipSuccess;
+    hipLaunchKernelGGL(pa_copy_kernel, dim3(static_cast<unsigned>(num_pairs), 2), dim3(256), 0, stream,
+                       static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), pairs,
+                       block_bytes / 16, num_blocks);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,59 @@
+// Internal launch interface between the C-ABI entry points (pa_api.hip) and
+// the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// Everything one decode launch needs. Pointers are device pointers.
+struct DecodeParams {
+    void* out;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float* ws_m;        // [S][Hq][pmax]  running max per partition (log2 units)
+    float* ws_l;        // [S][Hq][pmax]  softmax denominator per partition
+    float* ws_o;        // [S][Hq][pmax][D] normalised partial output
+    float scale_log2;   // scale * log2(e): logits are kept in base-2 units
+    int num_seqs;
+    int num_heads;
+    int num_kv_heads;
+    int group;          // num_heads / num_kv_heads
+    int num_blocks;
+    int max_blocks;     // max_blocks_per_seq (row stride of block_tables)
+    int max_ctx;        // host bound on context lengths
+    int part;           // tokens per partition
+    int pmax;           // ceil(max_ctx / part), >= 1
+    int log2_bs;        // block size = 1 << log2_bs
+};
+
+// Number of tokens per wave row-chunk of the VALU kernel for (dtype, D):
+// a 16-byte lane load covers 16 / E elements, so one row of D elements spans
+// D * E / 16 lanes and a wave covers 1024 / (D * E) rows per instruction.
+inline int rows_per_wave_load(pa_dtype_t dt, int head_dim) {
+    int e = dt == PA_F32 ? 4 : 2;
+    return 1024 / (head_dim * e);
+}
+
+// Returns hipSuccess or the launch error. `grid` <= 0 selects the
+// persistent grid size from the occupancy of the chosen kernel.
+hipError_t launch_decode_partitions(const DecodeParams& p, pa_dtype_t dt, int head_dim,
+                                    int num_cus, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeParams& p, pa_dtype_t dt, int head_dim,
+                               hipStream_t stream);
+bool decode_supported(pa_dtype_t dt, int head_dim, int group);
+
+hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int32_t* slots, int num_tokens, int num_kv_heads,
+                              int row_bytes, int block_size, int num_blocks, hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
+                              size_t block_bytes, int num_blocks, hipStream_t stream);
+
+}  // namespace pa

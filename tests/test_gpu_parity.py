@@ -1,0 +1,86 @@
+"""GPU parity on the six synthetic workloads: the full step (block copies,
+cache writes, decode) through the C ABI against the CPU oracle on the same
+seeded inputs. Cache contents must match bit for bit, attention within
+tolerance (harness.TOL_*). Sizes are the workloads' full sizes, in the
+launch configuration the bench times (default partition 512)."""
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from harness import DeviceCase, compare_attention, host_bits, log, oracle_step, raw_equal
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = ["layout", "tiny", "mha7b", "gqa8b", "prefix", "long"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_165_amd as pa
+    pa.library()  # raise now if the HIP library is missing
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_workload_parity(name):
+    t_start = time.perf_counter()
+    w = W.build(name)
+    log(f"[parity] {name}: {w.summary()}")
+    case = DeviceCase(w)
+    q_h = host_bits(case.q)
+    kc_h = host_bits(case.k_cache)
+    vc_h = host_bits(case.v_cache)
+    wv_h = [(host_bits(k), host_bits(v)) for k, v in case.write_values]
+    case.gpu_step()
+    torch.cuda.synchronize()
+    log(f"[parity] {name}: gpu step done, running oracle")
+    kc_o, vc_o, ref, t_or = oracle_step(w, q_h, kc_h, vc_h, wv_h)
+    assert raw_equal(case.k_cache, kc_o), f"{name}: k_cache differs from the oracle"
+    assert raw_equal(case.v_cache, vc_o), f"{name}: v_cache differs from the oracle"
+    stats = compare_attention(case.out, ref, name)
+    log(f"[parity] {name}: {stats} oracle {t_or:.1f}s total {time.perf_counter() - t_start:.1f}s")
+
+
+def test_layout_slot_id_probe_exact():
+    """Table [5, 1, 7], B = 4, ctx 10, K == 0, V = slot id: every output
+    element is exactly 165 / 10 = 16.5 (all weights are 1)."""
+    w = W.build("layout")
+    dev = "cuda"
+    nb, hkv, bs, d = w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
+    kc = torch.zeros(nb, hkv, bs, d, device=dev)
+    slot_ids = torch.arange(nb * bs, dtype=torch.float32, device=dev).view(nb, 1, bs, 1)
+    vc = slot_ids.expand(nb, hkv, bs, d).contiguous()
+    vc[7, :, 2:, :] = float("nan")  # never read
+    q = torch.randn(1, w.num_heads, d, device=dev)
+    out = torch.empty_like(q)
+    import paged_kv_cache_165_amd as pa
+    pa.decode(out, q, kc, vc, torch.tensor([[5, 1, 7]], dtype=torch.int32, device=dev),
+              torch.tensor([10], dtype=torch.int32, device=dev), w.scale, max_context_len=10)
+    torch.cuda.synchronize()
+    assert torch.all(out == 16.5), out
+
+
+def test_write_probe_position_9():
+    """Position 9 of table [5, 1, 7] with B = 4 is slot 29: the row lands in
+    block 7, offset 1, and nothing else changes."""
+    import paged_kv_cache_165_amd as pa
+    dev = "cuda"
+    kc = torch.randn(8, 2, 4, 64, device=dev).to(torch.bfloat16)
+    vc = torch.randn(8, 2, 4, 64, device=dev).to(torch.bfloat16)
+    k0, v0 = kc.clone(), vc.clone()
+    k = torch.randn(1, 2, 64, device=dev).to(torch.bfloat16)
+    v = torch.randn(1, 2, 64, device=dev).to(torch.bfloat16)
+    pa.write_cache(k, v, kc, vc, torch.tensor([29], dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(kc[7, :, 1].view(torch.int16), k[0].view(torch.int16))
+    assert torch.equal(vc[7, :, 1].view(torch.int16), v[0].view(torch.int16))
+    k0[7, :, 1] = k[0]
+    v0[7, :, 1] = v[0]
+    assert torch.equal(kc.view(torch.int16), k0.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), v0.view(torch.int16))
