@@ -47,8 +47,8 @@ def parse():
 
 
 def cpu_baseline(w, q_h, kc_h, vc_h, seconds: float):
-    """Time the oracle on the first sequences of the batch until about
-    `seconds` of CPU work has been done; single BLAS thread."""
+    """Time the oracle on the batch's sequences, in order and cycling, until
+    about `seconds` of CPU work has been done; single BLAS thread."""
     import numpy as np
     import oracle
     try:
@@ -60,8 +60,8 @@ def cpu_baseline(w, q_h, kc_h, vc_h, seconds: float):
     done, t_used, kv = 0, 0.0, 0
     e = 4 if w.dtype == "f32" else 2
     t0 = time.perf_counter()
-    while done < w.num_seqs and t_used < seconds:
-        i = done
+    while t_used < seconds:
+        i = done % w.num_seqs
         ts = time.perf_counter()
         oracle.paged_decode(q_h[i:i + 1], kc_h, vc_h, w.block_tables[i:i + 1], w.context_lens[i:i + 1],
                             w.scale, w.block_size, dt)
@@ -74,8 +74,8 @@ def cpu_baseline(w, q_h, kc_h, vc_h, seconds: float):
     return {
         "value": round(kv / t_used / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
         "seqs_per_s": round(done / t_used, 3),
-        "sample": f"first {done} of {w.num_seqs} sequences of {w.name} ({kv / 1e6:.1f} MB of K+V), "
-                  f"float64 numpy oracle, 1 BLAS thread, {wall:.1f} s",
+        "sample": f"{done} sequence decodes cycling over the {w.num_seqs} sequences of {w.name} "
+                  f"({kv / 1e6:.1f} MB of K+V), float64 numpy oracle, 1 BLAS thread, {wall:.1f} s",
     }
 
 
@@ -186,7 +186,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
-                   "partition_size": w.partition_size, "ctx": w.ctx_recipe, "tokens": int(w.context_lens.sum()),
+                   "partition_size": w.partition_size or pa.default_partition_size(), "ctx": w.ctx_recipe, "tokens": int(w.context_lens.sum()),
                    "kv_bytes": kv, "seed": w.seed, "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),

@@ -25,4 +25,8 @@ from .paged_attention import (  # noqa: F401
     write_cache,
     copy_blocks,
     to_float64,
+    v_tile,
+    v_cache_shape,
+    k_rows_at,
+    v_rows_at,
 )

@@ -15,7 +15,11 @@ Pages cited (the four web pages this method is taken from):
              vLLM如何用它解决大模型推理显存碎片问题".
 
 Storage layout (the pages fix none; this is the reading used everywhere):
-  k_cache, v_cache : [num_blocks, num_kv_heads, block_size, head_dim]
+  k_cache          : [num_blocks, num_kv_heads, block_size, head_dim]
+  v_cache          : [num_blocks, num_kv_heads, block_size // T, head_dim, T],
+                     T = min(block_size, 16): each block's V rows are stored as
+                     tiles of T tokens, transposed (head_dim-major, token-minor).
+                     V row of (block pid, offset off) = v_cache[pid, :, off // T, :, off % T].
   q, out           : [num_seqs, num_heads, head_dim]
   k, v (new tokens): [num_tokens, num_kv_heads, head_dim]
   block_tables     : int [num_seqs, max_blocks_per_seq]
@@ -60,6 +64,28 @@ def _check_storage(x: np.ndarray, dtype: str, name: str) -> None:
     want = _STORAGE[dtype]
     if x.dtype != want:
         raise TypeError(f"{name}: expected numpy {np.dtype(want).name} storage for {dtype}, got {x.dtype}")
+
+
+def v_tile(block_size: int) -> int:
+    """Tokens per transposed V tile: min(block_size, 16)."""
+    return min(block_size, 16)
+
+
+def v_cache_shape(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int) -> tuple:
+    t = v_tile(block_size)
+    return (num_blocks, num_kv_heads, block_size // t, head_dim, t)
+
+
+def k_rows_at(cache: np.ndarray, pid, off) -> np.ndarray:
+    """K rows [..., num_kv_heads, head_dim] of (block, offset) pairs."""
+    return cache[pid, :, off, :]
+
+
+def v_rows_at(cache: np.ndarray, pid, off, block_size: int) -> np.ndarray:
+    """V rows [..., num_kv_heads, head_dim] of (block, offset) pairs, read from
+    the transposed tile layout."""
+    t = v_tile(block_size)
+    return cache[pid, :, off // t, :, off % t]
 
 
 def to_float64(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -108,21 +134,30 @@ def translate(block_table_row, position: int, block_size: int) -> tuple[int, int
 
 
 def gather_rows(cache: np.ndarray, block_table_row, context_len: int, block_size: int,
-                dtype: str) -> np.ndarray:
+                dtype: str, kind: str = "k") -> np.ndarray:
     """Contiguous float64 view [context_len, num_kv_heads, head_dim] of one
-    sequence's cached rows, read through its block table.
+    sequence's cached K rows (kind "k") or V rows (kind "v"), read through its
+    block table.
 
     Each logical position t in [0, context_len) is translated with
-    ``translate`` and the row cache[pid, :, off, :] is taken. Only the first
+    ``translate`` and the row at (pid, off) is taken. Only the first
     ceil(context_len / B) table entries are read and no slot at or beyond
     context_len is read ([lihaoran] "末块会浪费多少空间？": the tail slots of the
     last block are empty; [ipipp] "分页式KV缓存的底层设计": the kernel presents a
     contiguous sequence view assembled from the physical blocks).
     """
     _check_storage(cache, dtype, "cache")
-    nb, hkv, bs, d = cache.shape
-    if bs != block_size:
-        raise ValueError("cache block dimension does not match block_size")
+    nb, hkv = cache.shape[0], cache.shape[1]
+    if kind == "k":
+        if cache.ndim != 4 or cache.shape[2] != block_size:
+            raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+        d = cache.shape[3]
+    elif kind == "v":
+        if cache.ndim != 5 or cache.shape != v_cache_shape(nb, hkv, block_size, cache.shape[3]):
+            raise ValueError("v_cache must be [num_blocks, num_kv_heads, block_size // T, head_dim, T]")
+        d = cache.shape[3]
+    else:
+        raise ValueError("kind must be 'k' or 'v'")
     if context_len == 0:
         return np.zeros((0, hkv, d), dtype=np.float64)
     t = np.arange(context_len)
@@ -131,7 +166,7 @@ def gather_rows(cache: np.ndarray, block_table_row, context_len: int, block_size
     pid = np.asarray(block_table_row, dtype=np.int64)[logical]
     if pid.min() < 0 or pid.max() >= nb:
         raise IndexError("block table entry outside the block pool")
-    rows = cache[pid, :, offset, :]  # [context_len, hkv, d]
+    rows = k_rows_at(cache, pid, offset) if kind == "k" else v_rows_at(cache, pid, offset, block_size)
     return to_float64(rows, dtype)
 
 
@@ -174,12 +209,12 @@ def _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, block_si
     _check_storage(q, dtype, "q")
     _check_storage(k_cache, dtype, "k_cache")
     _check_storage(v_cache, dtype, "v_cache")
-    if k_cache.shape != v_cache.shape:
-        raise ValueError("k_cache and v_cache shapes differ")
     s, hq, d = q.shape
     nb, hkv, bs, d2 = k_cache.shape
     if d2 != d or bs != block_size:
         raise ValueError("cache shape does not match q / block_size")
+    if v_cache.shape != v_cache_shape(nb, hkv, block_size, d):
+        raise ValueError("v_cache shape does not match the transposed tile layout")
     if len(context_lens) != s or len(block_tables) != s:
         raise ValueError("one block table and one context length per sequence")
     for L in context_lens:
@@ -205,8 +240,8 @@ def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     out = np.zeros(q.shape, dtype=np.float64)
     for i in range(s):
         L = int(context_lens[i])
-        k_rows = gather_rows(k_cache, block_tables[i], L, block_size, dtype)
-        v_rows = gather_rows(v_cache, block_tables[i], L, block_size, dtype)
+        k_rows = gather_rows(k_cache, block_tables[i], L, block_size, dtype, "k")
+        v_rows = gather_rows(v_cache, block_tables[i], L, block_size, dtype, "v")
         out[i] = attend_contiguous(to_float64(q[i], dtype), k_rows, v_rows, scale)
     return out
 
@@ -271,8 +306,8 @@ def paged_decode_partitioned(q, k_cache, v_cache, block_tables, context_lens, sc
     out = np.zeros(q.shape, dtype=np.float64)
     for i in range(s):
         L = int(context_lens[i])
-        k_rows = gather_rows(k_cache, block_tables[i], L, block_size, dtype)
-        v_rows = gather_rows(v_cache, block_tables[i], L, block_size, dtype)
+        k_rows = gather_rows(k_cache, block_tables[i], L, block_size, dtype, "k")
+        v_rows = gather_rows(v_cache, block_tables[i], L, block_size, dtype, "v")
         qi = to_float64(q[i], dtype)
         nparts = max(1, -(-L // partition_size))
         for h in range(hq):
@@ -293,20 +328,21 @@ def write_cache(k: np.ndarray, v: np.ndarray, k_cache: np.ndarray, v_cache: np.n
                 slot_mapping, block_size: int) -> tuple[np.ndarray, np.ndarray]:
     """Write each new token's K and V rows into its slot; returns new caches.
 
-    For token i with slot_i >= 0: pid, off = divmod(slot_i, B) and
-    cache[pid, :, off, :] = k[i] (and the same for V). A slot of -1 means the
-    token is skipped. Elements are moved as stored (no conversion), so the
-    result is defined bit for bit. This is the "write the new token" step of
-    [aiqz] "前缀共享机制"; the slot is the position of that step's (pid, off)
-    pair of [aiqz] "块表映射机制" flattened as pid * B + off.
+    For token i with slot_i >= 0: pid, off = divmod(slot_i, B), the K row at
+    (pid, off) becomes k[i] and the V row at (pid, off) becomes v[i] (in the
+    transposed tile layout). A slot of -1 means the token is skipped.
+    Elements are moved as stored (no conversion), so the result is defined bit
+    for bit. This is the "write the new token" step of [aiqz] "前缀共享机制";
+    the slot is the (pid, off) pair of [aiqz] "块表映射机制" flattened as
+    pid * B + off.
     Preconditions (raise): equal storage dtypes, slots in {-1} U [0, NB * B),
     non-negative slots pairwise distinct.
     """
     if not (k.dtype == v.dtype == k_cache.dtype == v_cache.dtype):
         raise TypeError("all arrays must share one storage dtype")
     nb, hkv, bs, d = k_cache.shape
-    if bs != block_size or v_cache.shape != k_cache.shape:
-        raise ValueError("cache shape does not match block_size")
+    if bs != block_size or v_cache.shape != v_cache_shape(nb, hkv, block_size, d):
+        raise ValueError("cache shapes do not match block_size")
     slots = np.asarray(slot_mapping, dtype=np.int64)
     if k.shape != (len(slots), hkv, d) or v.shape != k.shape:
         raise ValueError("k/v must be [num_tokens, num_kv_heads, head_dim]")
@@ -315,6 +351,7 @@ def write_cache(k: np.ndarray, v: np.ndarray, k_cache: np.ndarray, v_cache: np.n
         raise IndexError("slot outside the block pool")
     if len(np.unique(live)) != len(live):
         raise ValueError("duplicate slot in slot_mapping")
+    t = v_tile(block_size)
     k_new = k_cache.copy()
     v_new = v_cache.copy()
     for i, slot in enumerate(slots):
@@ -322,7 +359,7 @@ def write_cache(k: np.ndarray, v: np.ndarray, k_cache: np.ndarray, v_cache: np.n
             continue
         pid, off = divmod(int(slot), block_size)
         k_new[pid, :, off, :] = k[i]
-        v_new[pid, :, off, :] = v[i]
+        v_new[pid, :, off // t, :, off % t] = v[i]
     return k_new, v_new
 
 
@@ -336,8 +373,8 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray,
     into it. Pairs act as if applied at once. Preconditions (raise): ids in
     range, every dst distinct, no dst equal to any src.
     """
-    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
-        raise ValueError("k_cache and v_cache must match")
+    if k_cache.shape[0] != v_cache.shape[0] or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must have the same block count and dtype")
     nb = k_cache.shape[0]
     pairs = np.asarray(src_dst_pairs, dtype=np.int64).reshape(-1, 2)
     if pairs.size and (pairs.min() < 0 or pairs.max() >= nb):

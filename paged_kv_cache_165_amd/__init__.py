@@ -7,7 +7,9 @@ runs in the library's HIP kernels. PyTorch supplies device memory and
 streams only. There is no fallback path: a missing library raises.
 
 Layouts (see include/pa.h):
-  k_cache, v_cache  [num_blocks, num_kv_heads, block_size, head_dim]
+  k_cache           [num_blocks, num_kv_heads, block_size, head_dim]
+  v_cache           [num_blocks, num_kv_heads, block_size // T, head_dim, T],
+                    T = min(block_size, 16) (``v_cache_shape``)
   q, out            [num_seqs, num_heads, head_dim]
   k, v              [num_tokens, num_kv_heads, head_dim]
   block_tables      int32 [num_seqs, max_blocks_per_seq]
@@ -26,6 +28,7 @@ from . import _lib
 
 __all__ = [
     "PaError", "library", "default_partition_size", "workspace_size", "alloc_workspace",
+    "v_tile", "v_cache_shape", "alloc_cache",
     "decode", "decode_partitions", "decode_merge", "write_cache", "copy_blocks",
 ]
 
@@ -66,6 +69,36 @@ def _stream(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def v_tile(block_size: int) -> int:
+    """Tokens per transposed V tile of the cache layout."""
+    return min(block_size, 16)
+
+
+def v_cache_shape(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int) -> tuple:
+    t = v_tile(block_size)
+    return (num_blocks, num_kv_heads, block_size // t, head_dim, t)
+
+
+def alloc_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+                dtype=torch.bfloat16, device="cuda"):
+    """Uninitialised (k_cache, v_cache) pair in the library's layout."""
+    k = torch.empty(num_blocks, num_kv_heads, block_size, head_dim, dtype=dtype, device=device)
+    v = torch.empty(v_cache_shape(num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype, device=device)
+    return k, v
+
+
+def _check_caches(k_cache, v_cache):
+    _dev_tensor(k_cache, "k_cache", ndim=4)
+    if k_cache.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {k_cache.dtype}")
+    _dev_tensor(v_cache, "v_cache", dtype=k_cache.dtype, ndim=5)
+    nb, hkv, bs, d = k_cache.shape
+    if tuple(v_cache.shape) != v_cache_shape(nb, hkv, bs, d):
+        raise ValueError(f"v_cache must have shape {v_cache_shape(nb, hkv, bs, d)} "
+                         f"(transposed tiles), got {tuple(v_cache.shape)}")
+    return nb, hkv, bs, d
+
+
 def default_partition_size() -> int:
     return int(library().pa_default_partition_size())
 
@@ -89,16 +122,16 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     _dev_tensor(out, "out", dtype=q.dtype, ndim=3)
-    _dev_tensor(k_cache, "k_cache", dtype=q.dtype, ndim=4)
-    _dev_tensor(v_cache, "v_cache", dtype=q.dtype, ndim=4)
+    if k_cache.dtype != q.dtype:
+        raise ValueError(f"k_cache must be {q.dtype}, got {k_cache.dtype}")
+    nb, hkv, bs, d2 = _check_caches(k_cache, v_cache)
     _dev_tensor(block_tables, "block_tables", dtype=torch.int32, ndim=2)
     _dev_tensor(context_lens, "context_lens", dtype=torch.int32, ndim=1)
     s, hq, d = q.shape
-    nb, hkv, bs, d2 = k_cache.shape
     if tuple(out.shape) != (s, hq, d):
         raise ValueError("out must have the shape of q")
-    if tuple(v_cache.shape) != tuple(k_cache.shape) or d2 != d:
-        raise ValueError("k_cache and v_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    if d2 != d:
+        raise ValueError("cache head_dim differs from q")
     if block_tables.shape[0] != s or context_lens.shape[0] != s:
         raise ValueError("one block table row and one context length per sequence")
     if max_context_len is None:
@@ -145,17 +178,11 @@ def decode_merge(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
 
 def write_cache(k, v, k_cache, v_cache, slot_mapping):
     """Write new tokens' K/V rows into their slots (``pa_write_cache``)."""
-    _dev_tensor(k_cache, "k_cache", ndim=4)
-    if k_cache.dtype not in _DTYPES:
-        raise ValueError(f"unsupported dtype {k_cache.dtype}")
-    _dev_tensor(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+    nb, hkv, bs, d = _check_caches(k_cache, v_cache)
     _dev_tensor(k, "k", dtype=k_cache.dtype, ndim=3)
     _dev_tensor(v, "v", dtype=k_cache.dtype, ndim=3)
     _dev_tensor(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
-    nb, hkv, bs, d = k_cache.shape
     n = slot_mapping.shape[0]
-    if tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise ValueError("k_cache and v_cache shapes differ")
     if tuple(k.shape) != (n, hkv, d) or tuple(v.shape) != (n, hkv, d):
         raise ValueError("k and v must be [num_tokens, num_kv_heads, head_dim]")
     _check(library().pa_write_cache(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -165,14 +192,10 @@ def write_cache(k, v, k_cache, v_cache, slot_mapping):
 
 def copy_blocks(k_cache, v_cache, src_dst_pairs):
     """Copy whole blocks src -> dst in both caches (``pa_copy_blocks``)."""
-    _dev_tensor(k_cache, "k_cache", ndim=4)
-    if k_cache.dtype not in _DTYPES:
-        raise ValueError(f"unsupported dtype {k_cache.dtype}")
-    _dev_tensor(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+    nb, hkv, bs, d = _check_caches(k_cache, v_cache)
     _dev_tensor(src_dst_pairs, "src_dst_pairs", dtype=torch.int32, ndim=2)
     if src_dst_pairs.shape[1] != 2:
         raise ValueError("src_dst_pairs must be [num_pairs, 2]")
-    nb, hkv, bs, d = k_cache.shape
     _check(library().pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src_dst_pairs.data_ptr(),
                                     src_dst_pairs.shape[0], hkv, bs, d, nb, _DTYPES[k_cache.dtype],
                                     _stream(k_cache)))

@@ -31,14 +31,20 @@ def compile_flags(extra=()) -> list:
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results go to ordinary VGPRs: the accumulators are then
+        # rescaled in place instead of being copied out of AGPRs every tile
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-function",
         f"-I{INCLUDE}", f"-I{CSRC}", *extra,
     ]
 
 
-def build_library(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source to an object in parallel, then link libpa.so."""
-    objdir = os.path.join(PKG_DIR, "_build")
+def build_library(verbose: bool = False, jobs: int = 4, extra_flags=(), out: str = LIB_PATH,
+                  objdir: str = None) -> str:
+    """Compile every source to an object in parallel, then link the library
+    (default: libpa.so in the package directory). `extra_flags` are passed to
+    every compile (e.g. -D tuning macros for a side build)."""
+    objdir = objdir or os.path.join(PKG_DIR, "_build")
     os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
     procs = []
@@ -46,7 +52,7 @@ def build_library(verbose: bool = False, jobs: int = 4) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *compile_flags(extra_flags), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
@@ -54,21 +60,21 @@ def build_library(verbose: bool = False, jobs: int = 4) -> str:
             procs[0][1].wait()
     failed = []
     for src, p in procs:
-        out, _ = p.communicate()
-        msg = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+        log, _ = p.communicate()
+        msg = "\n".join(l for l in log.splitlines() if "packed-fp32-ops" not in l)
         if p.returncode != 0:
             failed.append((src, msg))
         elif verbose and msg.strip():
             print(msg)
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(f"--- {s}\n{m}" for s, m in failed))
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

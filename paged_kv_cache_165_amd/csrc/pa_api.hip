@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kDefaultPartition = 512;
+constexpr int kDefaultPartition = 1024;
 constexpr int kMaxSeqs = 8192;
 constexpr int kMaxTableSlice = 256;
 
@@ -117,13 +117,14 @@ pa_status_t prepare_decode(void* out, const void* q, const void* k_cache, const 
     const int group = num_heads / num_kv_heads;
     if (!pa::decode_supported(dtype, head_dim, group))
         return fail(PA_ERR_UNSUPPORTED, "no kernel for dtype=%d head_dim=%d group=%d "
-                    "(head_dim 64/128/256, group 1/2/4/8)", static_cast<int>(dtype), head_dim, group);
+                    "(head_dim 64/128/256; group 1/2/4/8, or 16 for 16-bit types)", static_cast<int>(dtype), head_dim, group);
     if (num_seqs > kMaxSeqs) return fail(PA_ERR_UNSUPPORTED, "num_seqs %d > %d", num_seqs, kMaxSeqs);
     if (!is_pow2(block_size) || block_size < 4 || block_size > 256)
         return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two in [4, 256]", block_size);
-    const int rpi = pa::rows_per_wave_load(dtype, head_dim);
-    if (block_size < rpi)
-        return fail(PA_ERR_UNSUPPORTED, "block_size %d < %d rows per wave load for this dtype/head_dim", block_size, rpi);
+    const int min_bs = pa::decode_min_block_size(dtype, head_dim, group);
+    if (block_size < min_bs)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d < %d, the smallest block this dtype/head_dim/group supports",
+                    block_size, min_bs);
     const int part = resolve_partition(partition_size);
     if (part % 16 != 0 || part % block_size != 0 || part / block_size > kMaxTableSlice)
         return fail(PA_ERR_INVALID_ARG, "partition_size %d must be a multiple of 16 and of block_size %d "
@@ -167,6 +168,8 @@ pa_status_t prepare_decode(void* out, const void* q, const void* k_cache, const 
     p->part = part;
     p->pmax = pmax;
     p->log2_bs = log2i(block_size);
+    p->log2_vt = log2i(pa::v_tile_tokens(block_size));
+    p->ring_slots = 1;  // set per kernel at launch
     return PA_OK;
 }
 
@@ -271,12 +274,15 @@ pa_status_t pa_write_cache(const void* k, const void* v, void* k_cache, void* v_
     const int row_bytes = head_dim * elem_bytes(dtype);
     if (row_bytes % 16 != 0)
         return fail(PA_ERR_UNSUPPORTED, "head_dim * element size = %d bytes is not a multiple of 16", row_bytes);
+    if (!is_pow2(block_size) || block_size < 4)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two >= 4", block_size);
     if (num_tokens == 0) return PA_OK;
     if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
     if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PA_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
     hipError_t e = pa::launch_write_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
-                                          row_bytes, block_size, num_blocks, static_cast<hipStream_t>(stream));
+                                          head_dim, elem_bytes(dtype), block_size, num_blocks,
+                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "cache write kernel launch");
     return PA_OK;
 }
@@ -288,6 +294,8 @@ pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_
         return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_pairs=%d num_kv_heads=%d block_size=%d "
                     "head_dim=%d num_blocks=%d)", num_pairs, num_kv_heads, block_size, head_dim, num_blocks);
     if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if (!is_pow2(block_size) || block_size < 4)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two >= 4", block_size);
     const size_t block_bytes = static_cast<size_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
     if (block_bytes % 16 != 0)
         return fail(PA_ERR_UNSUPPORTED, "block of %zu bytes is not a multiple of 16", block_bytes);

@@ -13,15 +13,19 @@
 
 namespace pa {
 
-// One workgroup per new token. Thread c moves 16-byte chunk c of the token's
-// [Hkv][D] row set into k_cache[pid][kv][off][:] (and the same for V).
+// One workgroup per new token. K: thread c moves 16-byte chunk c of the
+// token's [Hkv][D] rows into k_cache[pid][kv][off][:]. V: the cache holds each
+// block's rows as tiles of vt tokens stored head_dim-major
+// ([NB][Hkv][B/vt][D][vt]), so element d of head kv goes to
+// v_cache[pid][kv][off / vt][d][off % vt], one element per thread.
+template <typename EW>
 __global__ __launch_bounds__(256) void pa_write_kernel(const u32x4* __restrict__ k,
-                                                       const u32x4* __restrict__ v,
+                                                       const EW* __restrict__ v,
                                                        u32x4* __restrict__ kc,
-                                                       u32x4* __restrict__ vc,
+                                                       EW* __restrict__ vc,
                                                        const int32_t* __restrict__ slots,
-                                                       int num_kv_heads, int row16,
-                                                       int block_size, long long pool_slots) {
+                                                       int num_kv_heads, int head_dim, int row16,
+                                                       int block_size, int vt, long long pool_slots) {
     const int i = blockIdx.x;
     const int slot = slots[i];
     if (slot < 0 || static_cast<long long>(slot) >= pool_slots) return;
@@ -32,9 +36,16 @@ __global__ __launch_bounds__(256) void pa_write_kernel(const u32x4* __restrict__
         const int kvh = c / row16;
         const int r = c - kvh * row16;
         const size_t dst = ((static_cast<size_t>(pid) * num_kv_heads + kvh) * block_size + off) * row16 + r;
-        const size_t src = static_cast<size_t>(i) * chunks + c;
-        kc[dst] = k[src];
-        vc[dst] = v[src];
+        kc[dst] = k[static_cast<size_t>(i) * chunks + c];
+    }
+    const int elems = num_kv_heads * head_dim;
+    const size_t tile_off = static_cast<size_t>(off / vt) * head_dim * vt + (off % vt);
+    for (int c = threadIdx.x; c < elems; c += blockDim.x) {
+        const int kvh = c / head_dim;
+        const int d = c - kvh * head_dim;
+        const size_t dst = (static_cast<size_t>(pid) * num_kv_heads + kvh) * block_size * head_dim + tile_off +
+                           static_cast<size_t>(d) * vt;
+        vc[dst] = v[static_cast<size_t>(i) * elems + c];
     }
 }
 
@@ -60,16 +71,26 @@ __global__ __launch_bounds__(256) void pa_copy_kernel(u32x4* __restrict__ kc, u3
 
 hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                               const int32_t* slots, int num_tokens, int num_kv_heads,
-                              int row_bytes, int block_size, int num_blocks, hipStream_t stream) {
+                              int head_dim, int elem_bytes, int block_size, int num_blocks,
+                              hipStream_t stream) {
     if (num_tokens == 0) return hipSuccess;
-    const int row16 = row_bytes / 16;
-    const int chunks = num_kv_heads * row16;
-    int threads = chunks < 256 ? ((chunks + 63) / 64) * 64 : 256;
-    hipLaunchKernelGGL(pa_write_kernel, dim3(static_cast<unsigned>(num_tokens)), dim3(threads), 0, stream,
-                       static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
-                       static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), slots,
-                       num_kv_heads, row16, block_size,
-                       static_cast<long long>(num_blocks) * block_size);
+    const int row16 = head_dim * elem_bytes / 16;
+    const int work = num_kv_heads * head_dim;
+    const int threads = work < 256 ? ((work + 63) / 64) * 64 : 256;
+    const int vt = v_tile_tokens(block_size);
+    const long long pool_slots = static_cast<long long>(num_blocks) * block_size;
+    const dim3 grid(static_cast<unsigned>(num_tokens));
+    if (elem_bytes == 2) {
+        hipLaunchKernelGGL(pa_write_kernel<uint16_t>, grid, dim3(threads), 0, stream,
+                           static_cast<const u32x4*>(k), static_cast<const uint16_t*>(v),
+                           static_cast<u32x4*>(k_cache), static_cast<uint16_t*>(v_cache), slots,
+                           num_kv_heads, head_dim, row16, block_size, vt, pool_slots);
+    } else {
+        hipLaunchKernelGGL(pa_write_kernel<uint32_t>, grid, dim3(threads), 0, stream,
+                           static_cast<const u32x4*>(k), static_cast<const uint32_t*>(v),
+                           static_cast<u32x4*>(k_cache), static_cast<uint32_t*>(v_cache), slots,
+                           num_kv_heads, head_dim, row16, block_size, vt, pool_slots);
+    }
     return hipGetLastError();
 }
 

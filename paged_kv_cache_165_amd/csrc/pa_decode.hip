@@ -5,22 +5,35 @@
 // lives at block_table[t / B], offset t % B; attention over all visible tokens
 // is ordinary softmax attention, only the addressing differs.
 //
+// Cache layout. K: [NB][Hkv][B][D] (one 16-byte lane load = part of a row).
+// V: [NB][Hkv][B/T][D][T] with T = min(B, 16): every block holds its V rows
+// as tiles of T tokens stored head_dim-major, so the token index -- the axis
+// P.V contracts over -- is contiguous. Each 16-token step therefore reads one
+// contiguous run of V bytes, and the MFMA operand of P.V is a plain load.
+//
 // Work decomposition. An item is (sequence, KV head, partition of `part`
 // tokens). A persistent grid of 256-thread workgroups walks the item list;
 // every workgroup first builds, in LDS, the prefix sum of partition counts
 // over the batch so that an item index maps to its sequence by binary search.
-// The four waves of a workgroup share one item and take its steps of
-// 4 x (rows per load) tokens round robin.
+// The four waves of a workgroup share one item and take its steps round
+// robin. The slice of the block table the partition reads is staged in LDS
+// (cf-1.com blog, 2.2 and 5.4: table lookups served from shared memory, not
+// global memory). K/V are streamed with nontemporal 16-byte loads, the next
+// step always in flight while the current one is reduced (cf-1.com 5.1 and
+// 6.2: prefetch the next physical block).
 //
-// Per item: the slice of the block table the partition reads is staged in
-// LDS (cf-1.com blog, 2.2 and 5.4: table lookups served from shared memory,
-// not global memory). Per step every lane loads four 16-byte pieces of K and
-// of V -- each wave load instruction covers whole rows, 1 KiB contiguous for
-// bf16 D=128 at B=16 -- while the previous step is being reduced, so the next
-// block is always in flight (cf-1.com 5.1 and 6.2: prefetch the next
-// physical block). q.k is a per-lane partial dot product finished by a DPP
-// butterfly inside the lanes that hold one row; each lane keeps an online
-// softmax (running max m, sum l, weighted V sum) over the rows it saw.
+// Two inner loops:
+//  * pa_decode_valu (one query head per KV head, and float32): q.k is a
+//    per-lane partial dot product finished by a DPP butterfly over the lanes
+//    that hold one K row; each lane keeps an online softmax over its rows and
+//    accumulates P.V with FMAs.
+//  * pa_decode_mfma (bfloat16/float16 with 2..16 query heads per KV head):
+//    the heads sharing a KV head form a real small dense product. Per 16-token
+//    tile, S^T = K Q^T is D/32 v_mfma_f32_16x16x32 (K rows as A, the group's
+//    query rows as B columns), and O^T += V^T P^T is D/16 v_mfma_f32_16x16x16
+//    whose B operand is exactly the lane layout of S^T after exp2, so P never
+//    leaves registers. The softmax max is rescaled lazily (only when a tile's
+//    max exceeds the running max by more than 2^8).
 // Lanes, then waves (through LDS), are merged by the log-sum-exp rule.
 // A sequence that fits one partition is written straight to `out`; longer
 // ones leave one (m, l, o) record per partition for the merge kernel.
@@ -34,39 +47,37 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxTableSlice = 256;  // table entries one partition may span
 
+// Workgroups per compute unit of the persistent grid; 0 = as many as the
+// kernel's occupancy allows.
+#ifndef PA_WG_PER_CU
+#define PA_WG_PER_CU 0
+#endif
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ int clamp_ctx(int L, const DecodeParams& p) {
     L = L < 0 ? 0 : L;
-    L = L > p.max_ctx ? p.max_ctx : L;
-    return L;
+    return L > p.max_ctx ? p.max_ctx : L;
 }
 
-template <int DT, int D, int G>
-__global__ __launch_bounds__(kThreads) void pa_partition_valu(DecodeParams p) {
-    using EL = Elem<DT>;
-    constexpr int E = EL::E;
-    constexpr int EPL = 16 / E;        // elements per lane per 16-byte load
-    constexpr int LPR = D / EPL;       // lanes holding one row
-    constexpr int RPI = 64 / LPR;      // rows per wave load instruction
-    constexpr int U = 4;               // row chunks per step
-    constexpr int STEP = U * RPI;      // tokens per step
-    static_assert(LPR >= 8 && LPR <= 64 && RPI * LPR == 64, "row mapping");
+struct Item {
+    int s, kv, pidx, nparts, t0, t1, b0, nblk;
+};
 
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int S = p.num_seqs;
-    int* prefix = reinterpret_cast<int*>(smem);                  // S + 1
-    int* tbl = prefix + ((S + 4) & ~3);                           // kMaxTableSlice
-    float* red = reinterpret_cast<float*>(tbl + kMaxTableSlice);  // kWaves * G * (D + 2)
+// LDS: prefix[(S + 4) & ~3] | tbl[kMaxTableSlice] | red[kWaves * G * (D + 4)]
+__host__ __device__ constexpr size_t red_stride(int d) { return static_cast<size_t>(d) + 4; }
+
+// Prefix sum of partition counts over the batch; every thread takes part.
+// Returns the total number of partitions.
+__device__ int build_prefix(const DecodeParams& p, int* prefix) {
     __shared__ int wave_tot[kWaves];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int rg = lane / LPR;             // row inside a load instruction
-    const int dsl = (lane % LPR) * EPL;    // first head-dim element of the lane
-    const int bs = 1 << p.log2_bs;
-    const int hkv = p.num_kv_heads;
-
-    // ---- prefix sum of partition counts (every workgroup builds its own copy)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int S = p.num_seqs;
     if (tid == 0) prefix[0] = 0;
     int carry = 0;
     for (int base = 0; base < S; base += kThreads) {
@@ -90,46 +101,179 @@ __global__ __launch_bounds__(kThreads) void pa_partition_valu(DecodeParams p) {
         carry += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
         __syncthreads();
     }
-    const int total_items = prefix[S] * hkv;
+    return prefix[S];
+}
 
-    const size_t kv_head_stride = static_cast<size_t>(bs) * D;  // elements
+__device__ __forceinline__ Item locate_item(const DecodeParams& p, const int* prefix, int item) {
+    Item it;
+    const int j = item / p.num_kv_heads;
+    it.kv = item - j * p.num_kv_heads;
+    int lo = 0, hi = p.num_seqs;  // prefix[lo] <= j < prefix[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (prefix[mid] <= j) lo = mid; else hi = mid;
+    }
+    it.s = lo;
+    it.pidx = j - prefix[lo];
+    it.nparts = prefix[lo + 1] - prefix[lo];
+    const int L = clamp_ctx(p.context_lens[lo], p);
+    it.t0 = it.pidx * p.part;
+    it.t1 = min(L, it.t0 + p.part);
+    it.b0 = it.t0 >> p.log2_bs;
+    it.nblk = (it.t1 - it.t0 + (1 << p.log2_bs) - 1) >> p.log2_bs;
+    return it;
+}
+
+__device__ __forceinline__ void stage_table(const DecodeParams& p, const Item& it, int* tbl) {
+    if (static_cast<int>(threadIdx.x) < it.nblk) {
+        int pid = p.block_tables[static_cast<size_t>(it.s) * p.max_blocks + it.b0 + threadIdx.x];
+        pid = pid < 0 ? 0 : (pid >= p.num_blocks ? p.num_blocks - 1 : pid);
+        tbl[threadIdx.x] = pid;
+    }
+}
+
+// Item results are not stored as soon as they are known: every global store
+// holds back the streaming loads issued after it (measured: about 4 us per
+// item on MI355X), so each workgroup keeps the results of up to
+// `ring_slots` items in an LDS ring and writes them out together.
+// Slot layout (floats): o[G][D] | m[G] | l[G] | s, kv, pidx, nparts (as ints).
+__host__ __device__ constexpr int ring_slot_floats(int g, int d) { return ((g * d + 2 * g + 4) + 3) & ~3; }
+
+// The MFMA kernel double-buffers its wave partials (no barrier between an
+// item's combine and the next item's writes) when they are small enough.
+__host__ __device__ constexpr bool mfma_red_double(int g, int d) { return g * d <= 1024; }
+
+// Merge the waves' partial results held in `red` (per wave and head: D
+// weighted V sums, then the running max in log2 units, then the sum of
+// weights) into one ring slot.
+template <int D, int G>
+__device__ __forceinline__ void combine_to_ring(const Item& it, const float* red, float* slot) {
+    constexpr int RS = static_cast<int>(red_stride(D));
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        const int h = idx / D;
+        const int d = idx - h * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * G + h) * RS + D]);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float lsum = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float* r = red + (w * G + h) * RS;
+            const float f = fast_exp2(r[D] - Mu);
+            lsum += r[D + 1] * f;
+            o += r[d] * f;
+        }
+        slot[idx] = lsum > 0.f ? o / lsum : 0.f;
+        if (d == 0) {
+            slot[G * D + h] = M;
+            slot[G * D + G + h] = lsum;
+        }
+    }
+    if (threadIdx.x == 0) {
+        int* meta = reinterpret_cast<int*>(slot + G * D + 2 * G);
+        meta[0] = it.s;
+        meta[1] = it.kv;
+        meta[2] = it.pidx;
+        meta[3] = it.nparts;
+    }
+}
+
+// Write `n` ring slots: a single-partition sequence's rows go to `out`
+// (rounded to the element type), a partition's record to the workspace.
+template <int DT, int D, int G>
+__device__ __forceinline__ void flush_ring(const DecodeParams& p, const float* ring, int n) {
+    using EL = Elem<DT>;
+    constexpr int SL = ring_slot_floats(G, D);
+    for (int i = 0; i < n; ++i) {
+        const float* slot = ring + i * SL;
+        const int* meta = reinterpret_cast<const int*>(slot + G * D + 2 * G);
+        const int s = meta[0], kv = meta[1], pidx = meta[2], nparts = meta[3];
+        const size_t row0 = static_cast<size_t>(s) * p.num_heads + kv * G;  // first query head row
+        if (nparts == 1) {
+            for (int idx = threadIdx.x; idx < G * D; idx += kThreads) EL::store(p.out, row0 * D + idx, slot[idx]);
+        } else {
+            for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+                const int h = idx / D;
+                const int d = idx - h * D;
+                p.ws_o[((row0 + h) * p.pmax + pidx) * D + d] = slot[idx];
+            }
+            if (threadIdx.x < G) {
+                const size_t rec = (row0 + threadIdx.x) * p.pmax + pidx;
+                p.ws_m[rec] = slot[G * D + threadIdx.x];
+                p.ws_l[rec] = slot[G * D + G + threadIdx.x];
+            }
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ T nt_load(const char* base, size_t byte_off) {
+    return __builtin_nontemporal_load(reinterpret_cast<const T*>(base + byte_off));
+}
+
+// ---------------------------------------------------------------------------
+// VALU kernel
+// ---------------------------------------------------------------------------
+
+// Row-group geometry of the VALU kernel for one (element size, D): LPR lanes
+// hold one K row (16 bytes each), RPI row groups per wave, U consecutive
+// tokens per row group and step.
+template <int E, int D>
+struct ValuGeom {
+    static constexpr int EPL = 16 / E;
+    static constexpr int LPR = D / EPL;
+    static constexpr int RPI = 64 / LPR;
+    static constexpr int U = RPI >= 4 ? 4 : 16 / RPI;
+    static constexpr int STEP = RPI * U;
+    static constexpr int VW = U * E / 4;  // 32-bit words of one lane's V^T segment
+};
+
+template <int DT, int D, int G, bool BIGB>
+__global__ __launch_bounds__(kThreads) void pa_decode_valu(DecodeParams p) {
+    using EL = Elem<DT>;
+    constexpr int E = EL::E;
+    using GM = ValuGeom<E, D>;
+    constexpr int EPL = GM::EPL, LPR = GM::LPR, U = GM::U, STEP = GM::STEP, VW = GM::VW;
+    constexpr int RS = static_cast<int>(red_stride(D));
+    static_assert(LPR >= 8 && LPR <= 64 && GM::RPI * LPR == 64, "row mapping");
+    static_assert(VW == 2 || VW % 4 == 0, "V segment is 8 bytes or a multiple of 16");
+    constexpr int NVL = VW == 2 ? 1 : VW / 4;  // loads per V^T segment
+
+    // LDS: prefix | tbl[kMaxTableSlice] | red[kWaves * G * RS] | ring[ring_slots]
+    extern __shared__ __align__(16) unsigned char smem[];
+    int* prefix = reinterpret_cast<int*>(smem);
+    int* tbl = prefix + ((p.num_seqs + 4) & ~3);
+    float* red = reinterpret_cast<float*>(tbl + kMaxTableSlice);
+    float* ring = red + kWaves * G * RS;
+    constexpr int SL = ring_slot_floats(G, D);
+    int nring = 0;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rg = lane / LPR;           // row group: tokens U*rg .. U*rg+U-1 of a step
+    const int li = lane % LPR;
+    const int dsl = li * EPL;            // K side: first head-dim element of the lane
+    const int bs = 1 << p.log2_bs;
+    const int vt = 1 << p.log2_vt;
+    const int hkv = p.num_kv_heads;
+    const size_t blk_el = static_cast<size_t>(bs) * D;  // elements of one (block, head) tile
     const char* kbase = static_cast<const char*>(p.k_cache);
     const char* vbase = static_cast<const char*>(p.v_cache);
 
-    for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
-        const int j = item / hkv;
-        const int kv = item - j * hkv;
-        int lo = 0, hi = S;  // prefix[lo] <= j < prefix[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (prefix[mid] <= j) lo = mid; else hi = mid;
-        }
-        const int s = lo;
-        const int pidx = j - prefix[s];
-        const int nparts = prefix[s + 1] - prefix[s];
-        const int L = clamp_ctx(p.context_lens[s], p);
-        const int t0 = pidx * p.part;
-        const int t1 = min(L, t0 + p.part);
-        const int ntok = t1 - t0;  // 0 only for an empty sequence
-        const int b0 = t0 >> p.log2_bs;
-        const int nblk = (ntok + bs - 1) >> p.log2_bs;
+    const int total_items = build_prefix(p, prefix) * hkv;
 
-        if (tid < nblk) {
-            int pid = p.block_tables[static_cast<size_t>(s) * p.max_blocks + b0 + tid];
-            pid = pid < 0 ? 0 : (pid >= p.num_blocks ? p.num_blocks - 1 : pid);
-            tbl[tid] = pid;
-        }
+    for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+        const Item it = locate_item(p, prefix, item);
+        stage_table(p, it, tbl);
         __syncthreads();
 
-        // query rows of the G heads sharing this KV head, widened to float
         float qv[G][EPL];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const size_t qoff = (static_cast<size_t>(s) * p.num_heads + kv * G + h) * D + dsl;
+            const size_t qoff = (static_cast<size_t>(it.s) * p.num_heads + it.kv * G + h) * D + dsl;
             const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q) + qoff * E);
             EL::to_float(w, qv[h]);
         }
-
         float m[G], l[G], acc[G][EPL];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -138,30 +282,59 @@ __global__ __launch_bounds__(kThreads) void pa_partition_valu(DecodeParams p) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
         }
-
+        const int t1 = it.t1;
+        const int ntok = t1 - it.t0;
         const int nsteps = ntok > 0 ? (ntok + STEP - 1) / STEP : 0;
+        const int last_u = ntok > 0 ? ((t1 - 1) / U) * U : 0;  // first token of the last valid U-group
 
-        auto load_step = [&](int step, u32x4 (&kb)[U], u32x4 (&vb)[U]) {
+        struct Buf {
+            u32x4 k[U];
+            uint32_t v[EPL][NVL * 4];
+        };
+
+        auto load_step = [&](int step, Buf& b) {
+            const int g0 = it.t0 + step * STEP + U * rg;  // first token of this lane's row group
+            const int vtok = min(g0, last_u);
+            int pid;
+            if constexpr (BIGB) {
+                pid = __builtin_amdgcn_readfirstlane(tbl[(min(it.t0 + step * STEP, t1 - 1) >> p.log2_bs) - it.b0]);
+            } else {
+                pid = tbl[(vtok >> p.log2_bs) - it.b0];
+            }
+            const size_t tile = (static_cast<size_t>(pid) * hkv + it.kv) * blk_el;
 #pragma unroll
             for (int c = 0; c < U; ++c) {
-                const int tc = t0 + step * STEP + c * RPI;  // first token of the chunk
-                const int tcc = min(tc, t1 - 1);
-                const int trow = min(tc + rg, t1 - 1);       // this lane's row (clamped)
-                const int pid = __builtin_amdgcn_readfirstlane(tbl[(tcc >> p.log2_bs) - b0]);
-                const size_t tile = (static_cast<size_t>(pid) * hkv + kv) * kv_head_stride;
-                const size_t el = tile + static_cast<size_t>(trow & (bs - 1)) * D + dsl;
-                kb[c] = *reinterpret_cast<const u32x4*>(kbase + el * E);
-                vb[c] = *reinterpret_cast<const u32x4*>(vbase + el * E);
+                const int trow = min(g0 + c, t1 - 1);
+                b.k[c] = nt_load<u32x4>(kbase, (tile + static_cast<size_t>(trow & (bs - 1)) * D + dsl) * E);
+            }
+            const int voff = vtok & (bs - 1);
+            const size_t vt0 = tile + static_cast<size_t>(voff >> p.log2_vt) * D * vt + (voff & (vt - 1));
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const size_t el = vt0 + static_cast<size_t>(li + LPR * e) * vt;
+                if constexpr (VW == 2) {
+                    const u32x2 w = nt_load<u32x2>(vbase, el * E);
+                    b.v[e][0] = w.x;
+                    b.v[e][1] = w.y;
+                } else {
+#pragma unroll
+                    for (int x = 0; x < NVL; ++x) {
+                        const u32x4 w = nt_load<u32x4>(vbase, el * E + 16 * x);
+                        b.v[e][4 * x] = w.x; b.v[e][4 * x + 1] = w.y;
+                        b.v[e][4 * x + 2] = w.z; b.v[e][4 * x + 3] = w.w;
+                    }
+                }
             }
         };
 
-        auto compute_step = [&](int step, const u32x4 (&kb)[U], const u32x4 (&vb)[U]) {
+        auto compute_step = [&](int step, const Buf& b) {
+            const int g0 = it.t0 + step * STEP + U * rg;
             float x[U][G];
 #pragma unroll
             for (int c = 0; c < U; ++c) {
                 float kf[EPL];
-                EL::to_float(kb[c], kf);
-                const bool valid = (t0 + step * STEP + c * RPI + rg) < t1;
+                EL::to_float(b.k[c], kf);
+                const bool valid = g0 + c < t1;
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     float d = 0.f;
@@ -192,30 +365,46 @@ __global__ __launch_bounds__(kThreads) void pa_partition_valu(DecodeParams p) {
                 for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
             }
 #pragma unroll
-            for (int c = 0; c < U; ++c) {
-                float vf[EPL];
-                EL::to_float(vb[c], vf);
+            for (int e = 0; e < EPL; ++e) {
+                float vf[U];
+                // tokens of this lane's segment past the context may hold
+                // anything (NaN included): zero them so 0 * v stays 0
+                if constexpr (E == 4) {
+#pragma unroll
+                    for (int c = 0; c < U; ++c) vf[c] = g0 + c < t1 ? u32_as_f32(b.v[e][c]) : 0.f;
+                } else {
+#pragma unroll
+                    for (int c = 0; c < U; ++c) {
+                        const uint32_t w = b.v[e][c >> 1];
+                        const uint32_t half = (c & 1) ? (w >> 16) : (w & 0xffffu);
+                        float f;
+                        if constexpr (DT == PA_BF16) f = u32_as_f32(half << 16);
+                        else f = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(half)));
+                        vf[c] = g0 + c < t1 ? f : 0.f;
+                    }
+                }
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
+                    float a = acc[h][e];
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pw[c][h], vf[e], acc[h][e]);
+                    for (int c = 0; c < U; ++c) a = fmaf(pw[c][h], vf[c], a);
+                    acc[h][e] = a;
                 }
             }
         };
 
-        // double-buffered walk over this wave's steps
         int s0 = wave;
         if (s0 < nsteps) {
-            u32x4 ka[U], va[U], kb2[U], vb2[U];
-            load_step(s0, ka, va);
+            Buf ba, bb;
+            load_step(s0, ba);
             while (true) {
                 const int s1 = s0 + kWaves;
-                if (s1 < nsteps) load_step(s1, kb2, vb2);
-                compute_step(s0, ka, va);
+                if (s1 < nsteps) load_step(s1, bb);
+                compute_step(s0, ba);
                 if (s1 >= nsteps) break;
                 s0 = s1 + kWaves;
-                if (s0 < nsteps) load_step(s0, ka, va);
-                compute_step(s1, kb2, vb2);
+                if (s0 < nsteps) load_step(s0, ba);
+                compute_step(s1, bb);
                 if (s0 >= nsteps) break;
             }
         }
@@ -230,19 +419,19 @@ __global__ __launch_bounds__(kThreads) void pa_partition_valu(DecodeParams p) {
                 const float mn = fmaxf(m[h], mo);
                 const float mu = mn == -INFINITY ? 0.f : mn;
                 const float a = fast_exp2(m[h] - mu);
-                const float b = fast_exp2(mo - mu);
-                l[h] = l[h] * a + lo2 * b;
+                const float b2 = fast_exp2(mo - mu);
+                l[h] = l[h] * a + lo2 * b2;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * a + __shfl_xor(acc[h][e], off) * b;
+                for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * a + __shfl_xor(acc[h][e], off) * b2;
                 m[h] = mn;
             }
         }
         if (lane < LPR) {
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                float* r = red + (wave * G + h) * (D + 2);
+                float* r = red + (wave * G + h) * RS;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) r[dsl + e] = acc[h][e];
+                for (int e = 0; e < EPL; ++e) r[li + LPR * e] = acc[h][e];
                 if (lane == 0) {
                     r[D] = m[h];
                     r[D + 1] = l[h];
@@ -250,37 +439,314 @@ __global__ __launch_bounds__(kThreads) void pa_partition_valu(DecodeParams p) {
             }
         }
         __syncthreads();
+        combine_to_ring<D, G>(it, red, ring + nring * SL);
+        ++nring;
+        if (nring == p.ring_slots || item + static_cast<int>(gridDim.x) >= total_items) {
+            __syncthreads();
+            flush_ring<DT, D, G>(p, ring, nring);
+            nring = 0;
+        }
+        __syncthreads();
+    }
+}
 
-        // merge the waves and write the partition's result
-        for (int idx = tid; idx < G * D; idx += kThreads) {
-            const int h = idx / D;
-            const int d = idx - h * D;
-            float M = -INFINITY;
+// ---------------------------------------------------------------------------
+// MFMA kernel (grouped query heads, bfloat16 / float16)
+// ---------------------------------------------------------------------------
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_qk(const u32x4& a, const u32x4& b, f32x4_t c) {
+    if constexpr (DT == PA_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_pv(const u32x2& a, const u32x2& b, f32x4_t c) {
+    if constexpr (DT == PA_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                         __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                     __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+}
+
+// Two probabilities packed as the MFMA element type (round to nearest even);
+// ra / rb return the rounded values so that the softmax denominator sums
+// exactly the weights the numerator multiplies.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b, float& ra, float& rb) {
+    if constexpr (DT == PA_BF16) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+        const uint32_t w = __builtin_bit_cast(uint32_t, v);
+        ra = u32_as_f32(w << 16);
+        rb = u32_as_f32(w & 0xffff0000u);
+        return w;
+    } else {
+        typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+        const f16x2_t v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+        ra = static_cast<float>(v.x);
+        rb = static_cast<float>(v.y);
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+template <int DT, int D, int G, bool BIGB>
+__global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
+    static_assert(DT == PA_BF16 || DT == PA_F16, "MFMA path is for 16-bit elements");
+    static_assert(G == 2 || G == 4 || G == 8 || G == 16, "group size");
+    constexpr int E = 2;
+    constexpr int NK = D / 32;   // 16x16x32 products for S^T
+    constexpr int NV = D / 16;   // 16x16x16 products for O^T
+    constexpr int RS = static_cast<int>(red_stride(D));
+    constexpr int QW = G * D / 2;                    // 32-bit words of one item's query block
+    constexpr int QPT = (QW + kThreads - 1) / kThreads;
+    constexpr float kLazy = 8.f;  // rescale only when the max grows by more than 2^8
+    constexpr bool kRed2 = mfma_red_double(G, D);
+
+    // LDS: prefix | tbl[2][kMaxTableSlice] | qs[2][QW] | red[1 or 2][kWaves * G * RS] | ring[ring_slots]
+    extern __shared__ __align__(16) unsigned char smem[];
+    int* prefix = reinterpret_cast<int*>(smem);
+    int* tbl2 = prefix + ((p.num_seqs + 4) & ~3);
+    uint32_t* qs2 = reinterpret_cast<uint32_t*>(tbl2 + 2 * kMaxTableSlice);
+    float* red2 = reinterpret_cast<float*>(qs2 + 2 * ((QW + 3) & ~3));
+    float* ring = red2 + (kRed2 ? 2 : 1) * kWaves * G * RS;
+    constexpr int SL = ring_slot_floats(G, D);
+    int nring = 0;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15;  // K row of the tile (A) / head column (B, C)
+    const int j = lane >> 4;    // 8-element chunk of K / 4-token group of V and S
+    const int bs = 1 << p.log2_bs;
+    const int vt = 1 << p.log2_vt;
+    const int hkv = p.num_kv_heads;
+    const size_t blk_el = static_cast<size_t>(bs) * D;
+    const char* kbase = static_cast<const char*>(p.k_cache);
+    const char* vbase = static_cast<const char*>(p.v_cache);
+    const uint32_t* qwords = static_cast<const uint32_t*>(p.q);
+
+    const int total_items = build_prefix(p, prefix) * hkv;
+    int item = blockIdx.x;
+    if (item >= total_items) return;
+
+    struct Buf {
+        u32x4 k[NK];
+        u32x2 v[NV];
+    };
+    auto ntiles_of = [](const Item& x) { return x.t1 > x.t0 ? (x.t1 - x.t0 + 15) >> 4 : 0; };
+    auto last4_of = [](const Item& x) { return x.t1 > x.t0 ? ((x.t1 - 1) >> 2) << 2 : 0; };
+    auto q_word0 = [&](const Item& x) {
+        return (static_cast<size_t>(x.s) * p.num_heads + x.kv * G) * (D / 2);
+    };
+    auto clamp_pid = [&](int pid) { return pid < 0 ? 0 : (pid >= p.num_blocks ? p.num_blocks - 1 : pid); };
+
+    // K/V loads of one 16-token tile. `pk`/`pv` are this lane's physical
+    // blocks for its K row and its 4-token V group.
+    auto load_with = [&](const Item& x, int tile, int pk, int pv, Buf& b) {
+        const int t1 = x.t1;
+        const int tt0 = x.t0 + 16 * tile;
+        const int krow = min(tt0 + r16, t1 - 1);
+        const int vtok = min(tt0 + 4 * j, last4_of(x));
+        if constexpr (BIGB) {
+            // the tile lies in one block and one 16-token V tile: scalar
+            // bases, 32-bit lane offsets, immediate offsets per load
+            const int pid = __builtin_amdgcn_readfirstlane(pk);
+            const size_t tile_el = (static_cast<size_t>(pid) * hkv + x.kv) * blk_el;
+            const char* kt = kbase + tile_el * E;
+            const char* vtp = vbase + (tile_el + static_cast<size_t>((tt0 & (bs - 1)) >> 4) * D * 16) * E;
+            const uint32_t ko = static_cast<uint32_t>(((krow & (bs - 1)) * D + 8 * j) * E);
+            const uint32_t vo = static_cast<uint32_t>(((vtok & 15) + 16 * r16) * E);
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * G + h) * (D + 2) + D]);
-            const float Mu = M == -INFINITY ? 0.f : M;
-            float lsum = 0.f, o = 0.f;
+            for (int c = 0; c < NK; ++c) b.k[c] = nt_load<u32x4>(kt, ko + 64 * c);
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float* r = red + (w * G + h) * (D + 2);
-                const float f = fast_exp2(r[D] - Mu);
-                lsum += r[D + 1] * f;
-                o += r[d] * f;
+            for (int v = 0; v < NV; ++v) b.v[v] = nt_load<u32x2>(vtp, vo + 512 * v);
+        } else {
+            const size_t kel = (static_cast<size_t>(pk) * hkv + x.kv) * blk_el +
+                               static_cast<size_t>(krow & (bs - 1)) * D + 8 * j;
+#pragma unroll
+            for (int c = 0; c < NK; ++c) b.k[c] = nt_load<u32x4>(kbase, (kel + 32 * c) * E);
+            const int voff = vtok & (bs - 1);
+            const size_t vel = (static_cast<size_t>(pv) * hkv + x.kv) * blk_el +
+                               static_cast<size_t>(voff >> p.log2_vt) * D * vt + (voff & (vt - 1)) +
+                               static_cast<size_t>(r16) * vt;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                b.v[v] = nt_load<u32x2>(vbase, (vel + static_cast<size_t>(16 * v) * vt) * E);
+        }
+    };
+    // tile of the current item: physical blocks from the LDS table slice
+    auto load_tile = [&](const Item& x, const int* tbl, int tile, Buf& b) {
+        const int tt0 = x.t0 + 16 * tile;
+        int pk, pv;
+        if constexpr (BIGB) {
+            pk = pv = tbl[(min(tt0, x.t1 - 1) >> p.log2_bs) - x.b0];
+        } else {
+            pk = tbl[(min(tt0 + r16, x.t1 - 1) >> p.log2_bs) - x.b0];
+            pv = tbl[(min(tt0 + 4 * j, last4_of(x)) >> p.log2_bs) - x.b0];
+        }
+        load_with(x, tile, pk, pv, b);
+    };
+
+    // ---- prologue: stage the first item's table slice and query block
+    Item cur = locate_item(p, prefix, item);
+    stage_table(p, cur, tbl2);
+    for (int w = tid; w < QW; w += kThreads) qs2[w] = qwords[q_word0(cur) + w];
+    __syncthreads();
+    Buf A, B;
+    bool start_b = false;
+    if (wave < ntiles_of(cur)) load_tile(cur, tbl2, wave, A);
+
+    for (int k = 0;; ++k) {
+        const int buf = k & 1;
+        const int* tbl = tbl2 + buf * kMaxTableSlice;
+        const bool has_next = item + static_cast<int>(gridDim.x) < total_items;
+        Item nxt = cur;
+        int tbl_reg = 0, pk_n = 0, pv_n = 0;
+        uint32_t q_reg[QPT];
+        bool next_tile = false;
+        if (has_next) {
+            // stage the next item while this one streams: its table slice and
+            // query block into registers (written to LDS at the end of this
+            // item), and this wave's blocks for its first tile of it
+            nxt = locate_item(p, prefix, item + gridDim.x);
+            const int* trow = p.block_tables + static_cast<size_t>(nxt.s) * p.max_blocks + nxt.b0;
+            if (tid < nxt.nblk) tbl_reg = clamp_pid(trow[tid]);
+#pragma unroll
+            for (int i = 0; i < QPT; ++i) {
+                const int w = tid + i * kThreads;
+                q_reg[i] = w < QW ? qwords[q_word0(nxt) + w] : 0u;
             }
-            const float res = lsum > 0.f ? o / lsum : 0.f;
-            const int hq = kv * G + h;
-            if (nparts == 1) {
-                EL::store(p.out, (static_cast<size_t>(s) * p.num_heads + hq) * D + d, res);
-            } else {
-                const size_t rec = (static_cast<size_t>(s) * p.num_heads + hq) * p.pmax + pidx;
-                p.ws_o[rec * D + d] = res;
-                if (d == 0) {
-                    p.ws_m[rec] = M;
-                    p.ws_l[rec] = lsum;
-                }
+            next_tile = wave < ntiles_of(nxt);
+            if (next_tile) {
+                const int tt0 = nxt.t0 + 16 * wave;
+                pk_n = clamp_pid(trow[(min(tt0 + r16, nxt.t1 - 1) >> p.log2_bs) - nxt.b0]);
+                pv_n = clamp_pid(trow[(min(tt0 + 4 * j, last4_of(nxt)) >> p.log2_bs) - nxt.b0]);
+            }
+        }
+
+        // query fragments of this item from LDS: column r16 is head (r16 % G)
+        u32x4 qf[NK];
+        {
+            const uint32_t* qrow = qs2 + buf * ((QW + 3) & ~3) + (r16 % G) * (D / 2);
+#pragma unroll
+            for (int c = 0; c < NK; ++c) qf[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c + 4 * j);
+        }
+        f32x4_t acc[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        float m_run = -INFINITY, lsum = 0.f;
+        const int t1 = cur.t1;
+        const int ntiles = ntiles_of(cur);
+
+        auto compute_tile = [&](int tile, const Buf& b) {
+            const int tt0 = cur.t0 + 16 * tile;
+            f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NK; ++c) st = mfma_qk<DT>(b.k[c], qf[c], st);
+            // st[r] = S^T[token tt0 + 4j + r][head column r16]
+            float x[4];
+            bool valid[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                valid[r] = tt0 + 4 * j + r < t1;
+                x[r] = valid[r] ? st[r] * p.scale_log2 : -INFINITY;
+            }
+            float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const bool need = tmax > m_run + kLazy;
+            if (__any(need)) {
+                const float mn = need ? tmax : m_run;
+                const float alpha = fast_exp2(m_run - mn);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) acc[v] *= alpha;
+                lsum *= alpha;
+                m_run = mn;
+            }
+            float pr[4];
+            u32x2 pb;
+            pb.x = pack2<DT>(fast_exp2(x[0] - m_run), fast_exp2(x[1] - m_run), pr[0], pr[1]);
+            pb.y = pack2<DT>(fast_exp2(x[2] - m_run), fast_exp2(x[3] - m_run), pr[2], pr[3]);
+            lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            // V^T values of tokens past the context may hold anything: zero them
+            const uint32_t mask0 = (valid[0] ? 0xffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
+            const uint32_t mask1 = (valid[2] ? 0xffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                u32x2 a = b.v[v];
+                a.x &= mask0;
+                a.y &= mask1;
+                acc[v] = mfma_pv<DT>(a, pb, acc[v]);
+            }
+        };
+
+        // this wave's tiles of the item; the buffer after the last one takes
+        // the wave's first tile of the next item. Returns true when that
+        // tile went to Y.
+        auto run = [&](Buf& X, Buf& Y) -> bool {
+            int tile = wave;
+            while (true) {
+                int tn = tile + kWaves;
+                if (tn < ntiles) load_tile(cur, tbl, tn, Y);
+                else if (next_tile) load_with(nxt, wave, pk_n, pv_n, Y);
+                compute_tile(tile, X);
+                tile = tn;
+                if (tile >= ntiles) return true;
+                tn = tile + kWaves;
+                if (tn < ntiles) load_tile(cur, tbl, tn, X);
+                else if (next_tile) load_with(nxt, wave, pk_n, pv_n, X);
+                compute_tile(tile, Y);
+                tile = tn;
+                if (tile >= ntiles) return false;
+            }
+        };
+        if (wave < ntiles) {
+            const bool r = start_b ? run(B, A) : run(A, B);
+            start_b = start_b ? !r : r;
+        } else {
+            if (next_tile) load_with(nxt, wave, pk_n, pv_n, A);
+            start_b = false;
+        }
+
+        // acc[v][r] = O^T[d = 16v + 4j + r][head column r16]; lsum covers this
+        // lane's 4-token groups only: total it over the four lanes of the column
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+        float* red = red2 + (kRed2 ? buf : 0) * (kWaves * G * RS);
+        if (r16 < G) {
+            float* r = red + (wave * G + r16) * RS;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) *reinterpret_cast<f32x4_t*>(r + 16 * v + 4 * j) = acc[v];
+            if (j == 0) {
+                r[D] = m_run;
+                r[D + 1] = lsum;
+            }
+        }
+        if (has_next) {
+            if (tid < nxt.nblk) tbl2[(buf ^ 1) * kMaxTableSlice + tid] = tbl_reg;
+            uint32_t* qn = qs2 + (buf ^ 1) * ((QW + 3) & ~3);
+#pragma unroll
+            for (int i = 0; i < QPT; ++i) {
+                const int w = tid + i * kThreads;
+                if (w < QW) qn[w] = q_reg[i];
             }
         }
         __syncthreads();
+        combine_to_ring<D, G>(cur, red, ring + nring * SL);
+        ++nring;
+        if constexpr (!kRed2) __syncthreads();  // the next item rewrites the single partials buffer
+        if (nring == p.ring_slots || !has_next) {
+            __syncthreads();
+            flush_ring<DT, D, G>(p, ring, nring);
+            nring = 0;
+        }
+        if (!has_next) break;
+        cur = nxt;
+        item += gridDim.x;
     }
 }
 
@@ -326,15 +792,47 @@ __global__ __launch_bounds__(64) void pa_merge(DecodeParams p) {
 
 namespace {
 
-template <int DT, int D, int G>
-hipError_t launch_part(const DecodeParams& p, int num_cus, hipStream_t stream) {
-    const size_t smem = (static_cast<size_t>((p.num_seqs + 4) & ~3) + kMaxTableSlice) * sizeof(int) +
-                        static_cast<size_t>(kWaves) * G * (D + 2) * sizeof(float);
-    auto kern = pa_partition_valu<DT, D, G>;
+// LDS per compute unit; the result ring gets what the resident workgroups
+// (as many as the kernel's registers allow) leave over.
+constexpr size_t kLdsPerCu = 160 * 1024;
+constexpr int kMaxRingSlots = 32;
+
+// Ring slots that fit next to `fixed` bytes of LDS when `resident`
+// workgroups share a compute unit.
+int ring_slots_for(size_t fixed, int d, int g, int resident) {
+    const size_t budget = kLdsPerCu / static_cast<size_t>(resident < 1 ? 1 : resident) - 512;
+    const size_t slot = static_cast<size_t>(ring_slot_floats(g, d)) * sizeof(float);
+    long long n = fixed < budget ? static_cast<long long>((budget - fixed) / slot) : 0;
+    if (n < 1) n = 1;
+    if (n > kMaxRingSlots) n = kMaxRingSlots;
+    return static_cast<int>(n);
+}
+
+size_t decode_smem_valu(int num_seqs, int d, int g) {
+    return (static_cast<size_t>((num_seqs + 4) & ~3) + kMaxTableSlice) * sizeof(int) +
+           static_cast<size_t>(kWaves) * g * red_stride(d) * sizeof(float);
+}
+
+size_t decode_smem_mfma(int num_seqs, int d, int g) {
+    // prefix | two table slices | two query blocks | two sets of wave partials
+    const size_t qw = ((static_cast<size_t>(g) * d / 2 + 3) & ~static_cast<size_t>(3));
+    return (static_cast<size_t>((num_seqs + 4) & ~3) + 2 * kMaxTableSlice) * sizeof(int) +
+           2 * qw * sizeof(uint32_t) +
+           (mfma_red_double(g, d) ? 2 : 1) * static_cast<size_t>(kWaves) * g * red_stride(d) * sizeof(float);
+}
+
+// Launch a persistent kernel: as many workgroups as can be resident, with
+// the result ring sized to the LDS the resident workgroups leave free.
+template <typename K>
+hipError_t launch_persistent(K kern, DecodeParams p, size_t fixed_smem, int d, int g, int num_cus,
+                             hipStream_t stream) {
     int occ = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, smem);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, fixed_smem);
     if (e != hipSuccess) return e;
     if (occ < 1) occ = 1;
+    if (PA_WG_PER_CU > 0 && occ > PA_WG_PER_CU) occ = PA_WG_PER_CU;
+    p.ring_slots = ring_slots_for(fixed_smem, d, g, occ);
+    const size_t smem = fixed_smem + static_cast<size_t>(p.ring_slots) * ring_slot_floats(g, d) * sizeof(float);
     const long long upper = static_cast<long long>(p.num_seqs) * p.num_kv_heads * p.pmax;
     long long grid = static_cast<long long>(num_cus) * occ;
     if (grid > upper) grid = upper;
@@ -343,23 +841,50 @@ hipError_t launch_part(const DecodeParams& p, int num_cus, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int DT, int D, int G>
+hipError_t launch_valu(const DecodeParams& p, int num_cus, hipStream_t stream) {
+    constexpr int step = ValuGeom<Elem<DT>::E, D>::STEP;
+    const size_t fixed = decode_smem_valu(p.num_seqs, D, G);
+    if ((1 << p.log2_bs) >= step)
+        return launch_persistent(pa_decode_valu<DT, D, G, true>, p, fixed, D, G, num_cus, stream);
+    return launch_persistent(pa_decode_valu<DT, D, G, false>, p, fixed, D, G, num_cus, stream);
+}
+
+template <int DT, int D, int G>
+hipError_t launch_mfma(const DecodeParams& p, int num_cus, hipStream_t stream) {
+    const size_t fixed = decode_smem_mfma(p.num_seqs, D, G);
+    if ((1 << p.log2_bs) >= 16)
+        return launch_persistent(pa_decode_mfma<DT, D, G, true>, p, fixed, D, G, num_cus, stream);
+    return launch_persistent(pa_decode_mfma<DT, D, G, false>, p, fixed, D, G, num_cus, stream);
+}
+
 template <int DT, int D>
-hipError_t launch_part_g(const DecodeParams& p, int num_cus, hipStream_t stream) {
-    switch (p.group) {
-        case 1: return launch_part<DT, D, 1>(p, num_cus, stream);
-        case 2: return launch_part<DT, D, 2>(p, num_cus, stream);
-        case 4: return launch_part<DT, D, 4>(p, num_cus, stream);
-        case 8: return launch_part<DT, D, 8>(p, num_cus, stream);
+hipError_t launch_d(const DecodeParams& p, int num_cus, hipStream_t stream) {
+    if constexpr (DT == PA_F32) {
+        switch (p.group) {
+            case 1: return launch_valu<DT, D, 1>(p, num_cus, stream);
+            case 2: return launch_valu<DT, D, 2>(p, num_cus, stream);
+            case 4: return launch_valu<DT, D, 4>(p, num_cus, stream);
+            case 8: return launch_valu<DT, D, 8>(p, num_cus, stream);
+        }
+    } else {
+        switch (p.group) {
+            case 1: return launch_valu<DT, D, 1>(p, num_cus, stream);
+            case 2: return launch_mfma<DT, D, 2>(p, num_cus, stream);
+            case 4: return launch_mfma<DT, D, 4>(p, num_cus, stream);
+            case 8: return launch_mfma<DT, D, 8>(p, num_cus, stream);
+            case 16: return launch_mfma<DT, D, 16>(p, num_cus, stream);
+        }
     }
     return hipErrorInvalidValue;
 }
 
 template <int DT>
-hipError_t launch_part_d(const DecodeParams& p, int head_dim, int num_cus, hipStream_t stream) {
+hipError_t launch_dt(const DecodeParams& p, int head_dim, int num_cus, hipStream_t stream) {
     switch (head_dim) {
-        case 64: return launch_part_g<DT, 64>(p, num_cus, stream);
-        case 128: return launch_part_g<DT, 128>(p, num_cus, stream);
-        case 256: return launch_part_g<DT, 256>(p, num_cus, stream);
+        case 64: return launch_d<DT, 64>(p, num_cus, stream);
+        case 128: return launch_d<DT, 128>(p, num_cus, stream);
+        case 256: return launch_d<DT, 256>(p, num_cus, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -378,19 +903,30 @@ hipError_t launch_merge_d(const DecodeParams& p, int head_dim, hipStream_t strea
 
 }  // namespace
 
+bool decode_uses_mfma(pa_dtype_t dt, int group) { return dt != PA_F32 && group >= 2; }
+
+int decode_min_block_size(pa_dtype_t dt, int head_dim, int group) {
+    if (decode_uses_mfma(dt, group)) return 4;
+    const int e = dt == PA_F32 ? 4 : 2;
+    const int lpr = head_dim / (16 / e);
+    const int rpi = 64 / lpr;
+    const int u = rpi >= 4 ? 4 : 16 / rpi;
+    return rpi > u ? rpi : u;
+}
+
 bool decode_supported(pa_dtype_t dt, int head_dim, int group) {
-    const bool d_ok = head_dim == 64 || head_dim == 128 || head_dim == 256;
-    const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8;
-    const bool t_ok = dt == PA_F32 || dt == PA_BF16 || dt == PA_F16;
-    return d_ok && g_ok && t_ok;
+    if (!(head_dim == 64 || head_dim == 128 || head_dim == 256)) return false;
+    if (dt == PA_F32) return group == 1 || group == 2 || group == 4 || group == 8;
+    if (dt == PA_BF16 || dt == PA_F16) return group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
+    return false;
 }
 
 hipError_t launch_decode_partitions(const DecodeParams& p, pa_dtype_t dt, int head_dim,
                                     int num_cus, hipStream_t stream) {
     switch (dt) {
-        case PA_F32: return launch_part_d<PA_F32>(p, head_dim, num_cus, stream);
-        case PA_BF16: return launch_part_d<PA_BF16>(p, head_dim, num_cus, stream);
-        case PA_F16: return launch_part_d<PA_F16>(p, head_dim, num_cus, stream);
+        case PA_F32: return launch_dt<PA_F32>(p, head_dim, num_cus, stream);
+        case PA_BF16: return launch_dt<PA_BF16>(p, head_dim, num_cus, stream);
+        case PA_F16: return launch_dt<PA_F16>(p, head_dim, num_cus, stream);
     }
     return hipErrorInvalidValue;
 }

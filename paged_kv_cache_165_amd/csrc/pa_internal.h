@@ -32,27 +32,27 @@ struct DecodeParams {
     int part;           // tokens per partition
     int pmax;           // ceil(max_ctx / part), >= 1
     int log2_bs;        // block size = 1 << log2_bs
+    int log2_vt;        // tokens per transposed V tile = min(block size, 16)
+    int ring_slots;     // item results a workgroup buffers in LDS before storing them
 };
 
-// Number of tokens per wave row-chunk of the VALU kernel for (dtype, D):
-// a 16-byte lane load covers 16 / E elements, so one row of D elements spans
-// D * E / 16 lanes and a wave covers 1024 / (D * E) rows per instruction.
-inline int rows_per_wave_load(pa_dtype_t dt, int head_dim) {
-    int e = dt == PA_F32 ? 4 : 2;
-    return 1024 / (head_dim * e);
-}
+// Tokens per transposed V tile: V rows of a block are stored as tiles of
+// this many tokens, head_dim-major.
+inline int v_tile_tokens(int block_size) { return block_size < 16 ? block_size : 16; }
 
-// Returns hipSuccess or the launch error. `grid` <= 0 selects the
-// persistent grid size from the occupancy of the chosen kernel.
+// Return hipSuccess or the launch error.
 hipError_t launch_decode_partitions(const DecodeParams& p, pa_dtype_t dt, int head_dim,
                                     int num_cus, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams& p, pa_dtype_t dt, int head_dim,
                                hipStream_t stream);
 bool decode_supported(pa_dtype_t dt, int head_dim, int group);
+bool decode_uses_mfma(pa_dtype_t dt, int group);
+int decode_min_block_size(pa_dtype_t dt, int head_dim, int group);
 
 hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                               const int32_t* slots, int num_tokens, int num_kv_heads,
-                              int row_bytes, int block_size, int num_blocks, hipStream_t stream);
+                              int head_dim, int elem_bytes, int block_size, int num_blocks,
+                              hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
                               size_t block_bytes, int num_blocks, hipStream_t stream);
 

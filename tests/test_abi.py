@@ -44,13 +44,13 @@ def test_status_strings_and_workspace_size():
     lib, L = _lib()
     assert lib.pa_status_string(0) == b"ok"
     assert lib.pa_status_string(3) == b"workspace missing or too small"
-    assert lib.pa_default_partition_size() == 512
+    assert lib.pa_default_partition_size() == 1024
     # single partition: no workspace needed
-    assert lib.pa_decode_workspace_size(4, 8, 128, 512, 0) == 0
+    assert lib.pa_decode_workspace_size(4, 8, 128, 1024, 0) == 0
     # records of (m, l, o[D]) floats, each region 256-byte aligned
     recs = 4 * 8 * 3
     a = lambda x: (x + 255) // 256 * 256
-    assert lib.pa_decode_workspace_size(4, 8, 128, 1100, 0) == a(recs * 4) * 2 + a(recs * 128 * 4)
+    assert lib.pa_decode_workspace_size(4, 8, 128, 1100, 512) == a(recs * 4) * 2 + a(recs * 128 * 4)
     assert lib.pa_decode_workspace_size(-1, 8, 128, 1100, 0) == 0
 
 
@@ -66,7 +66,8 @@ def _decode(lib, **over):
 
 @pytest.mark.parametrize("over,status,msg", [
     (dict(Hq=7), 1, b"multiple of num_kv_heads"),
-    (dict(Hq=32, Hkv=2), 2, b"no kernel"),          # group 16
+    (dict(Hq=64, Hkv=2), 2, b"no kernel"),          # group 32
+    (dict(Hq=32, Hkv=2, dtype=0), 2, b"no kernel"), # float32 group 16
     (dict(D=96), 2, b"no kernel"),
     (dict(bs=12), 2, b"power of two"),
     (dict(bs=0), 1, b"zero size"),
@@ -76,7 +77,7 @@ def _decode(lib, **over):
     (dict(dtype=7), 1, b"unknown dtype"),
     (dict(q=0), 1, b"null pointer"),
     (dict(out=8), 1, b"16-byte aligned"),
-    (dict(maxctx=2000, maxblk=200), 3, b"workspace"),
+    (dict(maxctx=3000, maxblk=200), 3, b"workspace"),
     (dict(scale=float("inf")), 1, b"scale"),
     (dict(S=9000), 2, b"num_seqs"),
 ])

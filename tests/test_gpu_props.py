@@ -48,13 +48,15 @@ def make_case(lens, hq, hkv, d, bs, dtype, seed, pool=None, trap_nan=True):
         k += n
     g = torch.Generator(device=DEV).manual_seed(seed)
     rn = lambda *s: torch.randn(*s, generator=g, device=DEV).to(dtype)
+    t = min(bs, 16)
     q = rn(len(lens), hq, d)
     kc = rn(nb, hkv, bs, d)
-    vc = rn(nb, hkv, bs, d)
+    vc = rn(nb, hkv, bs // t, d, t)   # transposed V tiles
     if trap_nan:
-        m = torch.from_numpy(valid).to(DEV).view(nb, 1, bs, 1)
-        kc = torch.where(m, kc, torch.full((), float("nan"), dtype=dtype, device=DEV))
-        vc = torch.where(m, vc, torch.full((), float("nan"), dtype=dtype, device=DEV))
+        m = torch.from_numpy(valid).to(DEV)
+        nan = torch.full((), float("nan"), dtype=dtype, device=DEV)
+        kc = torch.where(m.view(nb, 1, bs, 1), kc, nan)
+        vc = torch.where(m.view(nb, 1, bs // t, 1, t), vc, nan)
     return dict(q=q, kc=kc, vc=vc, tables=tables, lens=np.array(lens, np.int32), bs=bs)
 
 
@@ -83,6 +85,9 @@ MATRIX = [(dt, d, g) for dt in (torch.float32, torch.bfloat16, torch.float16)
           for d in (64, 128, 256) for g in (1, 2, 4, 8)]
 
 
+MATRIX += [(torch.bfloat16, d, 16) for d in (64, 128, 256)] + [(torch.float16, 128, 16)]
+
+
 @pytest.mark.parametrize("dt,d,g", MATRIX, ids=[f"{str(dt)[6:]}-D{d}-g{g}" for dt, d, g in MATRIX])
 def test_dtype_headdim_group_matrix(dt, d, g):
     hkv = 2
@@ -103,12 +108,25 @@ def test_partition_sizes(part):
 
 
 @pytest.mark.parametrize("bs", [4, 8, 16, 32, 64, 128, 256])
-def test_block_sizes(bs):
+@pytest.mark.parametrize("g", [1, 4])
+def test_block_sizes(bs, g):
     lens = [3, 64, 129, 1000, 2049]
-    c = make_case(lens, 8, 8, 128, bs, torch.bfloat16, seed=bs)
+    c = make_case(lens, 2 * g, 2, 128, bs, torch.bfloat16, seed=bs + g)
     part = max(512, bs)
     out = run_gpu(c, 0.09, part=part)
-    compare_attention(out, run_oracle(c, 0.09), f"bs {bs}")
+    compare_attention(out, run_oracle(c, 0.09), f"bs {bs} g {g}")
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("dt,d", [(torch.float32, 128), (torch.float32, 256), (torch.bfloat16, 256),
+                                  (torch.bfloat16, 64), (torch.float16, 64)])
+def test_block_sizes_wide_rows(bs, dt, d):
+    """Row geometries of the VALU kernel other than 256-byte rows."""
+    if dt == torch.float32 and d == 256 and bs < 16:
+        pytest.skip("float32 head_dim 256 needs blocks of at least 16 tokens")
+    c = make_case([5, 100, 700], 4, 4, d, bs, dt, seed=bs + d)
+    out = run_gpu(c, 0.1)
+    compare_attention(out, run_oracle(c, 0.1), f"{dt} D{d} bs {bs}")
 
 
 def test_permutation_invariance_bitwise():

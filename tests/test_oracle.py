@@ -90,8 +90,17 @@ def test_bf16_decoding_of_known_patterns():
 # Attention pins, written against a decode callable
 # ---------------------------------------------------------------------------
 
+def vstore(v_logical: np.ndarray) -> np.ndarray:
+    """Logical V [NB, Hkv, B, D] -> the transposed tile storage
+    [NB, Hkv, B // T, D, T] with T = min(B, 16) (test-side conversion)."""
+    nb, hkv, bs, d = v_logical.shape
+    t = min(bs, 16)
+    return np.ascontiguousarray(v_logical.reshape(nb, hkv, bs // t, t, d).transpose(0, 1, 2, 4, 3))
+
+
 def _decode(q, kc, vc, tables, lens, scale, bs, dtype=F32):
-    return oracle.paged_decode(q, kc, vc, tables, lens, scale, bs, dtype)
+    """The pins pass logical V; the oracle reads the storage layout."""
+    return oracle.paged_decode(q, kc, vstore(vc), tables, lens, scale, bs, dtype)
 
 
 def pin_slot_id_probe(decode):
@@ -278,7 +287,8 @@ def pin_prefix_sharing(decode):
     nb, hkv, bs, d = 12, 2, 4, 8
     kc = rng.standard_normal((nb, hkv, bs, d)).astype(np.float32)
     vc = rng.standard_normal((nb, hkv, bs, d)).astype(np.float32)
-    kc2, vc2 = oracle.copy_blocks(kc, vc, [[0, 5], [1, 6]])
+    kc2, vc2 = kc.copy(), vc.copy()  # logical copies of blocks 0, 1 into 5, 6
+    kc2[5], kc2[6], vc2[5], vc2[6] = kc[0], kc[1], vc[0], vc[1]
     tables = np.array([[0, 1, 2], [0, 1, 2], [5, 6, 2]])
     qrow = rng.standard_normal((1, 4, d)).astype(np.float32)
     q = np.repeat(qrow, 3, axis=0)
@@ -330,15 +340,15 @@ def test_oracle_bf16_storage_matches_f32_values():
     to_bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)
     qb, kb, vb = to_bf(q), to_bf(kc), to_bf(vc)
     out_b = oracle.paged_decode(qb.view(torch.uint16).numpy(), kb.view(torch.uint16).numpy(),
-                                vb.view(torch.uint16).numpy(), tables, lens, 0.25, 8, BF16)
-    out_f = oracle.paged_decode(qb.float().numpy(), kb.float().numpy(), vb.float().numpy(),
+                                vstore(vb.view(torch.uint16).numpy()), tables, lens, 0.25, 8, BF16)
+    out_f = oracle.paged_decode(qb.float().numpy(), kb.float().numpy(), vstore(vb.float().numpy()),
                                 tables, lens, 0.25, 8, F32)
     assert np.array_equal(out_b, out_f)
-    out_h = oracle.paged_decode(q.astype(np.float16), kc.astype(np.float16), vc.astype(np.float16),
+    out_h = oracle.paged_decode(q.astype(np.float16), kc.astype(np.float16), vstore(vc.astype(np.float16)),
                                 tables, lens, 0.25, 8, F16)
     ref_h = oracle.paged_decode(q.astype(np.float16).astype(np.float32),
                                 kc.astype(np.float16).astype(np.float32),
-                                vc.astype(np.float16).astype(np.float32), tables, lens, 0.25, 8, F32)
+                                vstore(vc.astype(np.float16).astype(np.float32)), tables, lens, 0.25, 8, F32)
     assert np.array_equal(out_h, ref_h)
 
 
@@ -414,9 +424,9 @@ def test_unmutated_copy_passes_all_pins():
 def test_lse_merge_equals_unsplit_softmax():
     lens = [1, 16, 17, 100, 513, 1030, 0]
     q, kc, vc, tables, lens_a = _random_case(12, lens, 4, 2, 16, 16, 120)
-    ref = oracle.paged_decode(q, kc, vc, tables, lens_a, 0.3, 16, F32)
+    ref = oracle.paged_decode(q, kc, vstore(vc), tables, lens_a, 0.3, 16, F32)
     for part in (16, 48, 512, 4096):
-        got = oracle.paged_decode_partitioned(q, kc, vc, tables, lens_a, 0.3, 16, F32, part)
+        got = oracle.paged_decode_partitioned(q, kc, vstore(vc), tables, lens_a, 0.3, 16, F32, part)
         np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
 
 
@@ -454,46 +464,52 @@ def test_write_probe_worked_example():
     nb, hkv, bs, d = 8, 2, c["block_size"], 8
     rng = np.random.default_rng(14)
     kc = rng.integers(0, 2 ** 16, (nb, hkv, bs, d), dtype=np.uint16)
-    vc = rng.integers(0, 2 ** 16, (nb, hkv, bs, d), dtype=np.uint16)
+    vl = rng.integers(0, 2 ** 16, (nb, hkv, bs, d), dtype=np.uint16)
+    vc = vstore(vl)
     k = rng.integers(0, 2 ** 16, (1, hkv, d), dtype=np.uint16)
     v = rng.integers(0, 2 ** 16, (1, hkv, d), dtype=np.uint16)
     logical, off = divmod(c["position"], bs)
     slot = c["block_table"][logical] * bs + off
     assert slot == 29
     k2, v2 = oracle.write_cache(k, v, kc, vc, [slot], bs)
-    assert np.array_equal(k2[7, :, 1, :], k[0]) and np.array_equal(v2[7, :, 1, :], v[0])
+    want_v = vl.copy()
+    want_v[7, :, 1, :] = v[0]
+    assert np.array_equal(k2[7, :, 1, :], k[0]) and np.array_equal(v2, vstore(want_v))
     mask = np.ones(kc.shape, bool)
     mask[7, :, 1, :] = False
-    assert np.array_equal(k2[mask], kc[mask]) and np.array_equal(v2[mask], vc[mask])
+    assert np.array_equal(k2[mask], kc[mask])
 
 
 def test_write_skips_negative_slot_and_keeps_raw_bits():
     nb, hkv, bs, d = 4, 1, 4, 4
     kc = np.zeros((nb, hkv, bs, d), np.uint16)
-    vc = np.zeros((nb, hkv, bs, d), np.uint16)
+    vc = np.zeros(oracle.v_cache_shape(nb, hkv, bs, d), np.uint16)
     # NaN payloads, signed zero, infinity: moved as bits
     k = np.array([[[0x7FC1, 0xFFFF, 0x8000, 0x7F80]], [[1, 2, 3, 4]]], np.uint16)
     v = np.array([[[0x7F81, 0x0001, 0xFF80, 0x3F80]], [[5, 6, 7, 8]]], np.uint16)
     k2, v2 = oracle.write_cache(k, v, kc, vc, [13, -1], bs)
-    assert np.array_equal(k2[3, 0, 1], k[0, 0]) and np.array_equal(v2[3, 0, 1], v[0, 0])
+    assert np.array_equal(k2[3, 0, 1], k[0, 0]) and np.array_equal(v2[3, 0, 0, :, 1], v[0, 0])
     assert int(k2.astype(np.int64).sum()) == int(k[0].astype(np.int64).sum())
 
 
 def test_write_preconditions():
     kc = np.zeros((2, 1, 4, 2), np.float32)
+    vc = np.zeros(oracle.v_cache_shape(2, 1, 4, 2), np.float32)
     k = np.ones((2, 1, 2), np.float32)
     with pytest.raises(ValueError):
-        oracle.write_cache(k, k, kc, kc, [3, 3], 4)
+        oracle.write_cache(k, k, kc, vc, [3, 3], 4)
     with pytest.raises(IndexError):
-        oracle.write_cache(k, k, kc, kc, [8, 1], 4)
+        oracle.write_cache(k, k, kc, vc, [8, 1], 4)
     with pytest.raises(IndexError):
-        oracle.write_cache(k, k, kc, kc, [-2, 1], 4)
+        oracle.write_cache(k, k, kc, vc, [-2, 1], 4)
+    with pytest.raises(ValueError):
+        oracle.write_cache(k, k, kc, kc, [0, 1], 4)  # V in the untransposed shape
 
 
 def test_copy_blocks_whole_block_and_source_untouched():
     rng = np.random.default_rng(15)
     kc = rng.integers(0, 2 ** 16, (6, 2, 4, 3), dtype=np.uint16)
-    vc = rng.integers(0, 2 ** 16, (6, 2, 4, 3), dtype=np.uint16)
+    vc = rng.integers(0, 2 ** 16, oracle.v_cache_shape(6, 2, 4, 3), dtype=np.uint16)
     k2, v2 = oracle.copy_blocks(kc, vc, [[1, 4], [2, 5]])
     assert np.array_equal(k2[4], kc[1]) and np.array_equal(k2[5], kc[2])
     assert np.array_equal(v2[4], vc[1]) and np.array_equal(v2[5], vc[2])
@@ -507,6 +523,8 @@ def test_copy_blocks_preconditions():
     kc = np.zeros((4, 1, 2, 2), np.float32)
     with pytest.raises(ValueError):
         oracle.copy_blocks(kc, kc, [[0, 1], [2, 1]])
+    with pytest.raises(ValueError):
+        oracle.copy_blocks(kc, np.zeros((5, 1, 1, 2, 2), np.float32), [[0, 1]])
     with pytest.raises(ValueError):
         oracle.copy_blocks(kc, kc, [[0, 1], [1, 2]])
     with pytest.raises(IndexError):
@@ -522,6 +540,7 @@ def test_cow_isolates_writer_from_sharers():
     vc = rng.standard_normal((nb, hkv, bs, d)).astype(np.float32)
     q = rng.standard_normal((2, 2, d)).astype(np.float32)
     tables = np.array([[0, 1], [0, 1]])  # both share blocks 0 and 1 (block 1 half full)
+    vc = vstore(vc)
     before = oracle.paged_decode(q, kc, vc, tables, np.array([6, 6]), 0.3, bs, F32)
     k2, v2 = oracle.copy_blocks(kc, vc, [[1, 5]])
     new_k = rng.standard_normal((1, hkv, d)).astype(np.float32)
@@ -531,3 +550,33 @@ def test_cow_isolates_writer_from_sharers():
     assert np.array_equal(after[0], before[0])
     assert np.array_equal(k3[1], kc[1]) and np.array_equal(v3[1], vc[1])
     assert not np.array_equal(after[1], before[1])
+
+
+def test_v_layout_reading():
+    """The transposed tile layout: the V row of (pid, off) is
+    v_cache[pid, :, off // T, :, off % T] with T = min(B, 16). Writing every
+    slot through write_cache and reading every row back through gather_rows
+    are inverse maps of the test-side conversion, for block sizes below, at
+    and above the tile."""
+    rng = np.random.default_rng(17)
+    for bs in (4, 8, 16, 32, 64):
+        nb, hkv, d = 3, 2, 8
+        vl = rng.integers(0, 2 ** 16, (nb, hkv, bs, d), dtype=np.uint16)
+        store = vstore(vl)
+        assert store.shape == oracle.v_cache_shape(nb, hkv, bs, d)
+        # element (pid, kv, off, dd) sits at flat index
+        # (((pid * hkv + kv) * (B / T) + off // T) * D + dd) * T + off % T
+        t = min(bs, 16)
+        flat = store.reshape(-1)
+        for (pid, kv, off, dd) in [(0, 0, 0, 0), (2, 1, bs - 1, d - 1), (1, 0, bs // 2, 3)]:
+            idx = (((pid * hkv + kv) * (bs // t) + off // t) * d + dd) * t + off % t
+            assert flat[idx] == vl[pid, kv, off, dd]
+        slots = np.arange(nb * bs)
+        k = np.zeros((nb * bs, hkv, d), np.uint16)
+        v = vl.transpose(0, 2, 1, 3).reshape(nb * bs, hkv, d)
+        _, v_written = oracle.write_cache(k, v, np.zeros((nb, hkv, bs, d), np.uint16),
+                                          np.zeros_like(store), slots, bs)
+        assert np.array_equal(v_written, store)
+        rows = oracle.gather_rows(store, [2, 0, 1], 3 * bs, bs, BF16, "v")
+        want = oracle.to_float64(np.concatenate([vl[2], vl[0], vl[1]], axis=1).transpose(1, 0, 2), BF16)
+        assert np.array_equal(rows, want, equal_nan=True)

@@ -70,7 +70,7 @@ class Workload:
     prefill_slots: np.ndarray  # int64 [n] slots holding prefilled data
     cow_pairs: np.ndarray      # int32 [n, 2]
     writes: list = field(default_factory=list)
-    partition_size: int = 512
+    partition_size: int = 0          # 0 = the library's default
     ctx_recipe: str = ""
     refcount_max: int = 1
 
@@ -118,7 +118,7 @@ class Workload:
 # ---------------------------------------------------------------------------
 
 def _finish(name, pool: HostBlockPool, seqs, prefill_slots, cow_pairs, writes, *, num_heads,
-            num_kv_heads, head_dim, dtype, scale, seed, trap, partition_size=512, ctx_recipe=""):
+            num_kv_heads, head_dim, dtype, scale, seed, trap, partition_size=0, ctx_recipe=""):
     pool.check_consistency()
     lens = np.array([pool.used[s] for s in seqs], dtype=np.int32)
     bs = pool.block_size
@@ -300,13 +300,19 @@ def build(name: str) -> Workload:
 # Values
 # ---------------------------------------------------------------------------
 
+def v_tile(block_size: int) -> int:
+    """Tokens per transposed V tile of the cache layout: min(block_size, 16)."""
+    return min(block_size, 16)
+
+
 def make_values(w: Workload, device="cpu", poison=True):
     """Seeded N(0, 1) values as torch tensors on ``device``.
 
-    Returns a dict with q [S, Hq, D], k_cache / v_cache [NB, Hkv, B, D] and,
-    per write op, k / v rows [n, Hkv, D]. Values are drawn in float32 and
-    rounded to the storage type (round to nearest even for bfloat16). With
-    ``poison`` every slot that holds no prefilled token is NaN.
+    Returns a dict with q [S, Hq, D], k_cache [NB, Hkv, B, D], v_cache in the
+    transposed tile layout [NB, Hkv, B // T, D, T] (T = min(B, 16)) and, per
+    write op, k / v rows [n, Hkv, D]. Values are drawn in float32 and rounded
+    to the storage type (round to nearest even for bfloat16). With ``poison``
+    every slot that holds no prefilled token is NaN.
     """
     import torch
 
@@ -318,21 +324,19 @@ def make_values(w: Workload, device="cpu", poison=True):
     def randn(*shape):
         return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(tdt)
 
-    shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
-    q = randn(w.num_seqs, w.num_heads, w.head_dim)
-    caches = []
-    mask = None
+    nb, hkv, bs, d = w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
+    t = v_tile(bs)
+    q = randn(w.num_seqs, w.num_heads, d)
+    k_cache = randn(nb, hkv, bs, d)
+    v_cache = randn(nb, hkv, bs // t, d, t)
     if poison:
-        m = torch.zeros(w.num_blocks * w.block_size, dtype=torch.bool)
+        m = torch.zeros(nb * bs, dtype=torch.bool)
         m[torch.from_numpy(w.prefill_slots)] = True
-        mask = m.view(w.num_blocks, 1, w.block_size, 1).to(dev)
-    for _ in range(2):
-        c = randn(*shape)
-        if mask is not None:
-            c = torch.where(mask, c, torch.full((), float("nan"), dtype=tdt, device=dev))
-        caches.append(c)
+        nan = torch.full((), float("nan"), dtype=tdt, device=dev)
+        k_cache = torch.where(m.view(nb, 1, bs, 1).to(dev), k_cache, nan)
+        v_cache = torch.where(m.view(nb, 1, bs // t, 1, t).to(dev), v_cache, nan)
     writes = []
     for op in w.writes:
         n = len(op.slots)
-        writes.append((randn(n, w.num_kv_heads, w.head_dim), randn(n, w.num_kv_heads, w.head_dim)))
-    return {"q": q, "k_cache": caches[0], "v_cache": caches[1], "writes": writes}
+        writes.append((randn(n, hkv, d), randn(n, hkv, d)))
+    return {"q": q, "k_cache": k_cache, "v_cache": v_cache, "writes": writes}
