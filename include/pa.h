@@ -19,7 +19,10 @@
  *
  * Memory layout (all arrays dense, row-major, in device memory owned by the
  * caller; the library never allocates, frees or synchronizes):
- *   k_cache, v_cache  [num_blocks][num_kv_heads][block_size][head_dim]  elements of `dtype`
+ *   k_cache           [num_blocks][num_kv_heads][block_size][head_dim]    elements of `dtype`
+ *   v_cache           [num_blocks][num_kv_heads][block_size / T][head_dim][T], T = min(block_size, 16):
+ *                     each block's V rows stored as tiles of T tokens, head_dim-major, so
+ *                     the V row of (block pid, offset off) is v_cache[pid][kv][off / T][:][off % T]
  *   q, out            [num_seqs][num_heads][head_dim]                   elements of `dtype`
  *   k, v (new tokens) [num_tokens][num_kv_heads][head_dim]              elements of `dtype`
  *   block_tables      int32 [num_seqs][max_blocks_per_seq]
@@ -81,9 +84,12 @@ const char* pa_last_error(void);
 int pa_default_partition_size(void);
 
 /*
- * Bytes of device workspace pa_decode needs: per sequence, per query head and
- * per context partition one (max, sum, output row) record in float32. Returns
- * 0 for invalid arguments. partition_size = 0 selects the default.
+ * Bytes of device workspace pa_decode needs: one (max, sum, output row)
+ * record in float32 per sequence, query head and partition, or 0 when no
+ * sequence can span more than one partition (max_context_len <=
+ * partition_size). Returns 0 for invalid arguments too. partition_size = 0
+ * selects the default. The workspace is caller-owned device memory with no
+ * required contents; calls that share one must not overlap.
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
                                 int max_context_len, int partition_size);
@@ -108,8 +114,11 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
  * only. A sequence with a single partition is written directly.
  *
  * Arguments: num_heads must be a multiple of num_kv_heads; num_heads /
- * num_kv_heads must be 1, 2, 4 or 8; head_dim 64, 128 or 256; block_size a
- * power of two from 4 to 256 and at least 1024 / (head_dim * sizeof(dtype));
+ * num_kv_heads must be 1, 2, 4 or 8 (also 16 for bfloat16 / float16);
+ * head_dim 64, 128 or 256; block_size a power of two from 4 to 256; with one
+ * query head per KV head or float32 elements the block must also hold at
+ * least max(1024 / (head_dim * sizeof(dtype)), 4, 16 * head_dim * sizeof(dtype) / 1024)
+ * tokens (PA_ERR_UNSUPPORTED names the bound);
  * partition_size (0 = default) a multiple of 16 and of block_size with
  * partition_size / block_size <= 256; num_seqs <= 8192;
  * max_blocks_per_seq * block_size >= max_context_len. workspace must hold
@@ -117,6 +126,10 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
  * max_context_len must be >= every context_lens[s]; a longer sequence is
  * clamped to max_context_len tokens. Table entries outside [0, num_blocks)
  * are clamped into that range (wrong values, no fault). q/out must not alias.
+ *
+ * Work is split into items of (sequence, KV head, partition) that a
+ * persistent grid processes largest first; an item's result does not depend
+ * on which workgroup ran it.
  */
 pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens, float scale,
@@ -152,7 +165,7 @@ pa_status_t pa_decode_merge(void* out, const void* q, const void* k_cache, const
 /*
  * Cache write: for every token i with 0 <= slot_mapping[i] < num_blocks *
  * block_size, with pid = slot / block_size and off = slot % block_size,
- *     k_cache[pid][kv][off][:] = k[i][kv][:]  and  v_cache[pid][kv][off][:] = v[i][kv][:]
+ *     k_cache[pid][kv][off][:] = k[i][kv][:]  and  the V row of (pid, off) = v[i][kv][:]
  * for every KV head kv -- the "write the new token" step of [aiqz] 前缀共享机制,
  * addressed as in [aiqz] 块表映射机制. Elements are copied as raw bits (NaN
  * payloads included). A negative slot skips the token; a slot past the pool

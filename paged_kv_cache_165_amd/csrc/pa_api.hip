@@ -36,6 +36,11 @@ pa_status_t hip_fail(hipError_t e, const char* what) {
     return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+pa_status_t lds_fail(int num_seqs, int head_dim, int group) {
+    return fail(PA_ERR_UNSUPPORTED, "num_seqs %d with head_dim %d and group %d needs more LDS than one "
+                "workgroup can hold", num_seqs, head_dim, group);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int elem_bytes(pa_dtype_t dt) { return dt == PA_F32 ? 4 : 2; }
@@ -77,13 +82,15 @@ int resolve_partition(int partition_size) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Workspace: the per-partition records m, l and o, needed only when some
+// sequence can span several partitions.
 struct WsLayout {
     size_t m_off, l_off, o_off, total;
 };
 
 WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int pmax) {
     WsLayout w{};
-    if (pmax <= 1) return w;  // single-partition sequences never touch the workspace
+    if (pmax <= 1) return w;  // single-partition sequences never write records
     const size_t recs = static_cast<size_t>(num_seqs) * num_heads * pmax;
     w.m_off = 0;
     w.l_off = align256(recs * sizeof(float));
@@ -222,6 +229,7 @@ pa_status_t pa_decode_partitions(void* out, const void* q, const void* k_cache,
     st = num_cus(&cus);
     if (st != PA_OK) return st;
     hipError_t e = pa::launch_decode_partitions(p, dtype, head_dim, cus, static_cast<hipStream_t>(stream));
+    if (e == hipErrorInvalidConfiguration) return lds_fail(num_seqs, head_dim, num_heads / num_kv_heads);
     if (e != hipSuccess) return hip_fail(e, "decode partition kernel launch");
     return PA_OK;
 }
@@ -257,6 +265,7 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void*
     if (st != PA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = pa::launch_decode_partitions(p, dtype, head_dim, cus, s);
+    if (e == hipErrorInvalidConfiguration) return lds_fail(num_seqs, head_dim, num_heads / num_kv_heads);
     if (e != hipSuccess) return hip_fail(e, "decode partition kernel launch");
     e = pa::launch_decode_merge(p, dtype, head_dim, s);
     if (e != hipSuccess) return hip_fail(e, "decode merge kernel launch");

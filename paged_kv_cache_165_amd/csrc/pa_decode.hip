@@ -69,25 +69,78 @@ struct Item {
     int s, kv, pidx, nparts, t0, t1, b0, nblk;
 };
 
-// LDS: prefix[(S + 4) & ~3] | tbl[kMaxTableSlice] | red[kWaves * G * (D + 4)]
 __host__ __device__ constexpr size_t red_stride(int d) { return static_cast<size_t>(d) + 4; }
 
-// Prefix sum of partition counts over the batch; every thread takes part.
-// Returns the total number of partitions.
-__device__ int build_prefix(const DecodeParams& p, int* prefix) {
+// ---------------------------------------------------------------------------
+// Work order and assignment
+// ---------------------------------------------------------------------------
+//
+// Items are ordered largest first: every full partition of every sequence
+// (sequence-major), then the partial last partitions sorted by size from
+// largest to smallest (stable counting sort into kBuckets size classes), then
+// empty sequences; the KV heads of one (sequence, partition) are consecutive
+// items. Each workgroup builds this order in LDS (fullpre: prefix sum of full
+// partitions per sequence; plist: sequences with a partial partition, in
+// order) and takes items in a snake: round r gives item r * G + g to
+// workgroup g for even r and to workgroup G - 1 - g for odd r. Over a
+// largest-first order this balances about as well as a shared queue, without
+// the device-scope atomic per item that a queue costs.
+
+constexpr int kBuckets = 256;
+
+// LDS ints of the schedule: fullpre[S + 1] | plist[S] | bucket[kBuckets]
+__host__ __device__ constexpr size_t sched_ints(int num_seqs) {
+    return static_cast<size_t>((num_seqs + 4) & ~3) + static_cast<size_t>((num_seqs + 3) & ~3) + kBuckets;
+}
+
+struct Sched {
+    int* fullpre;
+    int* plist;
+    int* bucket;
+    int full;    // number of full partitions
+    int total;   // number of items
+};
+
+__device__ __forceinline__ Sched sched_lds(const DecodeParams& p, int* base) {
+    Sched sc;
+    sc.fullpre = base;
+    sc.plist = sc.fullpre + ((p.num_seqs + 4) & ~3);
+    sc.bucket = sc.plist + ((p.num_seqs + 3) & ~3);
+    sc.full = sc.total = 0;
+    return sc;
+}
+
+// Size class of a partial partition of r tokens (r = 0: empty sequence):
+// larger partials get smaller classes.
+__device__ __forceinline__ int size_class(int r, int part) {
+    if (r == 0) return kBuckets - 1;
+    return static_cast<int>((static_cast<long long>(part - 1 - r) * kBuckets) / part);
+}
+
+// Every thread of the workgroup takes part; fills sc.full and sc.total.
+// Every workgroup must derive the same order, so the partial list is a
+// stable counting sort: sequences of one size class keep their index order
+// (ranks inside a wave come from ballots, not from atomics).
+__device__ void build_schedule(const DecodeParams& p, Sched& sc) {
+    static_assert(kBuckets == kThreads, "one size class per thread");
     __shared__ int wave_tot[kWaves];
+    __shared__ int wave_cnt[kWaves][kBuckets];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int S = p.num_seqs;
-    if (tid == 0) prefix[0] = 0;
+    sc.bucket[tid] = 0;
+    if (tid == 0) sc.fullpre[0] = 0;
+    __syncthreads();
     int carry = 0;
     for (int base = 0; base < S; base += kThreads) {
         const int i = base + tid;
-        int n = 0;
+        int nf = 0;
         if (i < S) {
             const int L = clamp_ctx(p.context_lens[i], p);
-            n = L > 0 ? ceil_div(L, p.part) : 1;
+            nf = L / p.part;
+            const int r = L - nf * p.part;
+            if (r != 0 || L == 0) atomicAdd(&sc.bucket[size_class(r, p.part)], 1);
         }
-        int x = n;
+        int x = nf;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int y = __shfl_up(x, off);
@@ -97,31 +150,94 @@ __device__ int build_prefix(const DecodeParams& p, int* prefix) {
         __syncthreads();
         int add = carry;
         for (int w = 0; w < wave; ++w) add += wave_tot[w];
-        if (i < S) prefix[i + 1] = x + add;
+        if (i < S) sc.fullpre[i + 1] = x + add;
         carry += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
         __syncthreads();
     }
-    return prefix[S];
+    // exclusive scan of the class sizes: class c starts at bucket[c]
+    int x = sc.bucket[tid];
+    const int own = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    int add = 0;
+    for (int w = 0; w < wave; ++w) add += wave_tot[w];
+    const int partials = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+    sc.bucket[tid] = x + add - own;  // cursor of class tid
+    __syncthreads();
+    for (int base = 0; base < S; base += kThreads) {
+        const int i = base + tid;
+        int c = -1;
+        if (i < S) {
+            const int L = clamp_ctx(p.context_lens[i], p);
+            const int r = L - (L / p.part) * p.part;
+            if (r != 0 || L == 0) c = size_class(r, p.part);
+        }
+        // lanes of this wave in the same class, from one ballot per class bit
+        unsigned long long same = __ballot(c >= 0);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const unsigned long long m = __ballot((c >> b) & 1);
+            same &= ((c >> b) & 1) ? m : ~m;
+        }
+        const int rank = __popcll(same & ((1ull << lane) - 1ull));
+        for (int w = 0; w < kWaves; ++w) wave_cnt[w][tid] = 0;
+        __syncthreads();
+        if (c >= 0 && rank == 0) wave_cnt[wave][c] = __popcll(same);
+        __syncthreads();
+        if (c >= 0) {
+            int pos = sc.bucket[c] + rank;
+            for (int w = 0; w < wave; ++w) pos += wave_cnt[w][c];
+            sc.plist[pos] = i;
+        }
+        __syncthreads();
+        sc.bucket[tid] += wave_cnt[0][tid] + wave_cnt[1][tid] + wave_cnt[2][tid] + wave_cnt[3][tid];
+        __syncthreads();
+    }
+    sc.full = sc.fullpre[S];
+    sc.total = (sc.full + partials) * p.num_kv_heads;
 }
 
-__device__ __forceinline__ Item locate_item(const DecodeParams& p, const int* prefix, int item) {
+__device__ __forceinline__ Item item_at(const DecodeParams& p, const Sched& sc, int item) {
     Item it;
     const int j = item / p.num_kv_heads;
     it.kv = item - j * p.num_kv_heads;
-    int lo = 0, hi = p.num_seqs;  // prefix[lo] <= j < prefix[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (prefix[mid] <= j) lo = mid; else hi = mid;
+    int s, pidx;
+    if (j < sc.full) {
+        int lo = 0, hi = p.num_seqs;  // fullpre[lo] <= j < fullpre[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (sc.fullpre[mid] <= j) lo = mid; else hi = mid;
+        }
+        s = lo;
+        pidx = j - sc.fullpre[lo];
+    } else {
+        s = sc.plist[j - sc.full];
+        pidx = -1;
     }
-    it.s = lo;
-    it.pidx = j - prefix[lo];
-    it.nparts = prefix[lo + 1] - prefix[lo];
-    const int L = clamp_ctx(p.context_lens[lo], p);
-    it.t0 = it.pidx * p.part;
+    const int L = clamp_ctx(p.context_lens[s], p);
+    const int nf = L / p.part;
+    const bool partial = L - nf * p.part != 0 || L == 0;
+    if (pidx < 0) pidx = nf;
+    it.s = s;
+    it.pidx = pidx;
+    it.nparts = nf + (partial ? 1 : 0);
+    it.t0 = pidx * p.part;
     it.t1 = min(L, it.t0 + p.part);
     it.b0 = it.t0 >> p.log2_bs;
     it.nblk = (it.t1 - it.t0 + (1 << p.log2_bs) - 1) >> p.log2_bs;
     return it;
+}
+
+// Item of round r for this workgroup (snake order), or -1 past the end.
+__device__ __forceinline__ int snake_item(const Sched& sc, int r) {
+    const int g = blockIdx.x, G = gridDim.x;
+    const int item = r * G + ((r & 1) ? (G - 1 - g) : g);
+    return item < sc.total ? item : -1;
 }
 
 __device__ __forceinline__ void stage_table(const DecodeParams& p, const Item& it, int* tbl) {
@@ -240,10 +356,10 @@ __global__ __launch_bounds__(kThreads) void pa_decode_valu(DecodeParams p) {
     static_assert(VW == 2 || VW % 4 == 0, "V segment is 8 bytes or a multiple of 16");
     constexpr int NVL = VW == 2 ? 1 : VW / 4;  // loads per V^T segment
 
-    // LDS: prefix | tbl[kMaxTableSlice] | red[kWaves * G * RS] | ring[ring_slots]
+    // LDS: schedule | tbl[kMaxTableSlice] | red[kWaves * G * RS] | ring[ring_slots]
     extern __shared__ __align__(16) unsigned char smem[];
-    int* prefix = reinterpret_cast<int*>(smem);
-    int* tbl = prefix + ((p.num_seqs + 4) & ~3);
+    Sched sc = sched_lds(p, reinterpret_cast<int*>(smem));
+    int* tbl = reinterpret_cast<int*>(smem) + sched_ints(p.num_seqs);
     float* red = reinterpret_cast<float*>(tbl + kMaxTableSlice);
     float* ring = red + kWaves * G * RS;
     constexpr int SL = ring_slot_floats(G, D);
@@ -260,10 +376,10 @@ __global__ __launch_bounds__(kThreads) void pa_decode_valu(DecodeParams p) {
     const char* kbase = static_cast<const char*>(p.k_cache);
     const char* vbase = static_cast<const char*>(p.v_cache);
 
-    const int total_items = build_prefix(p, prefix) * hkv;
+    build_schedule(p, sc);
 
-    for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
-        const Item it = locate_item(p, prefix, item);
+    for (int r = 0, item = snake_item(sc, 0); item >= 0;) {
+        const Item it = item_at(p, sc, item);
         stage_table(p, it, tbl);
         __syncthreads();
 
@@ -440,8 +556,9 @@ __global__ __launch_bounds__(kThreads) void pa_decode_valu(DecodeParams p) {
         }
         __syncthreads();
         combine_to_ring<D, G>(it, red, ring + nring * SL);
+        item = snake_item(sc, ++r);
         ++nring;
-        if (nring == p.ring_slots || item + static_cast<int>(gridDim.x) >= total_items) {
+        if (nring == p.ring_slots || item < 0) {
             __syncthreads();
             flush_ring<DT, D, G>(p, ring, nring);
             nring = 0;
@@ -508,10 +625,10 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
     constexpr float kLazy = 8.f;  // rescale only when the max grows by more than 2^8
     constexpr bool kRed2 = mfma_red_double(G, D);
 
-    // LDS: prefix | tbl[2][kMaxTableSlice] | qs[2][QW] | red[1 or 2][kWaves * G * RS] | ring[ring_slots]
+    // LDS: schedule | tbl[2][kMaxTableSlice] | qs[2][QW] | red[1 or 2][kWaves * G * RS] | ring[ring_slots]
     extern __shared__ __align__(16) unsigned char smem[];
-    int* prefix = reinterpret_cast<int*>(smem);
-    int* tbl2 = prefix + ((p.num_seqs + 4) & ~3);
+    Sched sc = sched_lds(p, reinterpret_cast<int*>(smem));
+    int* tbl2 = reinterpret_cast<int*>(smem) + sched_ints(p.num_seqs);
     uint32_t* qs2 = reinterpret_cast<uint32_t*>(tbl2 + 2 * kMaxTableSlice);
     float* red2 = reinterpret_cast<float*>(qs2 + 2 * ((QW + 3) & ~3));
     float* ring = red2 + (kRed2 ? 2 : 1) * kWaves * G * RS;
@@ -529,9 +646,9 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
     const char* vbase = static_cast<const char*>(p.v_cache);
     const uint32_t* qwords = static_cast<const uint32_t*>(p.q);
 
-    const int total_items = build_prefix(p, prefix) * hkv;
-    int item = blockIdx.x;
-    if (item >= total_items) return;
+    build_schedule(p, sc);
+    const int item0 = snake_item(sc, 0);
+    if (item0 < 0) return;
 
     struct Buf {
         u32x4 k[NK];
@@ -592,7 +709,7 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
     };
 
     // ---- prologue: stage the first item's table slice and query block
-    Item cur = locate_item(p, prefix, item);
+    Item cur = item_at(p, sc, item0);
     stage_table(p, cur, tbl2);
     for (int w = tid; w < QW; w += kThreads) qs2[w] = qwords[q_word0(cur) + w];
     __syncthreads();
@@ -603,7 +720,8 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
     for (int k = 0;; ++k) {
         const int buf = k & 1;
         const int* tbl = tbl2 + buf * kMaxTableSlice;
-        const bool has_next = item + static_cast<int>(gridDim.x) < total_items;
+        const int next_item = snake_item(sc, k + 1);
+        const bool has_next = next_item >= 0;
         Item nxt = cur;
         int tbl_reg = 0, pk_n = 0, pv_n = 0;
         uint32_t q_reg[QPT];
@@ -612,7 +730,7 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
             // stage the next item while this one streams: its table slice and
             // query block into registers (written to LDS at the end of this
             // item), and this wave's blocks for its first tile of it
-            nxt = locate_item(p, prefix, item + gridDim.x);
+            nxt = item_at(p, sc, next_item);
             const int* trow = p.block_tables + static_cast<size_t>(nxt.s) * p.max_blocks + nxt.b0;
             if (tid < nxt.nblk) tbl_reg = clamp_pid(trow[tid]);
 #pragma unroll
@@ -746,7 +864,6 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
         }
         if (!has_next) break;
         cur = nxt;
-        item += gridDim.x;
     }
 }
 
@@ -792,47 +909,62 @@ __global__ __launch_bounds__(64) void pa_merge(DecodeParams p) {
 
 namespace {
 
-// LDS per compute unit; the result ring gets what the resident workgroups
-// (as many as the kernel's registers allow) leave over.
+// LDS per compute unit (also the most one workgroup may hold); the result
+// ring gets what the resident workgroups (as many as the kernel's registers
+// allow) leave over.
 constexpr size_t kLdsPerCu = 160 * 1024;
 constexpr int kMaxRingSlots = 32;
 
-// Ring slots that fit next to `fixed` bytes of LDS when `resident`
-// workgroups share a compute unit.
-int ring_slots_for(size_t fixed, int d, int g, int resident) {
-    const size_t budget = kLdsPerCu / static_cast<size_t>(resident < 1 ? 1 : resident) - 512;
+// Ring slots that fit next to `used` bytes of LDS (static + fixed dynamic)
+// when `resident` workgroups share a compute unit; 0 if not even one does.
+int ring_slots_for(size_t used, int d, int g, int resident) {
     const size_t slot = static_cast<size_t>(ring_slot_floats(g, d)) * sizeof(float);
-    long long n = fixed < budget ? static_cast<long long>((budget - fixed) / slot) : 0;
+    if (used + slot > kLdsPerCu) return 0;
+    const size_t share = kLdsPerCu / static_cast<size_t>(resident < 1 ? 1 : resident);
+    long long n = share > used + slot ? static_cast<long long>((share - used) / slot) : 1;
     if (n < 1) n = 1;
     if (n > kMaxRingSlots) n = kMaxRingSlots;
     return static_cast<int>(n);
 }
 
 size_t decode_smem_valu(int num_seqs, int d, int g) {
-    return (static_cast<size_t>((num_seqs + 4) & ~3) + kMaxTableSlice) * sizeof(int) +
+    return (sched_ints(num_seqs) + kMaxTableSlice) * sizeof(int) +
            static_cast<size_t>(kWaves) * g * red_stride(d) * sizeof(float);
 }
 
 size_t decode_smem_mfma(int num_seqs, int d, int g) {
     // prefix | two table slices | two query blocks | two sets of wave partials
     const size_t qw = ((static_cast<size_t>(g) * d / 2 + 3) & ~static_cast<size_t>(3));
-    return (static_cast<size_t>((num_seqs + 4) & ~3) + 2 * kMaxTableSlice) * sizeof(int) +
+    return (sched_ints(num_seqs) + 2 * kMaxTableSlice) * sizeof(int) +
            2 * qw * sizeof(uint32_t) +
            (mfma_red_double(g, d) ? 2 : 1) * static_cast<size_t>(kWaves) * g * red_stride(d) * sizeof(float);
 }
 
 // Launch a persistent kernel: as many workgroups as can be resident, with
-// the result ring sized to the LDS the resident workgroups leave free.
+// the result ring sized to the LDS the resident workgroups leave free. A
+// configuration whose LDS (static + dynamic) cannot fit one workgroup is
+// refused with hipErrorInvalidConfiguration before anything is launched.
 template <typename K>
 hipError_t launch_persistent(K kern, DecodeParams p, size_t fixed_smem, int d, int g, int num_cus,
                              hipStream_t stream) {
+    hipFuncAttributes attr{};
+    hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kern));
+    if (e != hipSuccess) return e;
+    const size_t static_lds = attr.sharedSizeBytes;
     int occ = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, fixed_smem);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, fixed_smem);
     if (e != hipSuccess) return e;
     if (occ < 1) occ = 1;
     if (PA_WG_PER_CU > 0 && occ > PA_WG_PER_CU) occ = PA_WG_PER_CU;
-    p.ring_slots = ring_slots_for(fixed_smem, d, g, occ);
+    p.ring_slots = ring_slots_for(static_lds + fixed_smem, d, g, occ);
+    if (p.ring_slots < 1) return hipErrorInvalidConfiguration;
     const size_t smem = fixed_smem + static_cast<size_t>(p.ring_slots) * ring_slot_floats(g, d) * sizeof(float);
+    if (static_lds + smem > kLdsPerCu) return hipErrorInvalidConfiguration;
+    int resident = 0;  // workgroups per compute unit with the final LDS request
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident, kern, kThreads, smem);
+    if (e != hipSuccess) return e;
+    if (resident < 1) return hipErrorInvalidConfiguration;
+    if (resident < occ) occ = resident;
     const long long upper = static_cast<long long>(p.num_seqs) * p.num_kv_heads * p.pmax;
     long long grid = static_cast<long long>(num_cus) * occ;
     if (grid > upper) grid = upper;
