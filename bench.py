@@ -23,6 +23,16 @@ import time
 
 METRIC = "paged decode attention: KV GB/s read (% of HBM peak), seqs/sec"
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_165_amd", "csrc", "pa_decode.hip")
+PARTITION_KERNELS = ("pa_decode_mfma", "pa_decode_valu")
+CALIBRATION_KERNEL = "neg_kernel"  # torch's elementwise negate: reads N bytes, writes N bytes
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def progress(msg: str) -> None:
@@ -40,10 +50,61 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
-    ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                                                           "profiles", "traffic.json"),
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="counter-derived HBM bytes per partition-kernel launch, if measured")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after timing, run a plain N-MB elementwise copy (torch negate) so that "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE can be scaled to bytes")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a run with "
+                         "--copy-calibration-mb into --traffic-json, then exit")
     return ap.parse_args()
+
+
+def _counter_rows(path, counter):
+    """(kernel name, value in KiB) per dispatch from a rocprofv3 counter CSV."""
+    import csv
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            name = r.get("Kernel_Name", "")
+            per.setdefault(key, [name, 0.0])[1] += float(r["Counter_Value"])
+    return list(per.values())
+
+
+def summarize_counters(fetch_csv, write_csv, out_json, workload, calib_mb):
+    """Scale per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the partition
+    kernel by what the same counters read for a copy of known size."""
+    calib_bytes = calib_mb * (1 << 20)
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, counter)
+        cal = [v for n, v in rows if CALIBRATION_KERNEL in n]
+        part = [v for n, v in rows if any(k in n for k in PARTITION_KERNELS)]
+        if not cal or not part:
+            raise SystemExit(f"{path}: no {counter} rows for the calibration copy or the partition kernel")
+        scale = calib_bytes / (sum(cal) / len(cal) * 1024.0)
+        res[counter] = {"calibration_kib": sum(cal) / len(cal), "scale": scale,
+                        "partition_kib_mean": sum(part) / len(part), "dispatches": len(part),
+                        "partition_bytes": sum(part) / len(part) * 1024.0 * scale}
+    data = {}
+    if os.path.exists(out_json):
+        with open(out_json) as f:
+            data = json.load(f)
+    data[workload] = {
+        "bytes_per_launch": round(res["FETCH_SIZE"]["partition_bytes"] + res["WRITE_SIZE"]["partition_bytes"]),
+        "read_bytes": round(res["FETCH_SIZE"]["partition_bytes"]),
+        "write_bytes": round(res["WRITE_SIZE"]["partition_bytes"]),
+        "fetch_scale": res["FETCH_SIZE"]["scale"], "write_scale": res["WRITE_SIZE"]["scale"],
+        "calibration_mb": calib_mb, "kernel_source_sha256_16": kernel_source_hash(),
+        "counters": res,
+    }
+    with open(out_json, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps(data[workload], indent=1))
 
 
 def cpu_baseline(w, q_h, kc_h, vc_h, seconds: float):
@@ -81,6 +142,10 @@ def cpu_baseline(w, q_h, kc_h, vc_h, seconds: float):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.traffic_json,
+                           args.workload, args.copy_calibration_mb)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -151,12 +216,21 @@ def main():
     achieved = kv / (part_us * 1e-6) / 1e9
     progress(f"step {ms_step * 1e3:.1f} us, partition kernel mean {part_us:.1f} us (median {part_us_med:.1f})")
 
-    traffic = None
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    traffic = None  # counter bytes, valid only for the kernel source they were taken on
     if os.path.exists(args.traffic_json):
         try:
             with open(args.traffic_json) as f:
                 tj = json.load(f).get(w.name)
-            if tj:
+            if tj and tj.get("kernel_source_sha256_16") == kernel_source_hash():
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None
@@ -191,7 +265,8 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "wall_ms_per_step": round(1e3 * t_wall / args.steps, 5),
-        "roofline": {"bound": "hbm", "kernel": "pa_partition_valu", "achieved": round(achieved, 2),
+        "roofline": {"bound": "hbm", "kernel": "pa_decode_partitions (pa_decode_mfma / pa_decode_valu)",
+                     "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_us_mean": round(part_us, 2),
                      "kernel_us_median": round(part_us_med, 2), "bytes_per_launch": kv},
