@@ -166,10 +166,10 @@ pa_status_t pa_decode_merge(void* out, const void* q, const void* k_cache, const
  * Cache write: for every token i with 0 <= slot_mapping[i] < num_blocks *
  * block_size, with pid = slot / block_size and off = slot % block_size,
  *     k_cache[pid][kv][off][:] = k[i][kv][:]  and  the V row of (pid, off) = v[i][kv][:]
- * for every KV head kv -- the "write the new token" step of [aiqz] 前缀共享机制,
- * addressed as in [aiqz] 块表映射机制. Elements are copied as raw bits (NaN
- * payloads included). A negative slot skips the token; a slot past the pool
- * is skipped too. Slots must be distinct (two tokens writing one slot leave
+ * for every KV head kv -- the step that stores a sequence's newest token after
+ * any copy ([aiqz] 前缀共享机制), addressed as in [aiqz] 块表映射机制.
+ * Elements are copied as raw bits (NaN payloads included). A negative slot
+ * skips the token; a slot past the pool is skipped too. Slots must be distinct (two tokens writing one slot leave
  * either value). num_tokens = 0 is a no-op.
  */
 pa_status_t pa_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,

@@ -332,7 +332,8 @@ def write_cache(k: np.ndarray, v: np.ndarray, k_cache: np.ndarray, v_cache: np.n
     (pid, off) becomes k[i] and the V row at (pid, off) becomes v[i] (in the
     transposed tile layout). A slot of -1 means the token is skipped.
     Elements are moved as stored (no conversion), so the result is defined bit
-    for bit. This is the "write the new token" step of [aiqz] "前缀共享机制";
+    for bit. This stores each sequence's newest token, after any copy of a
+    shared block ([aiqz] "前缀共享机制");
     the slot is the (pid, off) pair of [aiqz] "块表映射机制" flattened as
     pid * B + off.
     Preconditions (raise): equal storage dtypes, slots in {-1} U [0, NB * B),

@@ -1,10 +1,13 @@
 // Cache maintenance kernels for gfx950: the per-token write through a slot
 // mapping and the whole-block copy of copy-on-write.
 //
-// Both move raw 16-byte vectors, so the result is bit-exact whatever the
-// element type. The write is the "write the new token" step and the copy the
-// "allocate a new block and copy the old one into it" step of copy-on-write
-// (aiqz.cc tutorial, section 前缀共享机制; cf-1.com blog, 4.2). The slot of a
+// Both move raw bits and never convert, so the result is bit-exact whatever
+// the element type (NaN payloads included): K rows and whole blocks as 16-byte
+// vectors, V elements one by one into their transposed tile. The write
+// stores a sequence's newest token; the copy duplicates a shared block into a
+// freshly allocated one before a sharer writes into it, the copy half of
+// copy-on-write (aiqz.cc tutorial, section 前缀共享机制; cf-1.com blog, 4.2).
+// The slot of a
 // token is its (physical block, offset) pair of the block-table equation
 // (aiqz.cc, section 块表映射机制) flattened as pid * B + off.
 
