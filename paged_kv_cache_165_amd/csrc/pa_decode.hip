@@ -88,14 +88,15 @@ __host__ __device__ constexpr size_t red_stride(int d) { return static_cast<size
 
 constexpr int kBuckets = 256;
 
-// LDS ints of the schedule: fullpre[S + 1] | plist[S] | bucket[kBuckets]
+// LDS ints of the schedule: fullpre[S + 1] | plist[S] | lens[S] | bucket[kBuckets]
 __host__ __device__ constexpr size_t sched_ints(int num_seqs) {
-    return static_cast<size_t>((num_seqs + 4) & ~3) + static_cast<size_t>((num_seqs + 3) & ~3) + kBuckets;
+    return static_cast<size_t>((num_seqs + 4) & ~3) + 2 * static_cast<size_t>((num_seqs + 3) & ~3) + kBuckets;
 }
 
 struct Sched {
     int* fullpre;
     int* plist;
+    int* lens;   // context lengths, clamped to [0, max_ctx]
     int* bucket;
     int full;    // number of full partitions
     int total;   // number of items
@@ -105,7 +106,8 @@ __device__ __forceinline__ Sched sched_lds(const DecodeParams& p, int* base) {
     Sched sc;
     sc.fullpre = base;
     sc.plist = sc.fullpre + ((p.num_seqs + 4) & ~3);
-    sc.bucket = sc.plist + ((p.num_seqs + 3) & ~3);
+    sc.lens = sc.plist + ((p.num_seqs + 3) & ~3);
+    sc.bucket = sc.lens + ((p.num_seqs + 3) & ~3);
     sc.full = sc.total = 0;
     return sc;
 }
@@ -136,6 +138,7 @@ __device__ void build_schedule(const DecodeParams& p, Sched& sc) {
         int nf = 0;
         if (i < S) {
             const int L = clamp_ctx(p.context_lens[i], p);
+            sc.lens[i] = L;
             nf = L / p.part;
             const int r = L - nf * p.part;
             if (r != 0 || L == 0) atomicAdd(&sc.bucket[size_class(r, p.part)], 1);
@@ -173,7 +176,7 @@ __device__ void build_schedule(const DecodeParams& p, Sched& sc) {
         const int i = base + tid;
         int c = -1;
         if (i < S) {
-            const int L = clamp_ctx(p.context_lens[i], p);
+            const int L = sc.lens[i];
             const int r = L - (L / p.part) * p.part;
             if (r != 0 || L == 0) c = size_class(r, p.part);
         }
@@ -219,7 +222,7 @@ __device__ __forceinline__ Item item_at(const DecodeParams& p, const Sched& sc, 
         s = sc.plist[j - sc.full];
         pidx = -1;
     }
-    const int L = clamp_ctx(p.context_lens[s], p);
+    const int L = sc.lens[s];
     const int nf = L / p.part;
     const bool partial = L - nf * p.part != 0 || L == 0;
     if (pidx < 0) pidx = nf;
@@ -365,7 +368,8 @@ __global__ __launch_bounds__(kThreads) void pa_decode_valu(DecodeParams p) {
     constexpr int SL = ring_slot_floats(G, D);
     int nring = 0;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform: branches on it stay scalar
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rg = lane / LPR;           // row group: tokens U*rg .. U*rg+U-1 of a step
     const int li = lane % LPR;
     const int dsl = li * EPL;            // K side: first head-dim element of the lane
@@ -635,7 +639,8 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
     constexpr int SL = ring_slot_floats(G, D);
     int nring = 0;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform: branches on it stay scalar
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15;  // K row of the tile (A) / head column (B, C)
     const int j = lane >> 4;    // 8-element chunk of K / 4-token group of V and S
     const int bs = 1 << p.log2_bs;
@@ -695,56 +700,68 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
                 b.v[v] = nt_load<u32x2>(vbase, (vel + static_cast<size_t>(16 * v) * vt) * E);
         }
     };
-    // tile of the current item: physical blocks from the LDS table slice
-    auto load_tile = [&](const Item& x, const int* tbl, int tile, Buf& b) {
+    // this lane's physical blocks (K row, 4-token V group) of `tile` of `x`,
+    // from x's table slice in LDS
+    auto tile_blocks = [&](const Item& x, const int* tbl, int tile, int& pk, int& pv) {
         const int tt0 = x.t0 + 16 * tile;
-        int pk, pv;
         if constexpr (BIGB) {
             pk = pv = tbl[(min(tt0, x.t1 - 1) >> p.log2_bs) - x.b0];
         } else {
             pk = tbl[(min(tt0 + r16, x.t1 - 1) >> p.log2_bs) - x.b0];
             pv = tbl[(min(tt0 + 4 * j, last4_of(x)) >> p.log2_bs) - x.b0];
         }
-        load_with(x, tile, pk, pv, b);
     };
 
-    // ---- prologue: stage the first item's table slice and query block
+    // Load schedule. The compiler waits for a load by counting the memory
+    // operations issued after it, and where paths issue different numbers
+    // of loads it must assume the fewest -- a conditional prefetch would make
+    // the reduction of one tile wait for the next tile too. So every step of
+    // every wave issues the same loads: the next tile of the item, else the
+    // wave's first tile of the next item, else a dummy tile of block 0
+    // (in bounds, and cached after its first read). The next item's table
+    // slice, query block and first-tile block ids are likewise loaded raw on
+    // every item, from a harmless address when there is nothing to load, and
+    // are clamped only where they are used.
+
+    // ---- prologue: the first item's table slice and query block, the next
+    // item's descriptor, this wave's first tile
     Item cur = item_at(p, sc, item0);
+    int next_item = snake_item(sc, 1);
+    Item nxt = next_item >= 0 ? item_at(p, sc, next_item) : cur;
     stage_table(p, cur, tbl2);
     for (int w = tid; w < QW; w += kThreads) qs2[w] = qwords[q_word0(cur) + w];
     __syncthreads();
     Buf A, B;
-    bool start_b = false;
-    if (wave < ntiles_of(cur)) load_tile(cur, tbl2, wave, A);
+    {
+        int pk = 0, pv = 0;
+        const bool real = wave < ntiles_of(cur);
+        if (real) tile_blocks(cur, tbl2, wave, pk, pv);
+        load_with(cur, real ? wave : 0, pk, pv, A);
+    }
 
     for (int k = 0;; ++k) {
         const int buf = k & 1;
         const int* tbl = tbl2 + buf * kMaxTableSlice;
-        const int next_item = snake_item(sc, k + 1);
         const bool has_next = next_item >= 0;
-        Item nxt = cur;
-        int tbl_reg = 0, pk_n = 0, pv_n = 0;
-        uint32_t q_reg[QPT];
-        bool next_tile = false;
-        if (has_next) {
-            // stage the next item while this one streams: its table slice and
-            // query block into registers (written to LDS at the end of this
-            // item), and this wave's blocks for its first tile of it
-            nxt = item_at(p, sc, next_item);
-            const int* trow = p.block_tables + static_cast<size_t>(nxt.s) * p.max_blocks + nxt.b0;
-            if (tid < nxt.nblk) tbl_reg = clamp_pid(trow[tid]);
-#pragma unroll
-            for (int i = 0; i < QPT; ++i) {
-                const int w = tid + i * kThreads;
-                q_reg[i] = w < QW ? qwords[q_word0(nxt) + w] : 0u;
-            }
-            next_tile = wave < ntiles_of(nxt);
-            if (next_tile) {
-                const int tt0 = nxt.t0 + 16 * wave;
-                pk_n = clamp_pid(trow[(min(tt0 + r16, nxt.t1 - 1) >> p.log2_bs) - nxt.b0]);
-                pv_n = clamp_pid(trow[(min(tt0 + 4 * j, last4_of(nxt)) >> p.log2_bs) - nxt.b0]);
+        const bool next_tile = has_next && wave < ntiles_of(nxt);
+        // raw metadata of the next item (see the load schedule above)
+        const int* trow = p.block_tables + static_cast<size_t>(nxt.s) * p.max_blocks + nxt.b0;
+        const int* safe = p.context_lens;
+        int pk_raw, pv_raw;
+        {
+            const int tt0 = nxt.t0 + 16 * wave;
+            if constexpr (BIGB) {
+                pk_raw = *(next_tile ? trow + ((min(tt0, nxt.t1 - 1) >> p.log2_bs) - nxt.b0) : safe);
+                pv_raw = pk_raw;
+            } else {
+                pk_raw = *(next_tile ? trow + ((min(tt0 + r16, nxt.t1 - 1) >> p.log2_bs) - nxt.b0) : safe);
+                pv_raw = *(next_tile ? trow + ((min(tt0 + 4 * j, last4_of(nxt)) >> p.log2_bs) - nxt.b0) : safe);
             }
         }
+        const int tbl_raw = *(has_next && tid < nxt.nblk ? trow + tid : safe);
+        uint32_t q_raw[QPT];
+#pragma unroll
+        for (int i = 0; i < QPT; ++i) q_raw[i] = qwords[q_word0(nxt) + min(tid + i * kThreads, QW - 1)];
 
         // query fragments of this item from LDS: column r16 is head (r16 % G)
         u32x4 qf[NK];
@@ -802,33 +819,58 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
             }
         };
 
-        // this wave's tiles of the item; the buffer after the last one takes
-        // the wave's first tile of the next item. Returns true when that
-        // tile went to Y.
-        auto run = [&](Buf& X, Buf& Y) -> bool {
-            int tile = wave;
-            while (true) {
-                int tn = tile + kWaves;
-                if (tn < ntiles) load_tile(cur, tbl, tn, Y);
-                else if (next_tile) load_with(nxt, wave, pk_n, pv_n, Y);
-                compute_tile(tile, X);
-                tile = tn;
-                if (tile >= ntiles) return true;
-                tn = tile + kWaves;
-                if (tn < ntiles) load_tile(cur, tbl, tn, X);
-                else if (next_tile) load_with(nxt, wave, pk_n, pv_n, X);
-                compute_tile(tile, Y);
-                tile = tn;
-                if (tile >= ntiles) return false;
-            }
+        auto load_tile = [&](int tile, Buf& b) {
+            int pk, pv;
+            tile_blocks(cur, tbl, tile, pk, pv);
+            load_with(cur, tile, pk, pv, b);
         };
-        if (wave < ntiles) {
-            const bool r = start_b ? run(B, A) : run(A, B);
-            start_b = start_b ? !r : r;
-        } else {
-            if (next_tile) load_with(nxt, wave, pk_n, pv_n, A);
-            start_b = false;
+        // this wave's first tile of the next item, else a dummy. The empty
+        // asm keeps the use of the raw block ids here: hoisted to the top of
+        // the item, it would wait for loads issued just before.
+        auto load_next = [&](Buf& b) {
+            int pk = pk_raw, pv = pv_raw;
+            asm volatile("" : "+v"(pk), "+v"(pv));
+            if (next_tile) load_with(nxt, wave, clamp_pid(pk), clamp_pid(pv), b);
+            else load_with(cur, 0, 0, 0, b);
+        };
+
+        // This wave's tiles of the item, two deep. A holds the wave's first
+        // tile on entry and the next item's first tile on exit; B is loaded
+        // and reduced within one pass. Only A (and the accumulators) live
+        // across the loop, a plain counted loop over the pairs of tiles that
+        // another tile follows, and the next item's first tile is loaded at
+        // one point that every path reaches: the compiler then keeps A in
+        // place instead of copying a buffer whose loads are in flight, and
+        // each wait counts exactly the loads issued after what it waits for.
+        // The scheduling barriers keep each load group ahead of the reduction
+        // after it, and A's reads ahead of its refill.
+        const int mine = wave < ntiles ? (ntiles - 1 - wave) / kWaves + 1 : 0;  // this wave's tiles
+        int t = wave;
+        if (mine > 0) {
+            for (int i = 0; i < ((mine - 1) >> 1); ++i) {
+                load_tile(t + kWaves, B);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_tile(t, A);
+                __builtin_amdgcn_sched_barrier(0);
+                load_tile(t + 2 * kWaves, A);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_tile(t + kWaves, B);
+                t += 2 * kWaves;
+            }
+            if (mine & 1) {
+                compute_tile(t, A);
+            } else {
+                load_tile(t + kWaves, B);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_tile(t, A);
+                compute_tile(t + kWaves, B);
+            }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        load_next(A);  // (a wave without a tile here replaces a dummy)
+        // every path has used the raw block ids by now (the compiler cannot
+        // tell): say so, so that no later reuse of their registers waits
+        asm volatile("" ::"v"(pk_raw), "v"(pv_raw));
 
         // acc[v][r] = O^T[d = 16v + 4j + r][head column r16]; lsum covers this
         // lane's 4-token groups only: total it over the four lanes of the column
@@ -844,14 +886,17 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
                 r[D + 1] = lsum;
             }
         }
-        if (has_next) {
-            if (tid < nxt.nblk) tbl2[(buf ^ 1) * kMaxTableSlice + tid] = tbl_reg;
+        {
+            // The next item's table slice and query block go to the other
+            // buffers, which nobody reads during this item. The stores are
+            // unconditional (entries past the slice are never read; lanes past
+            // the query block repeat its last word) so that every path
+            // consumes the raw loads.
+            static_assert(kMaxTableSlice == kThreads, "one table entry per thread");
+            tbl2[(buf ^ 1) * kMaxTableSlice + tid] = clamp_pid(tbl_raw);
             uint32_t* qn = qs2 + (buf ^ 1) * ((QW + 3) & ~3);
 #pragma unroll
-            for (int i = 0; i < QPT; ++i) {
-                const int w = tid + i * kThreads;
-                if (w < QW) qn[w] = q_reg[i];
-            }
+            for (int i = 0; i < QPT; ++i) qn[min(tid + i * kThreads, QW - 1)] = q_raw[i];
         }
         __syncthreads();
         combine_to_ring<D, G>(cur, red, ring + nring * SL);
@@ -864,6 +909,8 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
         }
         if (!has_next) break;
         cur = nxt;
+        next_item = snake_item(sc, k + 2);
+        if (next_item >= 0) nxt = item_at(p, sc, next_item);
     }
 }
 
@@ -911,20 +958,25 @@ namespace {
 
 // LDS per compute unit (also the most one workgroup may hold); the result
 // ring gets what the resident workgroups (as many as the kernel's registers
-// allow) leave over.
+// allow) leave over. A workgroup's LDS (static + dynamic) is allocated in
+// whole granules, so every fit below is computed on rounded sizes: the
+// occupancy query counts exact bytes, and a grid sized from it can exceed
+// what fits, leaving workgroups to start only when others finish.
 constexpr size_t kLdsPerCu = 160 * 1024;
+constexpr size_t kLdsGranule = 1024;  // at least the hardware's allocation unit
 constexpr int kMaxRingSlots = 32;
+
+constexpr size_t lds_alloc(size_t bytes) { return (bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule; }
 
 // Ring slots that fit next to `used` bytes of LDS (static + fixed dynamic)
 // when `resident` workgroups share a compute unit; 0 if not even one does.
 int ring_slots_for(size_t used, int d, int g, int resident) {
     const size_t slot = static_cast<size_t>(ring_slot_floats(g, d)) * sizeof(float);
-    if (used + slot > kLdsPerCu) return 0;
+    if (lds_alloc(used + slot) > kLdsPerCu) return 0;
     const size_t share = kLdsPerCu / static_cast<size_t>(resident < 1 ? 1 : resident);
-    long long n = share > used + slot ? static_cast<long long>((share - used) / slot) : 1;
-    if (n < 1) n = 1;
-    if (n > kMaxRingSlots) n = kMaxRingSlots;
-    return static_cast<int>(n);
+    int n = 1;
+    while (n < kMaxRingSlots && lds_alloc(used + static_cast<size_t>(n + 1) * slot) <= share) ++n;
+    return n;
 }
 
 size_t decode_smem_valu(int num_seqs, int d, int g) {
@@ -959,10 +1011,13 @@ hipError_t launch_persistent(K kern, DecodeParams p, size_t fixed_smem, int d, i
     p.ring_slots = ring_slots_for(static_lds + fixed_smem, d, g, occ);
     if (p.ring_slots < 1) return hipErrorInvalidConfiguration;
     const size_t smem = fixed_smem + static_cast<size_t>(p.ring_slots) * ring_slot_floats(g, d) * sizeof(float);
-    if (static_lds + smem > kLdsPerCu) return hipErrorInvalidConfiguration;
+    const size_t alloc = lds_alloc(static_lds + smem);
+    if (alloc > kLdsPerCu) return hipErrorInvalidConfiguration;
     int resident = 0;  // workgroups per compute unit with the final LDS request
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident, kern, kThreads, smem);
     if (e != hipSuccess) return e;
+    const int lds_resident = static_cast<int>(kLdsPerCu / alloc);
+    if (lds_resident < resident) resident = lds_resident;
     if (resident < 1) return hipErrorInvalidConfiguration;
     if (resident < occ) occ = resident;
     const long long upper = static_cast<long long>(p.num_seqs) * p.num_kv_heads * p.pmax;
