@@ -966,6 +966,12 @@ constexpr size_t kLdsPerCu = 160 * 1024;
 constexpr size_t kLdsGranule = 1024;  // at least the hardware's allocation unit
 constexpr int kMaxRingSlots = 32;
 
+// Workgroups per compute unit of the MFMA kernel. Its scattered 4 KB tile
+// reads run faster from fewer, deeper streams: measured on MI355X, one
+// workgroup per CU is as fast as two or three on the batch-256 grouped-query
+// decode and 10 % faster on the long-context one.
+constexpr int kMfmaWgPerCu = 1;
+
 constexpr size_t lds_alloc(size_t bytes) { return (bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule; }
 
 // Ring slots that fit next to `used` bytes of LDS (static + fixed dynamic)
@@ -998,7 +1004,7 @@ size_t decode_smem_mfma(int num_seqs, int d, int g) {
 // refused with hipErrorInvalidConfiguration before anything is launched.
 template <typename K>
 hipError_t launch_persistent(K kern, DecodeParams p, size_t fixed_smem, int d, int g, int num_cus,
-                             hipStream_t stream) {
+                             int max_per_cu, hipStream_t stream) {
     hipFuncAttributes attr{};
     hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kern));
     if (e != hipSuccess) return e;
@@ -1007,6 +1013,7 @@ hipError_t launch_persistent(K kern, DecodeParams p, size_t fixed_smem, int d, i
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, fixed_smem);
     if (e != hipSuccess) return e;
     if (occ < 1) occ = 1;
+    if (max_per_cu > 0 && occ > max_per_cu) occ = max_per_cu;
     if (PA_WG_PER_CU > 0 && occ > PA_WG_PER_CU) occ = PA_WG_PER_CU;
     p.ring_slots = ring_slots_for(static_lds + fixed_smem, d, g, occ);
     if (p.ring_slots < 1) return hipErrorInvalidConfiguration;
@@ -1033,16 +1040,16 @@ hipError_t launch_valu(const DecodeParams& p, int num_cus, hipStream_t stream) {
     constexpr int step = ValuGeom<Elem<DT>::E, D>::STEP;
     const size_t fixed = decode_smem_valu(p.num_seqs, D, G);
     if ((1 << p.log2_bs) >= step)
-        return launch_persistent(pa_decode_valu<DT, D, G, true>, p, fixed, D, G, num_cus, stream);
-    return launch_persistent(pa_decode_valu<DT, D, G, false>, p, fixed, D, G, num_cus, stream);
+        return launch_persistent(pa_decode_valu<DT, D, G, true>, p, fixed, D, G, num_cus, 0, stream);
+    return launch_persistent(pa_decode_valu<DT, D, G, false>, p, fixed, D, G, num_cus, 0, stream);
 }
 
 template <int DT, int D, int G>
 hipError_t launch_mfma(const DecodeParams& p, int num_cus, hipStream_t stream) {
     const size_t fixed = decode_smem_mfma(p.num_seqs, D, G);
     if ((1 << p.log2_bs) >= 16)
-        return launch_persistent(pa_decode_mfma<DT, D, G, true>, p, fixed, D, G, num_cus, stream);
-    return launch_persistent(pa_decode_mfma<DT, D, G, false>, p, fixed, D, G, num_cus, stream);
+        return launch_persistent(pa_decode_mfma<DT, D, G, true>, p, fixed, D, G, num_cus, kMfmaWgPerCu, stream);
+    return launch_persistent(pa_decode_mfma<DT, D, G, false>, p, fixed, D, G, num_cus, kMfmaWgPerCu, stream);
 }
 
 template <int DT, int D>
