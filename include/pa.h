@@ -169,8 +169,12 @@ pa_status_t pa_decode_merge(void* out, const void* q, const void* k_cache, const
  * for every KV head kv -- the step that stores a sequence's newest token after
  * any copy ([aiqz] 前缀共享机制), addressed as in [aiqz] 块表映射机制.
  * Elements are copied as raw bits (NaN payloads included). A negative slot
- * skips the token; a slot past the pool is skipped too. Slots must be distinct (two tokens writing one slot leave
- * either value). num_tokens = 0 is a no-op.
+ * skips the token; a slot past the pool is skipped too. Slots must be
+ * distinct (two tokens writing one slot leave either value). A K/V row
+ * (head_dim * element size) must be a multiple of 16 bytes and at most
+ * 32768 bytes (PA_ERR_UNSUPPORTED otherwise). num_tokens = 0 is a no-op.
+ * Tokens at consecutive offsets of a block are written fastest. The stores
+ * bypass the cache, so a decode launched right after reads them from memory.
  */
 pa_status_t pa_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                            const int32_t* slot_mapping, int num_tokens, int num_kv_heads,

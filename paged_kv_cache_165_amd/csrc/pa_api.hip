@@ -283,6 +283,8 @@ pa_status_t pa_write_cache(const void* k, const void* v, void* k_cache, void* v_
     const int row_bytes = head_dim * elem_bytes(dtype);
     if (row_bytes % 16 != 0)
         return fail(PA_ERR_UNSUPPORTED, "head_dim * element size = %d bytes is not a multiple of 16", row_bytes);
+    if (row_bytes > 32 * 1024)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim * element size = %d bytes is more than 32768", row_bytes);
     if (!is_pow2(block_size) || block_size < 4)
         return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two >= 4", block_size);
     if (num_tokens == 0) return PA_OK;

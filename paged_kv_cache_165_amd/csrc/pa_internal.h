@@ -40,6 +40,13 @@ struct DecodeParams {
 // this many tokens, head_dim-major.
 inline int v_tile_tokens(int block_size) { return block_size < 16 ? block_size : 16; }
 
+// log2 of a power of two
+inline int ilog2(int x) {
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
+}
+
 // Return hipSuccess or the launch error.
 hipError_t launch_decode_partitions(const DecodeParams& p, pa_dtype_t dt, int head_dim,
                                     int num_cus, hipStream_t stream);

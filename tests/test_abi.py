@@ -98,6 +98,8 @@ def test_write_and_copy_reject_before_launch():
     assert lib.pa_write_cache(16, 16, 16, 16, 0, 3, 2, 128, 16, 10, 1, None) == 1
     assert lib.pa_write_cache(16, 16, 16, 16, 16, 3, 2, 4, 16, 10, 1, None) == 2  # 8-byte rows
     assert lib.pa_write_cache(0, 0, 0, 0, 0, 0, 2, 128, 16, 10, 1, None) == 0     # no tokens
+    assert lib.pa_write_cache(16, 16, 16, 16, 16, 3, 2, 8200, 16, 10, 0, None) == 2  # 32800-byte rows
+    assert b"32768" in lib.pa_last_error()
     assert lib.pa_copy_blocks(16, 16, 16, -2, 2, 16, 128, 10, 1, None) == 1
     assert lib.pa_copy_blocks(16, 16, 0, 2, 2, 16, 128, 10, 1, None) == 1
     assert lib.pa_copy_blocks(0, 0, 0, 0, 2, 16, 128, 10, 1, None) == 0
