@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--workload", default="gqa8b",
                     choices=["tiny", "layout", "mha7b", "gqa8b", "prefix", "long"])
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="page the gqa8b sequences with this block size instead of 16 (block-size sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
@@ -165,7 +167,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     progress(f"device {torch.cuda.get_device_name(dev)}; building workload {args.workload}")
-    w = W.build(args.workload)
+    if args.block_size and args.workload != "gqa8b":
+        print("--block-size applies to the gqa8b workload only", file=sys.stderr)
+        sys.exit(2)
+    w = W.build(args.workload, **({"block_size": args.block_size} if args.block_size else {}))
     if args.partition_size:
         w.partition_size = args.partition_size
     vals = W.make_values(w, device=dev, poison=True)
@@ -261,7 +266,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
-                   "partition_size": w.partition_size or pa.default_partition_size(), "ctx": w.ctx_recipe, "tokens": int(w.context_lens.sum()),
+                   "partition_size": w.partition_size or pa.default_partition_size(), "ctx": w.ctx_recipe, "tokens": int(w.context_lens.sum()), "tail_waste": round(W.tail_waste(w), 5),
                    "kv_bytes": kv, "seed": w.seed, "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),

@@ -204,11 +204,13 @@ def gqa8b_lengths(rng, n=256, median=1024, sigma=1.0, cap=8192):
     return np.clip(np.rint(x), 1, cap).astype(np.int64)
 
 
-def gqa8b() -> Workload:
+def gqa8b(block_size: int = 16) -> Workload:
+    """The batch-256 GQA workload; ``block_size`` other than 16 gives the
+    same sequences paged with another block size (block-size sweep)."""
     seed = 1653
     rng = np.random.default_rng(seed)
     lens = gqa8b_lengths(rng)
-    return _prefill_then_append("gqa8b", lens, block_size=16, num_blocks=None, seed=seed, rng=rng,
+    return _prefill_then_append("gqa8b", lens, block_size=block_size, num_blocks=None, seed=seed, rng=rng,
                                 num_heads=32, num_kv_heads=8, head_dim=128, dtype=BF16,
                                 scale=1.0 / math.sqrt(128),
                                 ctx_recipe="lognormal median 1024 sigma 1, clipped to [1, 8192]")
@@ -292,8 +294,16 @@ BUILDERS = {
 }
 
 
-def build(name: str) -> Workload:
-    return BUILDERS[name]()
+def build(name: str, **kw) -> Workload:
+    return BUILDERS[name](**kw)
+
+
+def tail_waste(w: Workload) -> float:
+    """Fraction of allocated slots past the context ends: the empty tail of
+    each sequence's last block, over all allocated slots."""
+    b = w.block_size
+    alloc = (-(-w.context_lens.astype(np.int64) // b)) * b
+    return float((alloc - w.context_lens).sum() / alloc.sum()) if alloc.sum() else 0.0
 
 
 # ---------------------------------------------------------------------------
