@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum pa_dtype {
     PA_F32 = 0,  /* IEEE binary32 */
@@ -66,7 +66,8 @@ typedef enum pa_status {
     PA_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size, misalignment */
     PA_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for */
     PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than pa_decode_workspace_size */
-    PA_ERR_HIP = 4          /* the HIP runtime reported an error */
+    PA_ERR_HIP = 4,         /* the HIP runtime reported an error */
+    PA_ERR_NO_BLOCKS = 5    /* block manager (pa_blocks.h): not enough free blocks */
 } pa_status_t;
 
 /* ABI version of the loaded library (PA_ABI_VERSION it was built with). */

@@ -1,4 +1,5 @@
-"""ctypes loader for libpa.so, the C-ABI library declared in include/pa.h.
+"""ctypes loader for libpa.so, the C-ABI library declared in include/pa.h and
+include/pa_blocks.h.
 
 No compute happens here: this module only loads the shared library and
 declares the argument types of its exported functions. There is no fallback:
@@ -16,11 +17,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 PA_OK = 0
 
-# every symbol include/pa.h declares
+# every symbol include/pa.h and include/pa_blocks.h declare
 EXPORTED = (
     "pa_abi_version", "pa_status_string", "pa_last_error", "pa_default_partition_size",
     "pa_decode_workspace_size", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
     "pa_write_cache", "pa_copy_blocks",
+    "pa_bm_create", "pa_bm_destroy", "pa_bm_prefill", "pa_bm_share", "pa_bm_append", "pa_bm_free",
+    "pa_bm_block_tables", "pa_bm_num_free", "pa_bm_blocks_in_use", "pa_bm_refcount", "pa_bm_seq_tokens",
+    "pa_bm_blocks_without_sharing", "pa_bm_check",
 )
 
 _lock = threading.Lock()
@@ -64,5 +68,31 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.pa_write_cache.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
         lib.pa_copy_blocks.restype = _i
         lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
+        _i64 = ctypes.c_int64
+        lib.pa_bm_create.restype = _i
+        lib.pa_bm_create.argtypes = [_i, _i, _vp, ctypes.POINTER(_vp)]
+        lib.pa_bm_destroy.restype = None
+        lib.pa_bm_destroy.argtypes = [_vp]
+        lib.pa_bm_prefill.restype = _i
+        lib.pa_bm_prefill.argtypes = [_vp, _i64, _i]
+        lib.pa_bm_share.restype = _i
+        lib.pa_bm_share.argtypes = [_vp, _i64, _i64, _i]
+        lib.pa_bm_append.restype = _i
+        lib.pa_bm_append.argtypes = [_vp, _vp, _i, _vp, _vp, ctypes.POINTER(_i)]
+        lib.pa_bm_free.restype = _i
+        lib.pa_bm_free.argtypes = [_vp, _i64]
+        lib.pa_bm_block_tables.restype = _i
+        lib.pa_bm_block_tables.argtypes = [_vp, _vp, _i, _vp, _i, ctypes.c_int32, _vp]
+        for name in ("pa_bm_num_free", "pa_bm_blocks_in_use"):
+            getattr(lib, name).restype = _i
+            getattr(lib, name).argtypes = [_vp]
+        lib.pa_bm_refcount.restype = _i
+        lib.pa_bm_refcount.argtypes = [_vp, _i]
+        lib.pa_bm_seq_tokens.restype = _i64
+        lib.pa_bm_seq_tokens.argtypes = [_vp, _i64]
+        lib.pa_bm_blocks_without_sharing.restype = _i64
+        lib.pa_bm_blocks_without_sharing.argtypes = [_vp]
+        lib.pa_bm_check.restype = _i
+        lib.pa_bm_check.argtypes = [_vp]
         _lib = lib
         return lib

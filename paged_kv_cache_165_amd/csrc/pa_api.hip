@@ -21,7 +21,10 @@ constexpr int kMaxTableSlice = 256;
 
 thread_local std::string g_last_error;
 
-pa_status_t fail(pa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+}  // namespace
+
+namespace pa {
+
 pa_status_t fail(pa_status_t st, const char* fmt, ...) {
     char buf[512];
     va_list ap;
@@ -31,6 +34,12 @@ pa_status_t fail(pa_status_t st, const char* fmt, ...) {
     g_last_error = buf;
     return st;
 }
+
+}  // namespace pa
+
+namespace {
+
+using pa::fail;
 
 pa_status_t hip_fail(hipError_t e, const char* what) {
     return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -193,6 +202,7 @@ const char* pa_status_string(pa_status_t status) {
         case PA_ERR_UNSUPPORTED: return "unsupported configuration";
         case PA_ERR_WORKSPACE: return "workspace missing or too small";
         case PA_ERR_HIP: return "HIP runtime error";
+        case PA_ERR_NO_BLOCKS: return "not enough free blocks";
     }
     return "unknown status";
 }

@@ -10,6 +10,9 @@
 
 namespace pa {
 
+// Set the calling thread's pa_last_error() message and return `st`.
+pa_status_t fail(pa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 // Everything one decode launch needs. Pointers are device pointers.
 struct DecodeParams {
     void* out;
