@@ -19,6 +19,7 @@ from .paged_attention import (  # noqa: F401
     gather_rows,
     attend_contiguous,
     paged_decode,
+    paged_prefill,
     partition_stats,
     lse_merge,
     paged_decode_partitioned,

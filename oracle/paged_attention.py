@@ -41,6 +41,11 @@ Pins (all in ``tests/test_oracle.py``, run with ``-m "not gpu"``):
                           permutation invariance, shared-vs-copied blocks, NaN poison
   partition_stats/lse_merge equality with the unsplit softmax, single partition,
                           empty partition
+  paged_prefill           one new token per sequence equals paged_decode; a whole
+                          prompt equals float64 causal scaled_dot_product_attention;
+                          pure-Python brute force; the last new token equals the
+                          decode of the full context; a planted off-by-one in the
+                          causal bound is caught
   write_cache             write probe (position 9 -> slot 29 -> block 7 offset 1),
                           skip slot -1, raw-bit copies of NaN payloads
   copy_blocks             whole-block copy, source untouched, precondition errors
@@ -205,17 +210,18 @@ def attend_contiguous(q_seq: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray,
     return out
 
 
-def _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, block_size, dtype):
+def _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, block_size, dtype,
+                       one_row_per_seq=True):
     _check_storage(q, dtype, "q")
     _check_storage(k_cache, dtype, "k_cache")
     _check_storage(v_cache, dtype, "v_cache")
-    s, hq, d = q.shape
+    rows, hq, d = q.shape
     nb, hkv, bs, d2 = k_cache.shape
     if d2 != d or bs != block_size:
         raise ValueError("cache shape does not match q / block_size")
     if v_cache.shape != v_cache_shape(nb, hkv, block_size, d):
         raise ValueError("v_cache shape does not match the transposed tile layout")
-    if len(context_lens) != s or len(block_tables) != s:
+    if len(context_lens) != len(block_tables) or (one_row_per_seq and len(context_lens) != rows):
         raise ValueError("one block table and one context length per sequence")
     for L in context_lens:
         if L < 0:
@@ -243,6 +249,46 @@ def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         k_rows = gather_rows(k_cache, block_tables[i], L, block_size, dtype, "k")
         v_rows = gather_rows(v_cache, block_tables[i], L, block_size, dtype, "v")
         out[i] = attend_contiguous(to_float64(q[i], dtype), k_rows, v_rows, scale)
+    return out
+
+
+def paged_prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                  block_tables: np.ndarray, context_lens, query_start, scale: float,
+                  block_size: int, dtype: str) -> np.ndarray:
+    """Paged prefill (multi-token query) attention, float64 [total_q, num_heads, D].
+
+    Sequence s holds L_s = context_lens[s] tokens in its blocks, the last
+    M_s = query_start[s + 1] - query_start[s] of them new (their K and V
+    already written to the cache). Its i-th new token, at position
+    p = L_s - M_s + i, attends to tokens 0..p: the visible history up to and
+    including itself ([lihaoran] "块表把逻辑顺序映射到物理位置": attention
+    covers the whole visible history; for a token of the prompt, what it can
+    see is what precedes it). Each query row is ``attend_contiguous`` over the
+    first p + 1 gathered rows; q rows of sequence s are
+    q[query_start[s]:query_start[s + 1]].
+    """
+    starts = [int(x) for x in query_start]
+    s = len(starts) - 1
+    if s < 0 or q.shape[0] != starts[-1] or any(b < a for a, b in zip(starts, starts[1:])):
+        raise ValueError("query_start must be non-decreasing, from 0 to the number of query rows")
+    if starts[0] != 0:
+        raise ValueError("query_start[0] must be 0")
+    _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, block_size, dtype,
+                       one_row_per_seq=False)
+    if len(context_lens) != s:
+        raise ValueError("one context length per sequence")
+    out = np.zeros(q.shape, dtype=np.float64)
+    for i in range(s):
+        L = int(context_lens[i])
+        m = starts[i + 1] - starts[i]
+        if m > L:
+            raise ValueError("more new tokens than the sequence holds")
+        k_rows = gather_rows(k_cache, block_tables[i], L, block_size, dtype, "k")
+        v_rows = gather_rows(v_cache, block_tables[i], L, block_size, dtype, "v")
+        for j in range(m):
+            p = L - m + j
+            out[starts[i] + j] = attend_contiguous(to_float64(q[starts[i] + j], dtype), k_rows[:p + 1],
+                                                   v_rows[:p + 1], scale)
     return out
 
 
