@@ -1,9 +1,11 @@
 /*
  * pa.h -- C ABI of the MI355X (gfx950) paged KV-cache decode library.
  *
- * Three device operations, each enqueued on the caller's HIP stream:
+ * Device operations, each enqueued on the caller's HIP stream:
  *   pa_decode       single-query attention of every sequence over its KV
  *                   cache, read through its block table;
+ *   pa_prefill      attention of several new tokens per sequence, each over
+ *                   the cached tokens up to its own position;
  *   pa_write_cache  write each new token's K and V rows into the slot given by
  *                   a slot mapping;
  *   pa_copy_blocks  whole-block copies, the copy half of copy-on-write.
@@ -24,6 +26,9 @@
  *                     each block's V rows stored as tiles of T tokens, head_dim-major, so
  *                     the V row of (block pid, offset off) is v_cache[pid][kv][off / T][:][off % T]
  *   q, out            [num_seqs][num_heads][head_dim]                   elements of `dtype`
+ *                     (pa_prefill: [num_tokens][num_heads][head_dim], the new tokens of
+ *                     every sequence in order, delimited by query_start)
+ *   query_start       int32 [num_seqs + 1] (pa_prefill only)
  *   k, v (new tokens) [num_tokens][num_kv_heads][head_dim]              elements of `dtype`
  *   block_tables      int32 [num_seqs][max_blocks_per_seq]
  *   context_lens      int32 [num_seqs]
@@ -53,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum pa_dtype {
     PA_F32 = 0,  /* IEEE binary32 */
@@ -162,6 +167,46 @@ pa_status_t pa_decode_merge(void* out, const void* q, const void* k_cache, const
                             int max_blocks_per_seq, int max_context_len, int partition_size,
                             pa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * Paged prefill attention (several new tokens per sequence).
+ *
+ * Sequence s holds L = context_lens[s] tokens in its blocks; the last
+ * M = query_start[s + 1] - query_start[s] of them are new, their K and V
+ * already written (pa_write_cache), and their query rows are
+ * q[query_start[s] + i], i in [0, M). New token i sits at position
+ * p = L - M + i and attends to the tokens at positions 0..p -- everything
+ * before it and itself ([lihaoran] section 块表把逻辑顺序映射到物理位置: causal
+ * attention covers the visible history, whatever the blocks). With token t
+ * read at block_tables[s][t / block_size], offset t % block_size ([aiqz]
+ * 块表映射机制) and x_t = scale * <q_row[h], k_t[kv]>,
+ *     out[query_start[s] + i][h] = sum_{t <= p} exp(x_t - max x) v_t[kv] / sum_{t <= p} exp(x_t - max x),
+ * kv = h / (num_heads / num_kv_heads). M = 1 is the decode of the same
+ * sequence. A row whose position would be negative (M > L, an invalid input)
+ * is written as zeros. Arithmetic is float32 on MFMA; the probabilities are
+ * rounded to `dtype` before they weight V (the softmax denominator sums the
+ * rounded values), and out is rounded to `dtype`.
+ *
+ * Arguments: q and out hold num_tokens rows; query_start must be
+ * non-decreasing from 0 to at most num_tokens (entries are clamped into
+ * [0, num_tokens]). dtype bfloat16 or float16; head_dim 64, 128 or 256;
+ * num_heads / num_kv_heads 1, 2, 4, 8 or 16; block_size a power of two from
+ * 4 to 256; max_blocks_per_seq * block_size >= max_context_len.
+ * max_query_len must be >= every M and max_context_len >= every L: a longer
+ * sequence has only its last max_query_len rows computed, over at most
+ * max_context_len tokens. Table entries past ceil(L / block_size) are never
+ * read; entries outside [0, num_blocks) are clamped. q/out must not alias.
+ * No workspace is needed. num_seqs = 0 or max_query_len = 0 is a no-op.
+ *
+ * Work is split into (query tile, sequence, KV head) workgroups; a tile's
+ * result does not depend on the others.
+ */
+pa_status_t pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* query_start, float scale, int block_size, int num_seqs,
+                       int num_tokens, int num_heads, int num_kv_heads, int head_dim,
+                       int num_blocks, int max_blocks_per_seq, int max_query_len,
+                       int max_context_len, pa_dtype_t dtype, void* stream);
 
 /*
  * Cache write: for every token i with 0 <= slot_mapping[i] < num_blocks *

@@ -11,6 +11,8 @@ Layouts (see include/pa.h):
   v_cache           [num_blocks, num_kv_heads, block_size // T, head_dim, T],
                     T = min(block_size, 16) (``v_cache_shape``)
   q, out            [num_seqs, num_heads, head_dim]
+                    (prefill: [num_tokens, num_heads, head_dim], split by query_start)
+  query_start       int32 [num_seqs + 1] (prefill)
   k, v              [num_tokens, num_kv_heads, head_dim]
   block_tables      int32 [num_seqs, max_blocks_per_seq]
   context_lens      int32 [num_seqs]
@@ -29,7 +31,7 @@ from . import _lib
 __all__ = [
     "PaError", "library", "default_partition_size", "workspace_size", "alloc_workspace",
     "v_tile", "v_cache_shape", "alloc_cache",
-    "decode", "decode_partitions", "decode_merge", "write_cache", "copy_blocks",
+    "decode", "decode_partitions", "decode_merge", "prefill", "write_cache", "copy_blocks",
 ]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16, torch.float16: _lib.PA_F16}
@@ -174,6 +176,46 @@ def decode_merge(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
     args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                         max_context_len, partition_size, workspace)
     _check(library().pa_decode_merge(*args))
+
+
+def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+            max_query_len=None, max_context_len=None):
+    """Paged prefill attention into ``out`` (see ``pa_prefill`` in include/pa.h):
+    the new tokens of sequence s are rows query_start[s]:query_start[s + 1] of
+    ``q``, the last of its context_lens[s] cached tokens, each attending to the
+    tokens up to its own position.
+
+    ``max_query_len`` and ``max_context_len`` should be passed by callers that
+    know them; when None they are read from the device, which synchronizes the
+    stream.
+    """
+    _dev_tensor(q, "q", ndim=3)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _dev_tensor(out, "out", dtype=q.dtype, ndim=3)
+    if k_cache.dtype != q.dtype:
+        raise ValueError(f"k_cache must be {q.dtype}, got {k_cache.dtype}")
+    nb, hkv, bs, d2 = _check_caches(k_cache, v_cache)
+    _dev_tensor(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev_tensor(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _dev_tensor(query_start, "query_start", dtype=torch.int32, ndim=1)
+    n, hq, d = q.shape
+    s = context_lens.shape[0]
+    if tuple(out.shape) != (n, hq, d):
+        raise ValueError("out must have the shape of q")
+    if d2 != d:
+        raise ValueError("cache head_dim differs from q")
+    if block_tables.shape[0] != s or query_start.shape[0] != s + 1:
+        raise ValueError("one block table row and one context length per sequence, num_seqs + 1 query starts")
+    if max_query_len is None:
+        max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if s else 0
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if s else 0
+    _check(library().pa_prefill(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(),
+                                float(scale), bs, s, n, hq, hkv, d, nb, block_tables.shape[1],
+                                int(max_query_len), int(max_context_len), _DTYPES[q.dtype], _stream(q)))
+    return out
 
 
 def write_cache(k, v, k_cache, v_cache, slot_mapping):

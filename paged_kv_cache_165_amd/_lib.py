@@ -21,7 +21,7 @@ PA_OK = 0
 EXPORTED = (
     "pa_abi_version", "pa_status_string", "pa_last_error", "pa_default_partition_size",
     "pa_decode_workspace_size", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
-    "pa_write_cache", "pa_copy_blocks",
+    "pa_prefill", "pa_write_cache", "pa_copy_blocks",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_prefill", "pa_bm_share", "pa_bm_append", "pa_bm_free",
     "pa_bm_block_tables", "pa_bm_num_free", "pa_bm_blocks_in_use", "pa_bm_refcount", "pa_bm_seq_tokens",
     "pa_bm_blocks_without_sharing", "pa_bm_check",
@@ -64,6 +64,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             f = getattr(lib, name)
             f.restype = _i
             f.argtypes = _DECODE_ARGS
+        lib.pa_prefill.restype = _i
+        lib.pa_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _i, _i, _i, _i, _i, _i,
+                                   _i, _i, _i, _i, _i, _vp]
         lib.pa_write_cache.restype = _i
         lib.pa_write_cache.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
         lib.pa_copy_blocks.restype = _i

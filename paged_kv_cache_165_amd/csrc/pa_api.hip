@@ -282,6 +282,66 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void*
     return PA_OK;
 }
 
+pa_status_t pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* query_start, float scale, int block_size, int num_seqs,
+                       int num_tokens, int num_heads, int num_kv_heads, int head_dim,
+                       int num_blocks, int max_blocks_per_seq, int max_query_len,
+                       int max_context_len, pa_dtype_t dtype, void* stream) {
+    if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        num_blocks <= 0 || max_blocks_per_seq <= 0 || max_query_len < 0 || max_context_len < 0 ||
+        block_size <= 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_seqs=%d num_tokens=%d num_heads=%d "
+                    "num_kv_heads=%d head_dim=%d num_blocks=%d max_blocks_per_seq=%d max_query_len=%d "
+                    "max_context_len=%d block_size=%d)", num_seqs, num_tokens, num_heads, num_kv_heads,
+                    head_dim, num_blocks, max_blocks_per_seq, max_query_len, max_context_len, block_size);
+    if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if (num_heads % num_kv_heads != 0)
+        return fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    const int group = num_heads / num_kv_heads;
+    if (!pa::prefill_supported(dtype, head_dim, group))
+        return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for dtype=%d head_dim=%d group=%d "
+                    "(bfloat16 or float16; head_dim 64/128/256; group 1/2/4/8/16)",
+                    static_cast<int>(dtype), head_dim, group);
+    if (!is_pow2(block_size) || block_size < 4 || block_size > 256)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two in [4, 256]", block_size);
+    if (static_cast<long long>(max_blocks_per_seq) * block_size < max_context_len)
+        return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size = %lld < max_context_len %d",
+                    static_cast<long long>(max_blocks_per_seq) * block_size, max_context_len);
+    if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+        return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return fail(PA_ERR_INVALID_ARG, "q, out, k_cache and v_cache must be 16-byte aligned");
+    if (out == q) return fail(PA_ERR_INVALID_ARG, "out aliases q");
+    pa::PrefillParams p;
+    p.out = out;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.query_start = query_start;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.num_seqs = num_seqs;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.num_blocks = num_blocks;
+    p.max_blocks = max_blocks_per_seq;
+    p.max_ctx = max_context_len;
+    p.max_q = max_query_len;
+    p.num_tokens = num_tokens;
+    p.log2_bs = log2i(block_size);
+    p.log2_vt = log2i(pa::v_tile_tokens(block_size));
+    hipError_t e = pa::launch_prefill(p, dtype, head_dim, group, static_cast<hipStream_t>(stream));
+    if (e == hipErrorInvalidConfiguration)
+        return fail(PA_ERR_UNSUPPORTED, "num_seqs %d x num_kv_heads %d x query tiles of max_query_len %d "
+                    "exceeds the grid limit", num_seqs, num_kv_heads, max_query_len);
+    if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+    return PA_OK;
+}
+
 pa_status_t pa_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                            const int32_t* slot_mapping, int num_tokens, int num_kv_heads,
                            int head_dim, int block_size, int num_blocks, pa_dtype_t dtype,

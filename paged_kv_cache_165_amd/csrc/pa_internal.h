@@ -39,6 +39,28 @@ struct DecodeParams {
     int ring_slots;     // item results a workgroup buffers in LDS before storing them
 };
 
+// Everything one prefill launch needs. Pointers are device pointers.
+struct PrefillParams {
+    void* out;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    const int32_t* query_start;  // [num_seqs + 1]
+    float scale_log2;            // scale * log2(e)
+    int num_seqs;
+    int num_heads;
+    int num_kv_heads;
+    int num_blocks;
+    int max_blocks;     // max_blocks_per_seq (row stride of block_tables)
+    int max_ctx;        // host bound on context lengths
+    int max_q;          // host bound on new tokens per sequence
+    int num_tokens;     // rows of q and out
+    int log2_bs;
+    int log2_vt;
+};
+
 // Tokens per transposed V tile: V rows of a block are stored as tiles of
 // this many tokens, head_dim-major.
 inline int v_tile_tokens(int block_size) { return block_size < 16 ? block_size : 16; }
@@ -58,6 +80,10 @@ hipError_t launch_decode_merge(const DecodeParams& p, pa_dtype_t dt, int head_di
 bool decode_supported(pa_dtype_t dt, int head_dim, int group);
 bool decode_uses_mfma(pa_dtype_t dt, int group);
 int decode_min_block_size(pa_dtype_t dt, int head_dim, int group);
+
+bool prefill_supported(pa_dtype_t dt, int head_dim, int group);
+hipError_t launch_prefill(const PrefillParams& p, pa_dtype_t dt, int head_dim, int group,
+                          hipStream_t stream);
 
 hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                               const int32_t* slots, int num_tokens, int num_kv_heads,

@@ -30,7 +30,7 @@ def _declared():
 
 def test_header_declares_expected_entry_points():
     names = _declared()
-    for n in ("pa_decode", "pa_write_cache", "pa_copy_blocks", "pa_decode_workspace_size"):
+    for n in ("pa_decode", "pa_prefill", "pa_write_cache", "pa_copy_blocks", "pa_decode_workspace_size"):
         assert n in names
 
 
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(L.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
 
 
 def test_status_strings_and_workspace_size():
@@ -93,6 +93,43 @@ def test_decode_rejects_before_launch(over, status, msg):
 def test_decode_empty_batch_is_noop():
     lib, _ = _lib()
     assert _decode(lib, S=0, out=0, q=0, k=0, v=0, tables=0, lens=0) == 0
+
+
+def _prefill(lib, **over):
+    args = dict(out=16, q=32, k=48, v=64, tables=80, lens=96, qs=112, scale=0.1, bs=16, S=2, T=40, Hq=8, Hkv=2,
+                D=128, NB=10, maxblk=4, maxq=32, maxctx=64, dtype=1, stream=None)
+    args.update(over)
+    return lib.pa_prefill(args["out"], args["q"], args["k"], args["v"], args["tables"], args["lens"], args["qs"],
+                          args["scale"], args["bs"], args["S"], args["T"], args["Hq"], args["Hkv"], args["D"],
+                          args["NB"], args["maxblk"], args["maxq"], args["maxctx"], args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(Hq=7), 1, b"multiple of num_kv_heads"),
+    (dict(Hq=64, Hkv=2), 2, b"no prefill kernel"),   # group 32
+    (dict(dtype=0), 2, b"no prefill kernel"),        # float32
+    (dict(D=96), 2, b"no prefill kernel"),
+    (dict(bs=12), 2, b"power of two"),
+    (dict(bs=512), 2, b"power of two"),
+    (dict(T=-1), 1, b"zero size"),
+    (dict(maxq=-1), 1, b"zero size"),
+    (dict(maxblk=3), 1, b"max_blocks_per_seq"),
+    (dict(dtype=7), 1, b"unknown dtype"),
+    (dict(qs=0), 1, b"null pointer"),
+    (dict(out=8), 1, b"16-byte aligned"),
+    (dict(out=32), 1, b"aliases"),
+    (dict(scale=float("nan")), 1, b"scale"),
+])
+def test_prefill_rejects_before_launch(over, status, msg):
+    lib, _ = _lib()
+    assert _prefill(lib, **over) == status
+    assert msg in lib.pa_last_error()
+
+
+def test_prefill_empty_is_noop():
+    lib, _ = _lib()
+    assert _prefill(lib, S=0, out=0, q=0, k=0, v=0, tables=0, lens=0, qs=0) == 0
+    assert _prefill(lib, maxq=0, out=0, q=0, k=0, v=0, tables=0, lens=0, qs=0) == 0
 
 
 def test_write_and_copy_reject_before_launch():
