@@ -54,22 +54,39 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // Tile geometry for one head_dim.
 template <int D>
 struct PrefillShape {
-    static constexpr int NC = D >= 256 ? 2 : 4;   // 16-column blocks per wave
-    static constexpr int KT = D >= 256 ? 32 : 64;  // keys per LDS tile
-    static constexpr int KROW = D + 8;             // LDS K row stride (elements)
-    static constexpr int VROW = 32 + 8;            // LDS V row stride of a 32-key group (elements)
-    static constexpr int K_EL = KT * KROW;
-    static constexpr int V_EL = (KT / 32) * D * VROW;
-    static constexpr int BUF_EL = K_EL + V_EL;     // one buffer, in 16-bit elements
-    static constexpr int U = KT * D / 8 / kThreads;  // 16-byte K units (and V units) per thread
-    static_assert(U * kThreads * 8 == KT * D, "tile must split evenly over the threads");
+#ifndef PA_PREFILL_NC
+    static constexpr int NC = D >= 256 ? 1 : 2;    // 16-column blocks per wave
+#else
+    static constexpr int NC = PA_PREFILL_NC;
+#endif
+    static constexpr int KT = D >= 256 ? 32 : 64;   // keys per LDS tile
+    static constexpr int ROWB = D * 2;              // bytes of one K row
+    static constexpr int K_BYTES = KT * ROWB;       // K of a tile
+    static constexpr int V_BYTES = KT * ROWB;       // V of a tile
+    static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
+    static constexpr int UK = K_BYTES / 1024 / kWaves;  // 16-byte DMA loads of K per lane and tile
+    static constexpr int UV = V_BYTES / 1024 / kWaves;  // of V (blocks of 8 or more tokens)
+    static constexpr int UV4 = V_BYTES / 256 / kWaves;  // 4-byte DMA loads of V (blocks of 4 tokens)
+    static constexpr int TBL = 16;                  // block ids of one tile: KT / 4 at most
+    static_assert(UK * kWaves * 1024 == K_BYTES && UV * kWaves * 1024 == V_BYTES, "whole loads");
+    static_assert(KT / 4 <= TBL, "table slice");
 };
 
 template <int D>
 constexpr int prefill_query_tile(int g) { return kWaves * 16 * PrefillShape<D>::NC / g; }
 
 template <int D>
-constexpr size_t prefill_smem() { return 2 * static_cast<size_t>(PrefillShape<D>::BUF_EL) * 2; }
+constexpr size_t prefill_smem() {
+    return 2 * static_cast<size_t>(PrefillShape<D>::BUF_BYTES) + 2 * PrefillShape<D>::TBL * sizeof(int);
+}
+
+// Swizzle of the 16-byte chunks of K row r in LDS: the 16 rows one MFMA
+// operand read touches land on distinct banks.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+    if constexpr (D == 64) return (r >> 1) & 7;
+    else return r & 15;
+}
 
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma32(const u32x4& a, const u32x4& b, f32x4_t c) {
@@ -108,12 +125,52 @@ __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
     return u32x2{pack2<DT>(a, b, ra, rb), pack2<DT>(c, d, ra, rb)};
 }
 
+// Max and sum over the four lanes r16, r16 + 16, r16 + 32, r16 + 48 (one
+// column of a 16x16 MFMA result), every one of them receiving the result:
+// v_permlane16_swap exchanges rows 1 and 3 of its first operand with rows 0
+// and 2 of its second, v_permlane32_swap the upper half of the first with the
+// lower half of the second, so with both operands equal to v each pair of
+// results holds the two values to combine.
+__device__ __forceinline__ float column_max(float v) {
+    const uint32_t a = f32_as_u32(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    const uint32_t b = f32_as_u32(fmaxf(u32_as_f32(r0), u32_as_f32(r1)));
+    const auto t = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    const uint32_t t0 = t[0], t1 = t[1];
+    return fmaxf(u32_as_f32(t0), u32_as_f32(t1));
+}
+
+__device__ __forceinline__ float column_sum(float v) {
+    const uint32_t a = f32_as_u32(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    const uint32_t b = f32_as_u32(u32_as_f32(r0) + u32_as_f32(r1));
+    const auto t = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    const uint32_t t0 = t[0], t1 = t[1];
+    return u32_as_f32(t0) + u32_as_f32(t1);
+}
+
+typedef __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Global -> LDS load: every lane's `bytes` land at lds_base + lane * bytes
+// (lds_base is the same for the whole wave).
+template <int BYTES>
+__device__ __forceinline__ void dma(const void* src, void* lds_base) {
+    static_assert(BYTES == 4 || BYTES == 16, "load size");
+    if constexpr (BYTES == 16)
+        __builtin_amdgcn_global_load_lds((gptr_t)(const_cast<void*>(src)), (lptr_t)(lds_base), 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds((gptr_t)(const_cast<void*>(src)), (lptr_t)(lds_base), 4, 0, 0);
+}
+
 template <int DT, int D, int G>
 __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
     static_assert(DT == PA_BF16 || DT == PA_F16, "MFMA path is for 16-bit elements");
     static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
     using SH = PrefillShape<D>;
-    constexpr int NC = SH::NC, KT = SH::KT, KROW = SH::KROW, VROW = SH::VROW, U = SH::U;
+    constexpr int NC = SH::NC, KT = SH::KT, ROWB = SH::ROWB;
     constexpr int NK = D / 32;          // 16x16x32 products per S^T tile
     constexpr int NV = D / 16;          // 16-row blocks of O^T
     constexpr int TPW = 16 * NC / G;    // query tokens per wave
@@ -122,7 +179,9 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
     constexpr float kLazy = 8.f;
     constexpr float kFloor = -1e30f;    // running-max start: exp2(x - kFloor) never meets -inf - -inf
 
-    extern __shared__ __align__(16) uint16_t lds[];
+    // LDS: two tile buffers [K | V], then two table slices of block ids
+    extern __shared__ __align__(16) unsigned char lds[];
+    int* tbl = reinterpret_cast<int*>(lds + 2 * SH::BUF_BYTES);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -184,176 +243,189 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
     }
 
     if (nkt > 0) {
-        // ---- staging geometry: this thread's K units (key, 8-element chunk)
-        // and V units (d, 8 keys) of a tile
-        const int bs = 1 << p.log2_bs;
-        const int vt = 1 << p.log2_vt;
+        const int lb = p.log2_bs;
+        const int bs = 1 << lb;
+        const int lvt = p.log2_vt;
+        const int vt = 1 << lvt;
         const int hkv = p.num_kv_heads;
         const size_t blk_el = static_cast<size_t>(bs) * D;
         const char* kbase = static_cast<const char*>(p.k_cache);
         const char* vbase = static_cast<const char*>(p.v_cache);
         const int* trow = p.block_tables + static_cast<size_t>(s) * p.max_blocks;
         const int lastk = L - 1;
-        const bool v16 = vt >= 8;  // 8 consecutive keys are one 16-byte run
-        int k_key[U], k_ch[U], v_key[U], v_d[U], v_lds[U];
-#pragma unroll
-        for (int i = 0; i < U; ++i) {
-            const int uk = tid + i * kThreads;
-            k_key[i] = uk / (D / 8);
-            k_ch[i] = uk % (D / 8);
-            const int grp = uk / (4 * D);  // 32-key group of the tile
-            const int w = uk % (4 * D);
-            const int h = w / (2 * D);     // which 16 keys of the group
-            const int d = (w % (2 * D)) >> 1;
-            const int half = w & 1;        // which 8 of those 16
-            v_key[i] = 32 * grp + 16 * h + 8 * half;
-            v_d[i] = d;
-            // key 16h + 4j' + r of a group sits at position 8j' + 4h + r of its row
-            v_lds[i] = SH::K_EL + (grp * D + d) * VROW + 16 * half + 4 * h;
-        }
+        const int last_blk = lastk >> lb;
+        const int ntb = KT >= bs ? KT >> lb : 1;  // block ids one tile spans
         auto clamp_pid = [&](int pid) { return pid < 0 ? 0 : (pid >= p.num_blocks ? p.num_blocks - 1 : pid); };
-        // keys past the last one are read at a clamped, in-bounds position
-        // (their values are masked or zeroed)
-        auto kkey = [&](int t) { return min(t, lastk); };
-        auto vkey0 = [&](int t) { return min(t, v16 ? (lastk & ~7) : (lastk & ~3)); };
-        auto vkey1 = [&](int t) { return min(t + 4, lastk & ~3); };
+        // block id of table entry (kt * KT >> lb) + tid, for threads < ntb; the
+        // entries past the context's last block are never read
+        auto lookup = [&](int kt) {
+            const int e = min(((kt * KT) >> lb) + tid, last_blk);
+            return trow[tid < ntb ? e : 0];
+        };
+        auto head_el = [&](int pid) { return (static_cast<size_t>(pid) * hkv + kv) * blk_el; };
 
-        int tk[U], tv0[U], tv1[U];
-        auto fetch_table = [&](int kt) {
-            const int t0 = kt * KT;
+        // Issue the loads of tile kt into buffer `buf`. LDS row r of K holds
+        // key 32 (r / 32) + 8 ((r % 16) / 4) + 4 ((r / 16) % 2) + r % 4 of the
+        // tile, so that the two 16-row S^T tiles of a 32-key group give every
+        // lane eight consecutive keys; V keeps the cache's layout of 16-key
+        // tiles [D][16], the two 16-byte halves of row d swapped when bit 3 of
+        // d is set. Keys past the context are read at the last key (masked).
+        auto issue = [&](int kt, int buf) {
+            unsigned char* bk = lds + buf * SH::BUF_BYTES;
+            const int* tb = tbl + (kt & 1) * SH::TBL;
+            const int blk0 = (kt * KT) >> lb;
 #pragma unroll
-            for (int i = 0; i < U; ++i) {
-                tk[i] = trow[kkey(t0 + k_key[i]) >> p.log2_bs];
-                tv0[i] = trow[vkey0(t0 + v_key[i]) >> p.log2_bs];
-                if (!v16) tv1[i] = trow[vkey1(t0 + v_key[i]) >> p.log2_bs];
-                else tv1[i] = 0;
+            for (int i = 0; i < SH::UK; ++i) {
+                const int P = (wave * SH::UK + i) * 1024 + lane * 16;
+                const int r = P / ROWB;
+                const int ch = ((P % ROWB) >> 4) ^ k_swz<D>(r);
+                const int m = r & 15;
+                const int key = min(kt * KT + 32 * (r >> 5) + 8 * (m >> 2) + 4 * ((r >> 4) & 1) + (m & 3), lastk);
+                const int pid = tb[(key >> lb) - blk0];
+                const char* src = kbase + (head_el(pid) + static_cast<size_t>(key & (bs - 1)) * D) * E + ch * 16;
+                dma<16>(src, bk + (wave * SH::UK + i) * 1024);
             }
-        };
-        auto v_elem = [&](int pid, int t, int d) {
-            const int off = t & (bs - 1);
-            return (static_cast<size_t>(pid) * hkv + kv) * blk_el +
-                   static_cast<size_t>(off >> p.log2_vt) * D * vt + static_cast<size_t>(d) * vt + (off & (vt - 1));
-        };
-        u32x4 rk[U], rv[U];
-        auto fetch_kv = [&](int kt) {
-            const int t0 = kt * KT;
+            unsigned char* bv = bk + SH::K_BYTES;
+            if (lvt >= 3) {
 #pragma unroll
-            for (int i = 0; i < U; ++i) {
-                const int t = kkey(t0 + k_key[i]);
-                const size_t kel = (static_cast<size_t>(clamp_pid(tk[i])) * hkv + kv) * blk_el +
-                                   static_cast<size_t>(t & (bs - 1)) * D + 8 * k_ch[i];
-                rk[i] = *reinterpret_cast<const u32x4*>(kbase + kel * E);
-                const int tv = t0 + v_key[i];
-                if (v16) {
-                    rv[i] = *reinterpret_cast<const u32x4*>(vbase + v_elem(clamp_pid(tv0[i]), vkey0(tv), v_d[i]) * E);
-                } else {
-                    const u32x2 a = *reinterpret_cast<const u32x2*>(vbase + v_elem(clamp_pid(tv0[i]), vkey0(tv), v_d[i]) * E);
-                    const u32x2 b = *reinterpret_cast<const u32x2*>(vbase + v_elem(clamp_pid(tv1[i]), vkey1(tv), v_d[i]) * E);
-                    rv[i] = u32x4{a.x, a.y, b.x, b.y};
+                for (int i = 0; i < SH::UV; ++i) {
+                    const int P = (wave * SH::UV + i) * 1024 + lane * 16;
+                    const int sub = P / (D * 32);
+                    const int d = (P % (D * 32)) >> 5;
+                    const int half = ((P >> 4) & 1) ^ ((d >> 3) & 1);
+                    const int key = min(kt * KT + 16 * sub + 8 * half, lastk & ~7);
+                    const int pid = tb[(key >> lb) - blk0];
+                    const int off = key & (bs - 1);
+                    const size_t el = head_el(pid) + static_cast<size_t>(off >> lvt) * D * vt +
+                                      static_cast<size_t>(d) * vt + (off & (vt - 1));
+                    dma<16>(vbase + el * E, bv + (wave * SH::UV + i) * 1024);
                 }
-                // keys at or past nkeys are zeroed: their probability is 0,
-                // and a stale slot may hold a non-finite value
-                const int nv = nkeys - tv;
-                if (nv < 8) {
-                    const uint32_t lo = 0x0000ffffu, hi = 0xffff0000u;
-                    rv[i].x &= (nv > 0 ? lo : 0u) | (nv > 1 ? hi : 0u);
-                    rv[i].y &= (nv > 2 ? lo : 0u) | (nv > 3 ? hi : 0u);
-                    rv[i].z &= (nv > 4 ? lo : 0u) | (nv > 5 ? hi : 0u);
-                    rv[i].w &= (nv > 6 ? lo : 0u) | (nv > 7 ? hi : 0u);
+            } else {
+#pragma unroll 4
+                for (int i = 0; i < SH::UV4; ++i) {
+                    const int P = (wave * SH::UV4 + i) * 256 + lane * 4;
+                    const int sub = P / (D * 32);
+                    const int d = (P % (D * 32)) >> 5;
+                    const int half = ((P >> 4) & 1) ^ ((d >> 3) & 1);
+                    const int key = min(kt * KT + 16 * sub + 8 * half + 2 * ((P >> 2) & 3), lastk & ~1);
+                    const int pid = tb[(key >> lb) - blk0];
+                    const int off = key & (bs - 1);
+                    const size_t el = head_el(pid) + static_cast<size_t>(d) * vt + off;
+                    dma<4>(vbase + el * E, bv + (wave * SH::UV4 + i) * 256);
                 }
-            }
-        };
-        auto store_tile = [&](int buf) {
-            uint16_t* b = lds + buf * SH::BUF_EL;
-#pragma unroll
-            for (int i = 0; i < U; ++i) {
-                *reinterpret_cast<u32x4*>(b + k_key[i] * KROW + 8 * k_ch[i]) = rk[i];
-                *reinterpret_cast<u32x2*>(b + v_lds[i]) = u32x2{rv[i].x, rv[i].y};
-                *reinterpret_cast<u32x2*>(b + v_lds[i] + 8) = u32x2{rv[i].z, rv[i].w};
             }
         };
 
         // ---- reduce one LDS tile
         auto compute = [&](int kt, int buf) {
-            const uint16_t* bk = lds + buf * SH::BUF_EL;
-            const uint16_t* bv = bk + SH::K_EL;
+            const unsigned char* bk = lds + buf * SH::BUF_BYTES;
+            const unsigned char* bv = bk + SH::K_BYTES;
 #pragma unroll
             for (int g32 = 0; g32 < KT / 32; ++g32) {
                 const int tok0 = kt * KT + 32 * g32;
                 if (tok0 > pw_max) break;  // uniform: past this wave's last position
-                f32x4_t st[2][NC];
+                // every operand read of the step first: K rows of both S^T
+                // tiles, then V^T rows d = 16v + r16 of keys tok0 + 8j .. + 7
+                // (16-key tile 2 g32 + j / 2, half j % 2)
+                u32x4 kf[2][NK];
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    u32x4 kf[NK];
-                    const uint16_t* krow = bk + (32 * g32 + 16 * tt + r16) * KROW + 8 * j;
+                    const int r = 32 * g32 + 16 * tt + r16;
+                    const unsigned char* krow = bk + r * ROWB;
 #pragma unroll
-                    for (int c = 0; c < NK; ++c) kf[c] = *reinterpret_cast<const u32x4*>(krow + 32 * c);
+                    for (int c = 0; c < NK; ++c)
+                        kf[tt][c] = *reinterpret_cast<const u32x4*>(krow + (((4 * c + j) ^ k_swz<D>(r)) << 4));
+                }
+                u32x4 vf[NV];
+                {
+                    const int vsub = 2 * g32 + (j >> 1);
+                    const int vh = (j & 1) ^ ((r16 >> 3) & 1);
+                    const unsigned char* vrow = bv + (vsub * D + r16) * 32 + vh * 16;
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) vf[v] = *reinterpret_cast<const u32x4*>(vrow + 16 * v * 32);
+                }
+                f32x4_t st[2][NC];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                     for (int n = 0; n < NC; ++n) {
                         f32x4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int c = 0; c < NK; ++c) a = mfma32<DT>(kf[c], qf[n][c], a);
+                        for (int c = 0; c < NK; ++c) a = mfma32<DT>(kf[tt][c], qf[n][c], a);
                         st[tt][n] = a;
                     }
-                }
-                // keys at positions past a column's own are masked (only the
-                // diagonal groups have any)
+                // st[tt][n][r] is key tok0 + 8j + 4tt + r of column r16 of block n.
+                // Keys past a column's own position are masked (only the
+                // diagonal groups have any; keys past the context are among them).
                 const bool diag = tok0 + 31 > pw_min;
-                u32x4 pb[NC];
+                float x[NC][8], tmax[NC];
+                bool need_any = false;
 #pragma unroll
                 for (int n = 0; n < NC; ++n) {
-                    float x[8];
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const int key = tok0 + 16 * tt + 4 * j + r;
+                            const int key = tok0 + 8 * j + 4 * tt + r;
                             const bool ok = !diag || key <= pcol[n];
-                            x[4 * tt + r] = ok ? st[tt][n][r] * p.scale_log2 : -INFINITY;
+                            x[n][4 * tt + r] = ok ? st[tt][n][r] * p.scale_log2 : -INFINITY;
                         }
-                    float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-                    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-                    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-                    const bool need = tmax > m_run[n] + kLazy;
-                    if (__any(need)) {
-                        const float mn = need ? tmax : m_run[n];
+                    const float t = fmaxf(fmaxf(fmaxf(x[n][0], x[n][1]), fmaxf(x[n][2], x[n][3])),
+                                          fmaxf(fmaxf(x[n][4], x[n][5]), fmaxf(x[n][6], x[n][7])));
+                    tmax[n] = column_max(t);
+                    need_any |= tmax[n] > m_run[n] + kLazy;
+                }
+                if (__any(need_any)) {
+#pragma unroll
+                    for (int n = 0; n < NC; ++n) {
+                        const float mn = tmax[n] > m_run[n] + kLazy ? tmax[n] : m_run[n];
                         const float alpha = fast_exp2(m_run[n] - mn);
 #pragma unroll
                         for (int v = 0; v < NV; ++v) acc[n][v] *= alpha;
                         lsum[n] *= alpha;
                         m_run[n] = mn;
                     }
+                }
+                u32x4 pb[NC];
+#pragma unroll
+                for (int n = 0; n < NC; ++n) {
                     float pr[8];
                     const float m = m_run[n];
-                    pb[n].x = pack2<DT>(fast_exp2(x[0] - m), fast_exp2(x[1] - m), pr[0], pr[1]);
-                    pb[n].y = pack2<DT>(fast_exp2(x[2] - m), fast_exp2(x[3] - m), pr[2], pr[3]);
-                    pb[n].z = pack2<DT>(fast_exp2(x[4] - m), fast_exp2(x[5] - m), pr[4], pr[5]);
-                    pb[n].w = pack2<DT>(fast_exp2(x[6] - m), fast_exp2(x[7] - m), pr[6], pr[7]);
+                    pb[n].x = pack2<DT>(fast_exp2(x[n][0] - m), fast_exp2(x[n][1] - m), pr[0], pr[1]);
+                    pb[n].y = pack2<DT>(fast_exp2(x[n][2] - m), fast_exp2(x[n][3] - m), pr[2], pr[3]);
+                    pb[n].z = pack2<DT>(fast_exp2(x[n][4] - m), fast_exp2(x[n][5] - m), pr[4], pr[5]);
+                    pb[n].w = pack2<DT>(fast_exp2(x[n][6] - m), fast_exp2(x[n][7] - m), pr[6], pr[7]);
                     lsum[n] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
                 }
-                const uint16_t* vrow = bv + (g32 * D + r16) * VROW + 8 * j;
+                // keys past the context may hold anything: zero their V
+                const int nv = tok0 + 32 > L ? L - (tok0 + 8 * j) : 8;
+                const uint32_t lo = 0x0000ffffu, hi = 0xffff0000u;
+                const u32x4 vm = {(nv > 0 ? lo : 0u) | (nv > 1 ? hi : 0u), (nv > 2 ? lo : 0u) | (nv > 3 ? hi : 0u),
+                                  (nv > 4 ? lo : 0u) | (nv > 5 ? hi : 0u), (nv > 6 ? lo : 0u) | (nv > 7 ? hi : 0u)};
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
-                    const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + 16 * v * VROW);
+                    const u32x4 a = vf[v] & vm;
 #pragma unroll
-                    for (int n = 0; n < NC; ++n) acc[n][v] = mfma32<DT>(vf, pb[n], acc[n][v]);
+                    for (int n = 0; n < NC; ++n) acc[n][v] = mfma32<DT>(a, pb[n], acc[n][v]);
                 }
             }
         };
 
-        // ---- pipeline: tile kt is reduced while tile kt+1 is fetched and the
-        // block ids of tile kt+2 are read; fetches past the last tile repeat it
-        fetch_table(0);
-        fetch_kv(0);
-        fetch_table(min(1, nkt - 1));
-        store_tile(0);
+        // ---- pipeline: the loads of tile kt+1 fly while tile kt is reduced;
+        // block ids run one tile further ahead through tbl[tile & 1]
+        if (tid < SH::TBL) tbl[tid] = clamp_pid(lookup(0));
+        __syncthreads();
+        issue(0, 0);
+        {
+            const int t1 = clamp_pid(lookup(min(1, nkt - 1)));
+            if (tid < SH::TBL) tbl[SH::TBL + tid] = t1;
+        }
         __syncthreads();
         for (int kt = 0; kt < nkt; ++kt) {
-            fetch_kv(min(kt + 1, nkt - 1));
-            fetch_table(min(kt + 2, nkt - 1));
+            if (kt + 1 < nkt) issue(kt + 1, (kt + 1) & 1);
+            const int tnext = lookup(min(kt + 2, nkt - 1));
             compute(kt, kt & 1);
-            store_tile((kt + 1) & 1);  // the buffer nobody reads during this tile
+            if (tid < SH::TBL) tbl[(kt & 1) * SH::TBL + tid] = clamp_pid(tnext);
             __syncthreads();
         }
     }
@@ -361,9 +433,7 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
     // ---- normalise and store: acc[n][v][r] = O^T[d = 16v + 4j + r][column r16 of block n]
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-        float l = lsum[n];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = column_sum(lsum[n]);
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const int c = 16 * n + r16;
         const int u = uw0 + c / G;
