@@ -80,13 +80,16 @@ constexpr size_t prefill_smem() {
     return 2 * static_cast<size_t>(PrefillShape<D>::BUF_BYTES) + 2 * PrefillShape<D>::TBL * sizeof(int);
 }
 
-// Swizzle of the 16-byte chunks of K row r in LDS: the 16 rows one MFMA
-// operand read touches land on distinct banks.
+// Swizzle of the 16-byte chunks of K row r in LDS: any 8 (and any 16)
+// consecutive rows of one MFMA operand read land on distinct banks.
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
-    if constexpr (D == 64) return (r >> 1) & 7;
+    if constexpr (D == 64) return (r & 7) ^ ((r >> 3) & 1);
     else return r & 15;
 }
+
+// Which stored 16-byte half of V row d holds key half `h` (same rule).
+__device__ __forceinline__ int v_swz(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
 
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma32(const u32x4& a, const u32x4& b, f32x4_t c) {
@@ -135,10 +138,12 @@ __device__ __forceinline__ float column_max(float v) {
     const uint32_t a = f32_as_u32(v);
     const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
     const uint32_t r0 = r[0], r1 = r[1];
-    const uint32_t b = f32_as_u32(fmaxf(u32_as_f32(r0), u32_as_f32(r1)));
+    const float a0 = u32_as_f32(r0), a1 = u32_as_f32(r1);
+    const uint32_t b = f32_as_u32(a0 > a1 ? a0 : a1);
     const auto t = __builtin_amdgcn_permlane32_swap(b, b, false, false);
     const uint32_t t0 = t[0], t1 = t[1];
-    return fmaxf(u32_as_f32(t0), u32_as_f32(t1));
+    const float b0 = u32_as_f32(t0), b1 = u32_as_f32(t1);
+    return b0 > b1 ? b0 : b1;
 }
 
 __device__ __forceinline__ float column_sum(float v) {
@@ -214,8 +219,14 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
     const int pw_min = pos0 + uw0;
     const int pw_max = uw1 > uw0 ? pos0 + uw1 - 1 : -1;
 
-    // ---- query fragments and positions of this lane's columns
+    // ---- query fragments and positions of this lane's columns. A negative
+    // scale is folded into q (a sign flip is exact), so that the running
+    // maximum can be taken over the unscaled products.
     const int hq = p.num_heads;
+    const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+    // (a zero scale is taken as 1e-30: masked keys then stay at -inf, and
+    // exp2 of any finite logit times 1e-30 rounds to exactly 1)
+    const float sc = fmaxf(fabsf(p.scale_log2), 1e-30f);
     u32x4 qf[NC][NK];
     int pcol[NC];
 #pragma unroll
@@ -227,20 +238,25 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
         const char* qrow = static_cast<const char*>(p.q) +
                            ((static_cast<size_t>(row0 + u) * hq + h) * D + 8 * j) * E;
 #pragma unroll
-        for (int c2 = 0; c2 < NK; ++c2) qf[n][c2] = *reinterpret_cast<const u32x4*>(qrow + 64 * c2);
+        for (int c2 = 0; c2 < NK; ++c2) qf[n][c2] = *reinterpret_cast<const u32x4*>(qrow + 64 * c2) ^ qsign;
     }
 
-    f32x4_t acc[NC][NV];
-#pragma unroll
-    for (int n = 0; n < NC; ++n)
-#pragma unroll
-        for (int v = 0; v < NV; ++v) acc[n][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run[NC], lsum[NC];
+    // O^T accumulators, and per block one more 16x16 tile whose row 0 sums
+    // the probabilities: its A operand is 1 in row 0 and 0 elsewhere, so the
+    // softmax denominator comes out of the same MFMA pipe as the numerator
+    // and sums exactly the rounded weights the numerator multiplies.
+    f32x4_t acc[NC][NV], accl[NC];
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-        m_run[n] = kFloor;
-        lsum[n] = 0.f;
+        accl[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[n][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    constexpr uint32_t kOne2 = DT == PA_BF16 ? 0x3f803f80u : 0x3c003c00u;  // two 1.0 elements
+    const u32x4 ones = r16 == 0 ? u32x4{kOne2, kOne2, kOne2, kOne2} : u32x4{0u, 0u, 0u, 0u};
+    float m_run[NC];  // running max of the scaled logits, log2 units
+#pragma unroll
+    for (int n = 0; n < NC; ++n) m_run[n] = kFloor;
 
     if (nkt > 0) {
         const int lb = p.log2_bs;
@@ -255,6 +271,7 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
         const int lastk = L - 1;
         const int last_blk = lastk >> lb;
         const int ntb = KT >= bs ? KT >> lb : 1;  // block ids one tile spans
+        const bool big = bs >= 16;                 // every aligned 16 keys share a block
         auto clamp_pid = [&](int pid) { return pid < 0 ? 0 : (pid >= p.num_blocks ? p.num_blocks - 1 : pid); };
         // block id of table entry (kt * KT >> lb) + tid, for threads < ntb; the
         // entries past the context's last block are never read
@@ -264,54 +281,85 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
         };
         auto head_el = [&](int pid) { return (static_cast<size_t>(pid) * hkv + kv) * blk_el; };
 
-        // Issue the loads of tile kt into buffer `buf`. LDS row r of K holds
-        // key 32 (r / 32) + 8 ((r % 16) / 4) + 4 ((r / 16) % 2) + r % 4 of the
-        // tile, so that the two 16-row S^T tiles of a 32-key group give every
-        // lane eight consecutive keys; V keeps the cache's layout of 16-key
-        // tiles [D][16], the two 16-byte halves of row d swapped when bit 3 of
-        // d is set. Keys past the context are read at the last key (masked).
+        // Static part of this lane's loads. LDS row r of K holds key
+        // 32 (r / 32) + 8 ((r % 16) / 4) + 4 ((r / 16) % 2) + r % 4 of the tile,
+        // so that the two 16-row S^T tiles of a 32-key group give every lane
+        // eight consecutive keys; chunk ch of row r sits at ch ^ k_swz(r). One
+        // K load instruction covers rows of one aligned 16-key group. V keeps
+        // the cache's layout of 16-key tiles [D][16], its two 16-byte halves
+        // stored in the order v_swz(d); one 16-byte V load instruction covers
+        // rows of one 16-key tile.
+        int k_key[SH::UK], k_chb[SH::UK], v_d[SH::UV], v_half[SH::UV];
+#pragma unroll
+        for (int i = 0; i < SH::UK; ++i) {
+            const int P = (wave * SH::UK + i) * 1024 + lane * 16;
+            const int r = P / ROWB;
+            const int m = r & 15;
+            k_key[i] = 32 * (r >> 5) + 8 * (m >> 2) + 4 * ((r >> 4) & 1) + (m & 3);
+            k_chb[i] = (((P % ROWB) >> 4) ^ k_swz<D>(r)) << 4;
+        }
+#pragma unroll
+        for (int i = 0; i < SH::UV; ++i) {
+            const int P = (wave * SH::UV + i) * 1024 + lane * 16;
+            v_d[i] = (P % (D * 32)) >> 5;
+            v_half[i] = ((P >> 4) & 1) ^ v_swz(v_d[i]);
+        }
+
+        // Issue the loads of tile kt into buffer `buf`; keys past the context
+        // are read at the last key's position (their values are masked).
         auto issue = [&](int kt, int buf) {
             unsigned char* bk = lds + buf * SH::BUF_BYTES;
-            const int* tb = tbl + (kt & 1) * SH::TBL;
-            const int blk0 = (kt * KT) >> lb;
-#pragma unroll
-            for (int i = 0; i < SH::UK; ++i) {
-                const int P = (wave * SH::UK + i) * 1024 + lane * 16;
-                const int r = P / ROWB;
-                const int ch = ((P % ROWB) >> 4) ^ k_swz<D>(r);
-                const int m = r & 15;
-                const int key = min(kt * KT + 32 * (r >> 5) + 8 * (m >> 2) + 4 * ((r >> 4) & 1) + (m & 3), lastk);
-                const int pid = tb[(key >> lb) - blk0];
-                const char* src = kbase + (head_el(pid) + static_cast<size_t>(key & (bs - 1)) * D) * E + ch * 16;
-                dma<16>(src, bk + (wave * SH::UK + i) * 1024);
-            }
             unsigned char* bv = bk + SH::K_BYTES;
-            if (lvt >= 3) {
+            const int* tb = tbl + (kt & 1) * SH::TBL;
+            const int t0 = kt * KT;
+            const int blk0 = t0 >> lb;
+            if (big) {
+                // one block per load instruction: its id is wave-uniform
+#pragma unroll
+                for (int i = 0; i < SH::UK; ++i) {
+                    const int g16 = (wave * SH::UK + i) * 1024 / ROWB;  // first LDS row of the instruction
+                    const int gkey = min(t0 + 32 * (g16 >> 5) + 4 * ((g16 >> 4) & 1) + 8 * ((g16 & 15) >> 2), lastk);
+                    const int pid = __builtin_amdgcn_readfirstlane(tb[(gkey >> lb) - blk0]);
+                    const int key = min(t0 + k_key[i], lastk);
+                    const char* src = kbase + (head_el(pid) + static_cast<size_t>(key & (bs - 1)) * D) * E + k_chb[i];
+                    dma<16>(src, bk + (wave * SH::UK + i) * 1024);
+                }
 #pragma unroll
                 for (int i = 0; i < SH::UV; ++i) {
-                    const int P = (wave * SH::UV + i) * 1024 + lane * 16;
-                    const int sub = P / (D * 32);
-                    const int d = (P % (D * 32)) >> 5;
-                    const int half = ((P >> 4) & 1) ^ ((d >> 3) & 1);
-                    const int key = min(kt * KT + 16 * sub + 8 * half, lastk & ~7);
-                    const int pid = tb[(key >> lb) - blk0];
-                    const int off = key & (bs - 1);
-                    const size_t el = head_el(pid) + static_cast<size_t>(off >> lvt) * D * vt +
-                                      static_cast<size_t>(d) * vt + (off & (vt - 1));
-                    dma<16>(vbase + el * E, bv + (wave * SH::UV + i) * 1024);
+                    const int sub = (wave * SH::UV + i) * 1024 / (D * 32);
+                    const int key = min(t0 + 16 * sub, lastk & ~15);
+                    const int pid = __builtin_amdgcn_readfirstlane(tb[(key >> lb) - blk0]);
+                    const size_t el = head_el(pid) + static_cast<size_t>((key & (bs - 1)) >> 4) * D * 16;
+                    dma<16>(vbase + el * E + v_d[i] * 32 + v_half[i] * 16, bv + (wave * SH::UV + i) * 1024);
                 }
             } else {
-#pragma unroll 4
-                for (int i = 0; i < SH::UV4; ++i) {
-                    const int P = (wave * SH::UV4 + i) * 256 + lane * 4;
-                    const int sub = P / (D * 32);
-                    const int d = (P % (D * 32)) >> 5;
-                    const int half = ((P >> 4) & 1) ^ ((d >> 3) & 1);
-                    const int key = min(kt * KT + 16 * sub + 8 * half + 2 * ((P >> 2) & 3), lastk & ~1);
+#pragma unroll
+                for (int i = 0; i < SH::UK; ++i) {
+                    const int key = min(t0 + k_key[i], lastk);
                     const int pid = tb[(key >> lb) - blk0];
-                    const int off = key & (bs - 1);
-                    const size_t el = head_el(pid) + static_cast<size_t>(d) * vt + off;
-                    dma<4>(vbase + el * E, bv + (wave * SH::UV4 + i) * 256);
+                    const char* src = kbase + (head_el(pid) + static_cast<size_t>(key & (bs - 1)) * D) * E + k_chb[i];
+                    dma<16>(src, bk + (wave * SH::UK + i) * 1024);
+                }
+                if (lvt == 3) {
+#pragma unroll
+                    for (int i = 0; i < SH::UV; ++i) {
+                        const int P = (wave * SH::UV + i) * 1024 + lane * 16;
+                        const int key = min(t0 + 16 * (P / (D * 32)) + 8 * v_half[i], lastk & ~7);
+                        const int pid = tb[(key >> lb) - blk0];
+                        const size_t el = head_el(pid) + static_cast<size_t>(v_d[i]) * 8;
+                        dma<16>(vbase + el * E, bv + (wave * SH::UV + i) * 1024);
+                    }
+                } else {
+#pragma unroll 4
+                    for (int i = 0; i < SH::UV4; ++i) {
+                        const int P = (wave * SH::UV4 + i) * 256 + lane * 4;
+                        const int d = (P % (D * 32)) >> 5;
+                        const int half = ((P >> 4) & 1) ^ v_swz(d);
+                        const int key = min(t0 + 16 * (P / (D * 32)) + 8 * half + 2 * ((P >> 2) & 3), lastk & ~1);
+                        const int pid = tb[(key >> lb) - blk0];
+                        const size_t el = head_el(pid) + static_cast<size_t>(d) * vt + (key & (bs - 1));
+                        dma<4>(vbase + el * E, bv + (wave * SH::UV4 + i) * 256);
+                    }
                 }
             }
         };
@@ -339,8 +387,7 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
                 u32x4 vf[NV];
                 {
                     const int vsub = 2 * g32 + (j >> 1);
-                    const int vh = (j & 1) ^ ((r16 >> 3) & 1);
-                    const unsigned char* vrow = bv + (vsub * D + r16) * 32 + vh * 16;
+                    const unsigned char* vrow = bv + (vsub * D + r16) * 32 + (((j & 1) ^ v_swz(r16)) << 4);
 #pragma unroll
                     for (int v = 0; v < NV; ++v) vf[v] = *reinterpret_cast<const u32x4*>(vrow + 16 * v * 32);
                 }
@@ -354,25 +401,32 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
                         for (int c = 0; c < NK; ++c) a = mfma32<DT>(kf[tt][c], qf[n][c], a);
                         st[tt][n] = a;
                     }
-                // st[tt][n][r] is key tok0 + 8j + 4tt + r of column r16 of block n.
-                // Keys past a column's own position are masked (only the
-                // diagonal groups have any; keys past the context are among them).
-                const bool diag = tok0 + 31 > pw_min;
-                float x[NC][8], tmax[NC];
+                // st[tt][n][r] is the unscaled logit of key tok0 + 8j + 4tt + r
+                // and column r16 of block n. Keys past a column's own position
+                // are masked; only the diagonal groups have any, and keys past
+                // the context are among them.
+                if (tok0 + 31 > pw_min) {
+#pragma unroll
+                    for (int n = 0; n < NC; ++n)
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (tok0 + 8 * j + 4 * tt + r > pcol[n]) st[tt][n][r] = -INFINITY;
+                }
+                float tmax[NC];
                 bool need_any = false;
 #pragma unroll
                 for (int n = 0; n < NC; ++n) {
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int key = tok0 + 8 * j + 4 * tt + r;
-                            const bool ok = !diag || key <= pcol[n];
-                            x[n][4 * tt + r] = ok ? st[tt][n][r] * p.scale_log2 : -INFINITY;
-                        }
-                    const float t = fmaxf(fmaxf(fmaxf(x[n][0], x[n][1]), fmaxf(x[n][2], x[n][3])),
-                                          fmaxf(fmaxf(x[n][4], x[n][5]), fmaxf(x[n][6], x[n][7])));
-                    tmax[n] = column_max(t);
+                    const f32x4_t a = st[0][n], b = st[1][n];
+                    float t = a[0] > a[1] ? a[0] : a[1];
+                    t = a[2] > t ? a[2] : t;
+                    t = a[3] > t ? a[3] : t;
+                    t = b[0] > t ? b[0] : t;
+                    t = b[1] > t ? b[1] : t;
+                    t = b[2] > t ? b[2] : t;
+                    t = b[3] > t ? b[3] : t;
+                    tmax[n] = column_max(t) * sc;
                     need_any |= tmax[n] > m_run[n] + kLazy;
                 }
                 if (__any(need_any)) {
@@ -382,32 +436,40 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
                         const float alpha = fast_exp2(m_run[n] - mn);
 #pragma unroll
                         for (int v = 0; v < NV; ++v) acc[n][v] *= alpha;
-                        lsum[n] *= alpha;
+                        accl[n] *= alpha;
                         m_run[n] = mn;
                     }
                 }
                 u32x4 pb[NC];
 #pragma unroll
                 for (int n = 0; n < NC; ++n) {
+                    const float m = -m_run[n];
                     float pr[8];
-                    const float m = m_run[n];
-                    pb[n].x = pack2<DT>(fast_exp2(x[n][0] - m), fast_exp2(x[n][1] - m), pr[0], pr[1]);
-                    pb[n].y = pack2<DT>(fast_exp2(x[n][2] - m), fast_exp2(x[n][3] - m), pr[2], pr[3]);
-                    pb[n].z = pack2<DT>(fast_exp2(x[n][4] - m), fast_exp2(x[n][5] - m), pr[4], pr[5]);
-                    pb[n].w = pack2<DT>(fast_exp2(x[n][6] - m), fast_exp2(x[n][7] - m), pr[6], pr[7]);
-                    lsum[n] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+                    float e[8];
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) e[4 * tt + r] = fast_exp2(fmaf(st[tt][n][r], sc, m));
+                    pb[n].x = pack2<DT>(e[0], e[1], pr[0], pr[1]);
+                    pb[n].y = pack2<DT>(e[2], e[3], pr[2], pr[3]);
+                    pb[n].z = pack2<DT>(e[4], e[5], pr[4], pr[5]);
+                    pb[n].w = pack2<DT>(e[6], e[7], pr[6], pr[7]);
                 }
                 // keys past the context may hold anything: zero their V
-                const int nv = tok0 + 32 > L ? L - (tok0 + 8 * j) : 8;
-                const uint32_t lo = 0x0000ffffu, hi = 0xffff0000u;
-                const u32x4 vm = {(nv > 0 ? lo : 0u) | (nv > 1 ? hi : 0u), (nv > 2 ? lo : 0u) | (nv > 3 ? hi : 0u),
-                                  (nv > 4 ? lo : 0u) | (nv > 5 ? hi : 0u), (nv > 6 ? lo : 0u) | (nv > 7 ? hi : 0u)};
+                if (tok0 + 32 > L) {
+                    const int nv = L - (tok0 + 8 * j);
+                    const uint32_t lo = 0x0000ffffu, hi = 0xffff0000u;
+                    const u32x4 vm = {(nv > 0 ? lo : 0u) | (nv > 1 ? hi : 0u), (nv > 2 ? lo : 0u) | (nv > 3 ? hi : 0u),
+                                      (nv > 4 ? lo : 0u) | (nv > 5 ? hi : 0u), (nv > 6 ? lo : 0u) | (nv > 7 ? hi : 0u)};
 #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    const u32x4 a = vf[v] & vm;
-#pragma unroll
-                    for (int n = 0; n < NC; ++n) acc[n][v] = mfma32<DT>(a, pb[n], acc[n][v]);
+                    for (int v = 0; v < NV; ++v) vf[v] &= vm;
                 }
+#pragma unroll
+                for (int n = 0; n < NC; ++n) accl[n] = mfma32<DT>(ones, pb[n], accl[n]);
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+#pragma unroll
+                    for (int n = 0; n < NC; ++n) acc[n][v] = mfma32<DT>(vf[v], pb[n], acc[n][v]);
             }
         };
 
@@ -430,10 +492,12 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
         }
     }
 
-    // ---- normalise and store: acc[n][v][r] = O^T[d = 16v + 4j + r][column r16 of block n]
+    // ---- normalise and store: acc[n][v][r] = O^T[d = 16v + 4j + r][column r16
+    // of block n]; the denominator of column r16 is row 0 of accl[n], held by
+    // lane (r16, j = 0)
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-        const float l = column_sum(lsum[n]);
+        const float l = column_sum(j == 0 ? accl[n][0] : 0.f);
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const int c = 16 * n + r16;
         const int u = uw0 + c / G;
