@@ -55,6 +55,9 @@ def parse():
                     help="instead of the headline line, drive the workload's sequences through the "
                          "multi-step decoder (native block manager + the three device calls) for this "
                          "many steps and report host and device time per step")
+    ap.add_argument("--prefill", choices=["prompts", "chunked"], default=None,
+                    help="instead of the headline line, time paged prefill attention (cache write of the "
+                         "new tokens + pa_prefill) on this workload and print its own line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -207,6 +210,121 @@ def engine_bench(args, dev):
     }), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
+
+
+def prefill_cpu_baseline(w, q_h, kc_h, vc_h, seconds: float):
+    """Time the oracle's paged prefill on the last rows of the workload's
+    sequences, cycling, until about `seconds` of CPU work has been done; one
+    BLAS thread."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    qs = w.query_start
+    rows_per_call = 8
+    done, t_used, flops = 0, 0.0, 0
+    t0 = time.perf_counter()
+    while t_used < seconds:
+        s = done % w.num_seqs
+        L, m = int(w.context_lens[s]), min(rows_per_call, int(w.query_lens[s]))
+        rows = np.arange(qs[s + 1] - m, qs[s + 1])
+        ts = time.perf_counter()
+        oracle.paged_prefill(q_h[rows], kc_h, vc_h, w.block_tables[s:s + 1], [L], [0, m], w.scale,
+                             w.block_size, oracle.BF16)
+        t_used += time.perf_counter() - ts
+        flops += 4 * w.head_dim * w.num_heads * sum(L - m + i + 1 for i in range(m))
+        done += 1
+    wall = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.restore_original_limits()
+    return {
+        "value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+        "sample": f"{done} calls of the last {rows_per_call} new rows of one sequence, cycling over the "
+                  f"{w.num_seqs} sequences of {w.name}, float64 numpy oracle, 1 BLAS thread, {wall:.1f} s",
+    }
+
+
+def prefill_bench(args, dev):
+    """Paged prefill: each step writes the K/V rows of every sequence's new
+    tokens into their slots (pa_write_cache) and runs pa_prefill over the
+    batch. `value` is causal attention TFLOP/s of the whole step (4 * D * Hq
+    multiply-add flops per visible (row, key) pair); `roofline` reports the
+    prefill kernel alone against the dense bf16 MFMA peak."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_165_amd as pa
+    from workloads import prefill as P
+    w = P.BUILDERS[args.prefill]()
+    progress(f"prefill workload {w.name}: {w.summary()}")
+    vals = P.make_values(w, device=dev, poison=True)
+    q, kc, vc = vals["q"], vals["k_cache"], vals["v_cache"]
+    g = torch.Generator(device=dev).manual_seed(w.seed + 1)
+    kn = torch.randn(w.num_tokens, w.num_kv_heads, w.head_dim, generator=g, device=dev).to(q.dtype)
+    vn = torch.randn(w.num_tokens, w.num_kv_heads, w.head_dim, generator=g, device=dev).to(q.dtype)
+    pos = w.positions()
+    seq_of = np.repeat(np.arange(w.num_seqs), w.query_lens)
+    slots_h = (w.block_tables[seq_of, pos // w.block_size].astype(np.int64) * w.block_size
+               + pos % w.block_size).astype(np.int32)
+    slots = torch.from_numpy(slots_h).to(dev)
+    tables = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    qs = torch.from_numpy(w.query_start).to(dev)
+    out = torch.empty_like(q)
+    pargs = (out, q, kc, vc, tables, lens, qs, w.scale, w.max_query_len, w.max_context_len)
+
+    def step():
+        pa.write_cache(kn, vn, kc, vc, slots)
+        pa.prefill(*pargs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ka.record()
+    for _ in range(args.steps):
+        pa.prefill(*pargs)
+    kb.record()
+    torch.cuda.synchronize()
+    k_us = 1e3 * ka.elapsed_time(kb) / args.steps
+    flops = w.flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (k_us * 1e-6) / 1e12
+    progress(f"step {ms_step * 1e3:.1f} us, prefill kernel {k_us:.1f} us per launch")
+    cpu = None
+    if not args.no_cpu_baseline:
+        def host(t):
+            t = t.detach().cpu().contiguous()
+            return t.view(torch.uint16).numpy() if t.dtype == torch.bfloat16 else t.numpy()
+        cpu = prefill_cpu_baseline(w, host(q), host(kc), host(vc), args.cpu_seconds)
+        progress(f"cpu baseline: {cpu}")
+    print(json.dumps({
+        "metric": "paged prefill attention: causal TFLOP/s",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {**w.summary(), "new_tokens": w.num_tokens, "attended_pairs": w.attended_pairs(),
+                   "flops": flops, "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(w.num_tokens / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill (pa_prefill_mfma)", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel_us_mean": round(k_us, 2),
+                     "kernel_timing": f"{args.steps} back-to-back launches between two HIP events on the launch stream"},
+        "cpu_baseline": cpu,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -232,6 +350,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.engine_steps:
         engine_bench(args, dev)
+        return
+    if args.prefill:
+        prefill_bench(args, dev)
         return
     progress(f"device {torch.cuda.get_device_name(dev)}; building workload {args.workload}")
     if args.block_size and args.workload != "gqa8b":
