@@ -16,27 +16,30 @@
 // (token, head) pair with the head fastest, so a wave holds TPW = 16 * NC / G
 // consecutive tokens. Query tiles are counted back from the last new token,
 // and the workgroup ids cover the last tile of every sequence first: the
-// tiles with the most keys start first.
+// tiles with the most keys start first. Two workgroups fit per CU.
 //
-// Keys go through LDS in tiles of KT tokens, double buffered: every thread
-// fetches its share of the next tile (block ids one tile further ahead) into
-// registers while the current tile is reduced, then writes it to the other
-// buffer. K rows are padded by 16 bytes so that the MFMA operand reads are
-// free of bank conflicts. V is kept as the cache keeps it, head_dim-major, in
-// groups of 32 keys whose order is permuted to the operand layout below.
+// Keys go through LDS in tiles of KT tokens, double buffered, loaded by
+// global_load_lds (no register holds staged data): the next tile's loads fly
+// while the current tile is reduced. Each load instruction covers keys of one
+// aligned 16-key group, so with blocks of 16 or more tokens its block id is
+// wave-uniform. K rows are stored in a permuted order (below) with their
+// 16-byte chunks XOR-swizzled; V keeps the cache's own 16-key tiles [D][16],
+// the two halves of a row swizzled; both keep the MFMA operand reads on
+// distinct banks.
 //
 // Per 32 keys and 16-column block, S^T = K Q^T is two 16x16 tiles of D/32
 // v_mfma_f32_16x16x32 (K rows as A from LDS, the query columns as B, held in
-// registers for the whole item). Lane (r16, j) of a tile holds keys 4j..4j+3
-// of column r16. After exp2 and rounding, the lane's eight probabilities --
-// keys 4j..4j+3 of the first tile and 16+4j..16+4j+3 of the second -- are
-// exactly the B operand of one v_mfma_f32_16x16x32 over those 32 keys, taken
-// as its k index 8j..8j+7; the A operand, V^T rows with the same key order, is
-// one 16-byte LDS read because the staging wrote V in that order. P never
-// leaves registers, and both products run at the double-rate 16x16x32 form.
-// The running max is rescaled lazily, only when a block's max exceeds it by
-// more than 2^8, as in the decode kernel.
-
+// registers for the whole item). The K rows of a 32-key group are stored so
+// that lane (r16, j) of the two tiles holds keys 8j..8j+3 and 8j+4..8j+7:
+// eight consecutive keys, which after exp2 and rounding are exactly the B
+// operand of one v_mfma_f32_16x16x32 over the 32 keys (k index 8j..8j+7),
+// whose A operand, V^T, is then a plain 16-byte read of the cache's V layout.
+// P never leaves registers, and both products run at the double-rate 16x16x32
+// form. The softmax keeps its running max over unscaled logits (a negative
+// scale is folded into q), reduces a column's four lanes with lane swaps,
+// rescales lazily (only when the max grows by more than 2^8, as in the decode
+// kernel), and takes its denominator from one more MFMA against a row of
+// ones.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -57,7 +60,7 @@ struct PrefillShape {
 #ifndef PA_PREFILL_NC
     static constexpr int NC = D >= 256 ? 1 : 2;    // 16-column blocks per wave
 #else
-    static constexpr int NC = PA_PREFILL_NC;
+    static constexpr int NC = D >= 256 ? 1 : PA_PREFILL_NC;
 #endif
     static constexpr int KT = D >= 256 ? 32 : 64;   // keys per LDS tile
     static constexpr int ROWB = D * 2;              // bytes of one K row
