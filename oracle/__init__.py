@@ -25,6 +25,8 @@ from .paged_attention import (  # noqa: F401
     paged_decode_partitioned,
     write_cache,
     copy_blocks,
+    write_cache_layers,
+    copy_blocks_layers,
     to_float64,
     v_tile,
     v_cache_shape,

@@ -49,6 +49,10 @@ Pins (all in ``tests/test_oracle.py``, run with ``-m "not gpu"``):
   write_cache             write probe (position 9 -> slot 29 -> block 7 offset 1),
                           skip slot -1, raw-bit copies of NaN payloads
   copy_blocks             whole-block copy, source untouched, precondition errors
+  write_cache_layers /    (tests/test_oracle_layers.py) the write probe and a copy
+  copy_blocks_layers      probe in every layer with layer-specific values, one
+                          layer equal to the single-layer call, planted mistakes
+                          (layer 0's rows everywhere, copying layer 0 only) caught
 No function here is "parity unpinned".
 """
 
@@ -437,3 +441,38 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray,
         k_new[d_id] = k_cache[s_id]
         v_new[d_id] = v_cache[s_id]
     return k_new, v_new
+
+
+# --------------------------------------------------------------------------
+# Several layers at once
+# --------------------------------------------------------------------------
+
+def write_cache_layers(k: np.ndarray, v: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                       slot_mapping, block_size: int) -> tuple[np.ndarray, np.ndarray]:
+    """``write_cache`` applied to every layer with the one slot mapping:
+    k, v [L, num_tokens, Hkv, D]; k_cache [L, NB, Hkv, B, D]; v_cache
+    [L, NB, Hkv, B/T, D, T]. A token lives at the same slot in every layer's
+    cache (its position in the sequence fixes the slot, [aiqz] "块表映射机制"),
+    and each layer's rows are its own. Returns new caches."""
+    if k_cache.ndim != 5 or v_cache.ndim != 6 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("layered arrays need a leading layer axis")
+    n_layers = k_cache.shape[0]
+    if v_cache.shape[0] != n_layers or k.shape[0] != n_layers or v.shape[0] != n_layers:
+        raise ValueError("one slice per layer")
+    out_k, out_v = [], []
+    for layer in range(n_layers):
+        kc, vc = write_cache(k[layer], v[layer], k_cache[layer], v_cache[layer], slot_mapping, block_size)
+        out_k.append(kc)
+        out_v.append(vc)
+    return np.stack(out_k), np.stack(out_v)
+
+
+def copy_blocks_layers(k_cache: np.ndarray, v_cache: np.ndarray,
+                       src_dst_pairs) -> tuple[np.ndarray, np.ndarray]:
+    """``copy_blocks`` applied to every layer with the same pairs: a block
+    shared by sequences is shared in every layer, so copy-on-write copies it
+    in all of them ([aiqz] "前缀共享机制"). Returns new caches."""
+    if k_cache.ndim != 5 or v_cache.ndim != 6 or k_cache.shape[0] != v_cache.shape[0]:
+        raise ValueError("layered caches need the same leading layer axis")
+    pairs = [copy_blocks(k_cache[layer], v_cache[layer], src_dst_pairs) for layer in range(k_cache.shape[0])]
+    return np.stack([p[0] for p in pairs]), np.stack([p[1] for p in pairs])
