@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 typedef enum pa_dtype {
     PA_F32 = 0,  /* IEEE binary32 */
@@ -240,6 +240,28 @@ pa_status_t pa_write_cache(const void* k, const void* v, void* k_cache, void* v_
 pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
                            int num_pairs, int num_kv_heads, int block_size, int head_dim,
                            int num_blocks, pa_dtype_t dtype, void* stream);
+
+/*
+ * Multi-layer forms: one launch applies the same slot mapping, or the same
+ * copy pairs, to the caches of num_layers layers -- a token's K/V rows go
+ * into every layer's cache at its one slot, and a copy-on-write duplicates a
+ * block in every layer ([aiqz] 前缀共享机制: the copy is of the whole block).
+ * Layer l's caches follow layer l - 1's in one allocation:
+ *   k_cache  [num_layers][num_blocks][num_kv_heads][block_size][head_dim]
+ *   v_cache  [num_layers][num_blocks][num_kv_heads][block_size / T][head_dim][T]
+ *   k, v     [num_layers][num_tokens][num_kv_heads][head_dim]   (write only)
+ * Each layer's result is exactly what pa_write_cache / pa_copy_blocks would
+ * give on that layer's slice, with the same argument rules; num_layers = 1
+ * is those calls, num_layers = 0 a no-op, at most 65535 layers
+ * (PA_ERR_UNSUPPORTED beyond).
+ */
+pa_status_t pa_write_cache_layers(const void* k, const void* v, void* k_cache, void* v_cache,
+                                  const int32_t* slot_mapping, int num_tokens, int num_layers,
+                                  int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                  pa_dtype_t dtype, void* stream);
+pa_status_t pa_copy_blocks_layers(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
+                                  int num_pairs, int num_layers, int num_kv_heads, int block_size,
+                                  int head_dim, int num_blocks, pa_dtype_t dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -32,6 +32,7 @@ __all__ = [
     "PaError", "library", "default_partition_size", "workspace_size", "alloc_workspace",
     "v_tile", "v_cache_shape", "alloc_cache",
     "decode", "decode_partitions", "decode_merge", "prefill", "write_cache", "copy_blocks",
+    "alloc_cache_layers", "write_cache_layers", "copy_blocks_layers",
 ]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16, torch.float16: _lib.PA_F16}
@@ -241,3 +242,50 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs):
     _check(library().pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src_dst_pairs.data_ptr(),
                                     src_dst_pairs.shape[0], hkv, bs, d, nb, _DTYPES[k_cache.dtype],
                                     _stream(k_cache)))
+
+
+def alloc_cache_layers(num_layers: int, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+                       dtype=torch.bfloat16, device="cuda"):
+    """Uninitialised (k_cache, v_cache) of ``num_layers`` layers in one
+    allocation each: [L, NB, Hkv, B, D] and [L, *v_cache_shape]."""
+    k = torch.empty(num_layers, num_blocks, num_kv_heads, block_size, head_dim, dtype=dtype, device=device)
+    v = torch.empty(num_layers, *v_cache_shape(num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype,
+                    device=device)
+    return k, v
+
+
+def _check_layer_caches(k_cache, v_cache):
+    _dev_tensor(k_cache, "k_cache", ndim=5)
+    if k_cache.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {k_cache.dtype}")
+    _dev_tensor(v_cache, "v_cache", dtype=k_cache.dtype, ndim=6)
+    nl, nb, hkv, bs, d = k_cache.shape
+    if tuple(v_cache.shape) != (nl, *v_cache_shape(nb, hkv, bs, d)):
+        raise ValueError(f"v_cache must have shape {(nl, *v_cache_shape(nb, hkv, bs, d))}, got {tuple(v_cache.shape)}")
+    return nl, nb, hkv, bs, d
+
+
+def write_cache_layers(k, v, k_cache, v_cache, slot_mapping):
+    """``write_cache`` for every layer in one launch (``pa_write_cache_layers``):
+    k, v [L, num_tokens, Hkv, D]; caches from ``alloc_cache_layers``."""
+    nl, nb, hkv, bs, d = _check_layer_caches(k_cache, v_cache)
+    _dev_tensor(k, "k", dtype=k_cache.dtype, ndim=4)
+    _dev_tensor(v, "v", dtype=k_cache.dtype, ndim=4)
+    _dev_tensor(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
+    n = slot_mapping.shape[0]
+    if tuple(k.shape) != (nl, n, hkv, d) or tuple(v.shape) != (nl, n, hkv, d):
+        raise ValueError("k and v must be [num_layers, num_tokens, num_kv_heads, head_dim]")
+    _check(library().pa_write_cache_layers(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                           slot_mapping.data_ptr(), n, nl, hkv, d, bs, nb, _DTYPES[k_cache.dtype],
+                                           _stream(k_cache)))
+
+
+def copy_blocks_layers(k_cache, v_cache, src_dst_pairs):
+    """``copy_blocks`` for every layer in one launch (``pa_copy_blocks_layers``)."""
+    nl, nb, hkv, bs, d = _check_layer_caches(k_cache, v_cache)
+    _dev_tensor(src_dst_pairs, "src_dst_pairs", dtype=torch.int32, ndim=2)
+    if src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be [num_pairs, 2]")
+    _check(library().pa_copy_blocks_layers(k_cache.data_ptr(), v_cache.data_ptr(), src_dst_pairs.data_ptr(),
+                                           src_dst_pairs.shape[0], nl, hkv, bs, d, nb, _DTYPES[k_cache.dtype],
+                                           _stream(k_cache)))

@@ -189,6 +189,60 @@ pa_status_t prepare_decode(void* out, const void* q, const void* k_cache, const 
     return PA_OK;
 }
 
+constexpr int kMaxLayers = 65535;  // grid z
+
+pa_status_t write_cache_layers(const void* k, const void* v, void* k_cache, void* v_cache,
+                               const int32_t* slot_mapping, int num_tokens, int num_layers, int num_kv_heads,
+                               int head_dim, int block_size, int num_blocks, pa_dtype_t dtype, void* stream) {
+    if (num_tokens < 0 || num_layers < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_tokens=%d num_layers=%d num_kv_heads=%d "
+                    "head_dim=%d block_size=%d num_blocks=%d)", num_tokens, num_layers, num_kv_heads, head_dim,
+                    block_size, num_blocks);
+    if (num_layers > kMaxLayers) return fail(PA_ERR_UNSUPPORTED, "num_layers %d > %d", num_layers, kMaxLayers);
+    if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    const int row_bytes = head_dim * elem_bytes(dtype);
+    if (row_bytes % 16 != 0)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim * element size = %d bytes is not a multiple of 16", row_bytes);
+    if (row_bytes > 32 * 1024)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim * element size = %d bytes is more than 32768", row_bytes);
+    if (!is_pow2(block_size) || block_size < 4)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two >= 4", block_size);
+    if (num_tokens == 0 || num_layers == 0) return PA_OK;
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PA_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
+    hipError_t e = pa::launch_write_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_layers, num_kv_heads,
+                                          head_dim, elem_bytes(dtype), block_size, num_blocks,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "cache write kernel launch");
+    return PA_OK;
+}
+
+pa_status_t copy_blocks_layers(void* k_cache, void* v_cache, const int32_t* src_dst_pairs, int num_pairs,
+                               int num_layers, int num_kv_heads, int block_size, int head_dim, int num_blocks,
+                               pa_dtype_t dtype, void* stream) {
+    if (num_pairs < 0 || num_layers < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_pairs=%d num_layers=%d num_kv_heads=%d "
+                    "block_size=%d head_dim=%d num_blocks=%d)", num_pairs, num_layers, num_kv_heads, block_size,
+                    head_dim, num_blocks);
+    if (num_layers > kMaxLayers) return fail(PA_ERR_UNSUPPORTED, "num_layers %d > %d", num_layers, kMaxLayers);
+    if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if (!is_pow2(block_size) || block_size < 4)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two >= 4", block_size);
+    const size_t block_bytes = static_cast<size_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
+    if (block_bytes % 16 != 0)
+        return fail(PA_ERR_UNSUPPORTED, "block of %zu bytes is not a multiple of 16", block_bytes);
+    if (num_pairs == 0 || num_layers == 0) return PA_OK;
+    if (!k_cache || !v_cache || !src_dst_pairs) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PA_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+    hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, src_dst_pairs, num_pairs, num_layers, block_bytes,
+                                          num_blocks, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "block copy kernel launch");
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,48 +400,30 @@ pa_status_t pa_write_cache(const void* k, const void* v, void* k_cache, void* v_
                            const int32_t* slot_mapping, int num_tokens, int num_kv_heads,
                            int head_dim, int block_size, int num_blocks, pa_dtype_t dtype,
                            void* stream) {
-    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
-        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_tokens=%d num_kv_heads=%d head_dim=%d "
-                    "block_size=%d num_blocks=%d)", num_tokens, num_kv_heads, head_dim, block_size, num_blocks);
-    if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
-    const int row_bytes = head_dim * elem_bytes(dtype);
-    if (row_bytes % 16 != 0)
-        return fail(PA_ERR_UNSUPPORTED, "head_dim * element size = %d bytes is not a multiple of 16", row_bytes);
-    if (row_bytes > 32 * 1024)
-        return fail(PA_ERR_UNSUPPORTED, "head_dim * element size = %d bytes is more than 32768", row_bytes);
-    if (!is_pow2(block_size) || block_size < 4)
-        return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two >= 4", block_size);
-    if (num_tokens == 0) return PA_OK;
-    if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
-    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
-        return fail(PA_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
-    hipError_t e = pa::launch_write_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
-                                          head_dim, elem_bytes(dtype), block_size, num_blocks,
-                                          static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "cache write kernel launch");
-    return PA_OK;
+    return write_cache_layers(k, v, k_cache, v_cache, slot_mapping, num_tokens, 1, num_kv_heads, head_dim,
+                              block_size, num_blocks, dtype, stream);
+}
+
+pa_status_t pa_write_cache_layers(const void* k, const void* v, void* k_cache, void* v_cache,
+                                  const int32_t* slot_mapping, int num_tokens, int num_layers,
+                                  int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                  pa_dtype_t dtype, void* stream) {
+    return write_cache_layers(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_layers, num_kv_heads,
+                              head_dim, block_size, num_blocks, dtype, stream);
 }
 
 pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
                            int num_pairs, int num_kv_heads, int block_size, int head_dim,
                            int num_blocks, pa_dtype_t dtype, void* stream) {
-    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
-        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_pairs=%d num_kv_heads=%d block_size=%d "
-                    "head_dim=%d num_blocks=%d)", num_pairs, num_kv_heads, block_size, head_dim, num_blocks);
-    if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
-    if (!is_pow2(block_size) || block_size < 4)
-        return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two >= 4", block_size);
-    const size_t block_bytes = static_cast<size_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
-    if (block_bytes % 16 != 0)
-        return fail(PA_ERR_UNSUPPORTED, "block of %zu bytes is not a multiple of 16", block_bytes);
-    if (num_pairs == 0) return PA_OK;
-    if (!k_cache || !v_cache || !src_dst_pairs) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
-    if (!aligned16(k_cache) || !aligned16(v_cache))
-        return fail(PA_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
-    hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, src_dst_pairs, num_pairs, block_bytes, num_blocks,
-                                          static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "block copy kernel launch");
-    return PA_OK;
+    return copy_blocks_layers(k_cache, v_cache, src_dst_pairs, num_pairs, 1, num_kv_heads, block_size, head_dim,
+                              num_blocks, dtype, stream);
+}
+
+pa_status_t pa_copy_blocks_layers(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
+                                  int num_pairs, int num_layers, int num_kv_heads, int block_size,
+                                  int head_dim, int num_blocks, pa_dtype_t dtype, void* stream) {
+    return copy_blocks_layers(k_cache, v_cache, src_dst_pairs, num_pairs, num_layers, num_kv_heads, block_size,
+                              head_dim, num_blocks, dtype, stream);
 }
 
 }  // extern "C"

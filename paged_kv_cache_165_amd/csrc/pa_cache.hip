@@ -22,7 +22,10 @@ __host__ __device__ constexpr int write_lds_row(int head_dim, int elem_bytes) {
     return head_dim + (elem_bytes == 2 ? 2 : 1);
 }
 
-// One workgroup per (chunk of up to 16 consecutive tokens, KV head).
+// One workgroup per (chunk of up to 16 consecutive tokens, KV head, layer).
+// Layer z reads its new rows at k + z * num_tokens * Hkv * D (the same for v)
+// and writes the caches at kc + z * layer_blocks * Hkv * B * D (the same for
+// vc); with one layer the strides are never used.
 // K: each token's row is one contiguous run in the cache, copied as 16-byte
 // vectors. V: the cache holds each block's rows as tiles of vt tokens stored
 // head_dim-major ([NB][Hkv][B/vt][D][vt]), so element d of a token at offset
@@ -41,6 +44,17 @@ __global__ __launch_bounds__(256) void pa_write_kernel(const u32x4* __restrict__
                                                        int row16, int log2_bs, int log2_vt, int log2_chunk,
                                                        long long pool_slots) {
     constexpr int E = sizeof(EW);
+    {
+        // this workgroup's layer: pool_slots is also the cache's layer
+        // stride in slots (num_blocks * B)
+        const size_t z = blockIdx.z;
+        const size_t new_el = static_cast<size_t>(num_tokens) * num_kv_heads * row16;  // in 16-byte vectors
+        const size_t cache_el = static_cast<size_t>(pool_slots) * num_kv_heads * row16;
+        k += z * new_el;
+        v += z * new_el;
+        kc += z * cache_el;
+        vc += z * cache_el * (16 / E);
+    }
     extern __shared__ __align__(16) unsigned char smem[];
     const int chunk = 1 << log2_chunk;
     const int ld = write_lds_row(head_dim, E);  // padded row (elements): odd dword stride
@@ -98,8 +112,9 @@ __global__ __launch_bounds__(256) void pa_write_kernel(const u32x4* __restrict__
     }
 }
 
-// grid (pairs, 2): y = 0 copies K, y = 1 copies V. A block is contiguous
-// ([Hkv][B][D]), so the copy is one linear run of block16 vectors.
+// grid (pairs, 2, layers): y = 0 copies K, y = 1 copies V, z is the layer
+// (its caches start z * num_blocks * block16 vectors in). A block is
+// contiguous ([Hkv][B][D]), so the copy is one linear run of block16 vectors.
 __global__ __launch_bounds__(256) void pa_copy_kernel(u32x4* __restrict__ kc, u32x4* __restrict__ vc,
                                                       const int32_t* __restrict__ pairs,
                                                       size_t block16, int num_blocks) {
@@ -107,7 +122,7 @@ __global__ __launch_bounds__(256) void pa_copy_kernel(u32x4* __restrict__ kc, u3
     const int src = pairs[2 * i];
     const int dst = pairs[2 * i + 1];
     if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-    u32x4* c = blockIdx.y == 0 ? kc : vc;
+    u32x4* c = (blockIdx.y == 0 ? kc : vc) + static_cast<size_t>(blockIdx.z) * num_blocks * block16;
     const u32x4* from = c + static_cast<size_t>(src) * block16;
     u32x4* to = c + static_cast<size_t>(dst) * block16;
     size_t x = threadIdx.x;
@@ -124,10 +139,10 @@ __global__ __launch_bounds__(256) void pa_copy_kernel(u32x4* __restrict__ kc, u3
 }
 
 hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
-                              const int32_t* slots, int num_tokens, int num_kv_heads,
+                              const int32_t* slots, int num_tokens, int num_layers, int num_kv_heads,
                               int head_dim, int elem_bytes, int block_size, int num_blocks,
                               hipStream_t stream) {
-    if (num_tokens == 0) return hipSuccess;
+    if (num_tokens == 0 || num_layers == 0) return hipSuccess;
     const int row16 = head_dim * elem_bytes / 16;
     const int ld = write_lds_row(head_dim, elem_bytes);
     // tokens per workgroup: 16, fewer for rows so wide that 16 would not fit
@@ -140,7 +155,7 @@ hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void*
     const int log2_vt = ilog2(v_tile_tokens(block_size));
     const long long pool_slots = static_cast<long long>(num_blocks) * block_size;
     const unsigned chunks = static_cast<unsigned>((num_tokens + (1 << log2_chunk) - 1) >> log2_chunk);
-    const dim3 grid(chunks, static_cast<unsigned>(num_kv_heads));
+    const dim3 grid(chunks, static_cast<unsigned>(num_kv_heads), static_cast<unsigned>(num_layers));
     if (elem_bytes == 2) {
         hipLaunchKernelGGL(pa_write_kernel<uint16_t>, grid, dim3(256), smem, stream,
                            static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
@@ -156,9 +171,10 @@ hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void*
 }
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
-                              size_t block_bytes, int num_blocks, hipStream_t stream) {
-    if (num_pairs == 0) return hipSuccess;
-    hipLaunchKernelGGL(pa_copy_kernel, dim3(static_cast<unsigned>(num_pairs), 2), dim3(256), 0, stream,
+                              int num_layers, size_t block_bytes, int num_blocks, hipStream_t stream) {
+    if (num_pairs == 0 || num_layers == 0) return hipSuccess;
+    hipLaunchKernelGGL(pa_copy_kernel, dim3(static_cast<unsigned>(num_pairs), 2, static_cast<unsigned>(num_layers)),
+                       dim3(256), 0, stream,
                        static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), pairs,
                        block_bytes / 16, num_blocks);
     return hipGetLastError();

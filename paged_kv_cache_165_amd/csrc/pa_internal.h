@@ -85,11 +85,12 @@ bool prefill_supported(pa_dtype_t dt, int head_dim, int group);
 hipError_t launch_prefill(const PrefillParams& p, pa_dtype_t dt, int head_dim, int group,
                           hipStream_t stream);
 
+// num_layers caches laid out one after another (see pa_write_cache_layers)
 hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
-                              const int32_t* slots, int num_tokens, int num_kv_heads,
+                              const int32_t* slots, int num_tokens, int num_layers, int num_kv_heads,
                               int head_dim, int elem_bytes, int block_size, int num_blocks,
                               hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
-                              size_t block_bytes, int num_blocks, hipStream_t stream);
+                              int num_layers, size_t block_bytes, int num_blocks, hipStream_t stream);
 
 }  // namespace pa

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(L.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 3
+    assert lib.pa_abi_version() == 4
 
 
 def test_status_strings_and_workspace_size():
@@ -144,6 +144,19 @@ def test_write_and_copy_reject_before_launch():
     assert lib.pa_copy_blocks(16, 16, 0, 2, 2, 16, 128, 10, 1, None) == 1
     assert lib.pa_copy_blocks(0, 0, 0, 0, 2, 16, 128, 10, 1, None) == 0
     assert lib.pa_copy_blocks(16, 16, 16, 2, 2, 16, 128, 10, 9, None) == 1
+
+
+def test_layered_write_and_copy_reject_before_launch():
+    lib, _ = _lib()
+    assert lib.pa_write_cache_layers(16, 16, 16, 16, 16, 3, -1, 2, 128, 16, 10, 1, None) == 1
+    assert lib.pa_write_cache_layers(16, 16, 16, 16, 16, 3, 70000, 2, 128, 16, 10, 1, None) == 2
+    assert b"65535" in lib.pa_last_error()
+    assert lib.pa_write_cache_layers(0, 0, 0, 0, 0, 3, 0, 2, 128, 16, 10, 1, None) == 0  # no layers
+    assert lib.pa_write_cache_layers(16, 16, 16, 16, 16, 3, 2, 2, 4, 16, 10, 1, None) == 2  # 8-byte rows
+    assert lib.pa_copy_blocks_layers(16, 16, 16, 2, -3, 2, 16, 128, 10, 1, None) == 1
+    assert lib.pa_copy_blocks_layers(0, 0, 0, 2, 0, 2, 16, 128, 10, 1, None) == 0
+    assert lib.pa_copy_blocks_layers(16, 16, 0, 2, 2, 2, 16, 128, 10, 1, None) == 1
+    assert lib.pa_copy_blocks_layers(16, 16, 16, 2, 2, 2, 12, 128, 10, 1, None) == 2
 
 
 def test_binding_refuses_cpu_tensors():
