@@ -58,6 +58,10 @@ def parse():
     ap.add_argument("--prefill", choices=["prompts", "chunked"], default=None,
                     help="instead of the headline line, time paged prefill attention (cache write of the "
                          "new tokens + pa_prefill) on this workload and print its own line")
+    ap.add_argument("--cache-layers", type=int, default=0,
+                    help="instead of the headline line, time the decode step's cache write (256 scattered "
+                         "tokens) and 192 copy-on-write block copies for this many layers: one layered launch "
+                         "against one launch per layer")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -213,6 +217,67 @@ def engine_bench(args, dev):
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
 
 
+def cache_layers_bench(args, dev):
+    """Cache maintenance for a model of `args.cache_layers` layers (GQA 8 KV
+    heads, head_dim 128, bf16, block 16): the decode step's write of 256 new
+    tokens at scattered slots, and 192 copy-on-write block copies, each as one
+    layered launch and as one launch per layer. Bytes are moved bytes (read +
+    written) of K and V."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_165_amd as pa
+    nl, nb, hkv, bs, d, dt = args.cache_layers, 4096, 8, 16, 128, torch.bfloat16
+    rng = np.random.default_rng(1670)
+    g = torch.Generator(device=dev).manual_seed(1670)
+    kc, vc = pa.alloc_cache_layers(nl, nb, hkv, bs, d, dt, device=dev)
+    kc.zero_()
+    vc.zero_()
+    blocks = rng.permutation(nb)
+    slots = torch.from_numpy((blocks[:256] * bs + rng.integers(0, bs, 256)).astype(np.int32)).to(dev)
+    pairs = torch.from_numpy(np.stack([blocks[256:448], blocks[448:640]], 1).astype(np.int32)).to(dev)
+    k = torch.randn(nl, 256, hkv, d, generator=g, device=dev).to(dt)
+    v = torch.randn(nl, 256, hkv, d, generator=g, device=dev).to(dt)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / args.steps
+
+    def write_per_layer():
+        for layer in range(nl):
+            pa.write_cache(k[layer], v[layer], kc[layer], vc[layer], slots)
+
+    def copy_per_layer():
+        for layer in range(nl):
+            pa.copy_blocks(kc[layer], vc[layer], pairs)
+
+    w1 = timed(lambda: pa.write_cache_layers(k, v, kc, vc, slots))
+    wn = timed(write_per_layer)
+    c1 = timed(lambda: pa.copy_blocks_layers(kc, vc, pairs))
+    cn = timed(copy_per_layer)
+    wbytes = 2 * 2 * nl * 256 * hkv * d * 2       # K and V rows, read once and written once
+    cbytes = 2 * 2 * nl * 192 * hkv * bs * d * 2  # K and V blocks, read once and written once
+    print(json.dumps({
+        "metric": "multi-layer cache write and block copy: one layered launch against one launch per layer",
+        "value": round(wn / w1, 3), "unit": "x (write speedup)", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "cache_layers", "layers": nl, "num_kv_heads": hkv, "head_dim": d, "block_size": bs,
+                   "write_tokens": 256, "copy_pairs": 192},
+        "write_us": {"layered": round(w1, 2), "per_layer": round(wn, 2)},
+        "write_gb_per_s": {"layered": round(wbytes / w1 / 1e3, 1), "per_layer": round(wbytes / wn / 1e3, 1)},
+        "copy_us": {"layered": round(c1, 2), "per_layer": round(cn, 2)},
+        "copy_gb_per_s": {"layered": round(cbytes / c1 / 1e3, 1), "per_layer": round(cbytes / cn / 1e3, 1)},
+        "copy_speedup": round(cn / c1, 3),
+    }), flush=True)
+
+
 def prefill_cpu_baseline(w, q_h, kc_h, vc_h, seconds: float):
     """Time the oracle's paged prefill on the last rows of the workload's
     sequences, cycling, until about `seconds` of CPU work has been done; one
@@ -353,6 +418,9 @@ def main():
         return
     if args.prefill:
         prefill_bench(args, dev)
+        return
+    if args.cache_layers:
+        cache_layers_bench(args, dev)
         return
     progress(f"device {torch.cuda.get_device_name(dev)}; building workload {args.workload}")
     if args.block_size and args.workload != "gqa8b":
