@@ -131,6 +131,14 @@ __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
     return u32x2{pack2<DT>(a, b, ra, rb), pack2<DT>(c, d, ra, rb)};
 }
 
+// max(a, b, c) in one instruction. The operands are finite or -inf here, so
+// the IEEE-mode quieting the compiler would add around fmaxf is not needed.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Max and sum over the four lanes r16, r16 + 16, r16 + 32, r16 + 48 (one
 // column of a 16x16 MFMA result), every one of them receiving the result:
 // v_permlane16_swap exchanges rows 1 and 3 of its first operand with rows 0
@@ -173,8 +181,11 @@ __device__ __forceinline__ void dma(const void* src, void* lds_base) {
         __builtin_amdgcn_global_load_lds((gptr_t)(const_cast<void*>(src)), (lptr_t)(lds_base), 4, 0, 0);
 }
 
+// Two waves per SIMD (two workgroups per CU): the register budget is held to
+// 256 per lane.
 template <int DT, int D, int G>
-__global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void pa_prefill_mfma(
+    PrefillParams p) {
     static_assert(DT == PA_BF16 || DT == PA_F16, "MFMA path is for 16-bit elements");
     static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
     using SH = PrefillShape<D>;
@@ -292,21 +303,18 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
         // the cache's layout of 16-key tiles [D][16], its two 16-byte halves
         // stored in the order v_swz(d); one 16-byte V load instruction covers
         // rows of one 16-key tile.
-        int k_key[SH::UK], k_chb[SH::UK], v_d[SH::UV], v_half[SH::UV];
-#pragma unroll
-        for (int i = 0; i < SH::UK; ++i) {
-            const int P = (wave * SH::UK + i) * 1024 + lane * 16;
-            const int r = P / ROWB;
+        // (recomputed at every tile: a few instructions, no registers held)
+        auto k_key = [&](int i) {
+            const int r = ((wave * SH::UK + i) * 1024 + lane * 16) / ROWB;
             const int m = r & 15;
-            k_key[i] = 32 * (r >> 5) + 8 * (m >> 2) + 4 * ((r >> 4) & 1) + (m & 3);
-            k_chb[i] = (((P % ROWB) >> 4) ^ k_swz<D>(r)) << 4;
-        }
-#pragma unroll
-        for (int i = 0; i < SH::UV; ++i) {
-            const int P = (wave * SH::UV + i) * 1024 + lane * 16;
-            v_d[i] = (P % (D * 32)) >> 5;
-            v_half[i] = ((P >> 4) & 1) ^ v_swz(v_d[i]);
-        }
+            return 32 * (r >> 5) + 8 * (m >> 2) + 4 * ((r >> 4) & 1) + (m & 3);
+        };
+        auto k_chb = [&](int i) {
+            const int P = (wave * SH::UK + i) * 1024 + lane * 16;
+            return (((P % ROWB) >> 4) ^ k_swz<D>(P / ROWB)) << 4;
+        };
+        auto v_d = [&](int i) { return (((wave * SH::UV + i) * 1024 + lane * 16) % (D * 32)) >> 5; };
+        auto v_half = [&](int i) { return (lane & 1) ^ v_swz(v_d(i)); };  // bit 4 of the LDS byte position
 
         // Issue the loads of tile kt into buffer `buf`; keys past the context
         // are read at the last key's position (their values are masked).
@@ -317,39 +325,50 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
             const int t0 = kt * KT;
             const int blk0 = t0 >> lb;
             if (big) {
-                // one block per load instruction: its id is wave-uniform
+                // one block per load instruction: its id is wave-uniform. All
+                // ids are read from LDS first, then the loads are issued.
+                int kpid[SH::UK], vpid[SH::UV];
 #pragma unroll
                 for (int i = 0; i < SH::UK; ++i) {
                     const int g16 = (wave * SH::UK + i) * 1024 / ROWB;  // first LDS row of the instruction
                     const int gkey = min(t0 + 32 * (g16 >> 5) + 4 * ((g16 >> 4) & 1) + 8 * ((g16 & 15) >> 2), lastk);
-                    const int pid = __builtin_amdgcn_readfirstlane(tb[(gkey >> lb) - blk0]);
-                    const int key = min(t0 + k_key[i], lastk);
-                    const char* src = kbase + (head_el(pid) + static_cast<size_t>(key & (bs - 1)) * D) * E + k_chb[i];
+                    kpid[i] = tb[(gkey >> lb) - blk0];
+                }
+#pragma unroll
+                for (int i = 0; i < SH::UV; ++i) {
+                    const int sub = (wave * SH::UV + i) * 1024 / (D * 32);
+                    vpid[i] = tb[(min(t0 + 16 * sub, lastk & ~15) >> lb) - blk0];
+                }
+#pragma unroll
+                for (int i = 0; i < SH::UK; ++i) {
+                    const int pid = __builtin_amdgcn_readfirstlane(kpid[i]);
+                    const int key = min(t0 + k_key(i), lastk);
+                    const char* src = kbase + (head_el(pid) + static_cast<size_t>(key & (bs - 1)) * D) * E + k_chb(i);
                     dma<16>(src, bk + (wave * SH::UK + i) * 1024);
                 }
 #pragma unroll
                 for (int i = 0; i < SH::UV; ++i) {
                     const int sub = (wave * SH::UV + i) * 1024 / (D * 32);
                     const int key = min(t0 + 16 * sub, lastk & ~15);
-                    const int pid = __builtin_amdgcn_readfirstlane(tb[(key >> lb) - blk0]);
+                    const int pid = __builtin_amdgcn_readfirstlane(vpid[i]);
                     const size_t el = head_el(pid) + static_cast<size_t>((key & (bs - 1)) >> 4) * D * 16;
-                    dma<16>(vbase + el * E + v_d[i] * 32 + v_half[i] * 16, bv + (wave * SH::UV + i) * 1024);
+                    dma<16>(vbase + el * E + v_d(i) * 32 + v_half(i) * 16, bv + (wave * SH::UV + i) * 1024);
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < SH::UK; ++i) {
-                    const int key = min(t0 + k_key[i], lastk);
+                    const int key = min(t0 + k_key(i), lastk);
                     const int pid = tb[(key >> lb) - blk0];
-                    const char* src = kbase + (head_el(pid) + static_cast<size_t>(key & (bs - 1)) * D) * E + k_chb[i];
+                    const char* src = kbase + (head_el(pid) + static_cast<size_t>(key & (bs - 1)) * D) * E + k_chb(i);
                     dma<16>(src, bk + (wave * SH::UK + i) * 1024);
                 }
                 if (lvt == 3) {
 #pragma unroll
                     for (int i = 0; i < SH::UV; ++i) {
                         const int P = (wave * SH::UV + i) * 1024 + lane * 16;
-                        const int key = min(t0 + 16 * (P / (D * 32)) + 8 * v_half[i], lastk & ~7);
+                        const int key = min(t0 + 16 * (P / (D * 32)) + 8 * v_half(i), lastk & ~7);
                         const int pid = tb[(key >> lb) - blk0];
-                        const size_t el = head_el(pid) + static_cast<size_t>(v_d[i]) * 8;
+                        const size_t el = head_el(pid) + static_cast<size_t>(v_d(i)) * 8;
                         dma<16>(vbase + el * E, bv + (wave * SH::UV + i) * 1024);
                     }
                 } else {
@@ -367,131 +386,183 @@ __global__ __launch_bounds__(kThreads) void pa_prefill_mfma(PrefillParams p) {
             }
         };
 
-        // ---- reduce one LDS tile
-        auto compute = [&](int kt, int buf) {
-            const unsigned char* bk = lds + buf * SH::BUF_BYTES;
-            const unsigned char* bv = bk + SH::K_BYTES;
+        // ---- one 32-key step g (keys 32g .. 32g + 31) in four parts. Step g
+        // lies in tile g / SPT, held by buffer (g / SPT) & 1.
+        constexpr int SPT = KT / 32;  // steps per tile
+        auto step_base = [&](int g) {
+            return lds + ((g / SPT) & 1) * SH::BUF_BYTES;
+        };
+        // K rows of the step's two S^T tiles
+        auto read_k = [&](int g, u32x4 (&kf)[2][NK]) {
+            const unsigned char* bk = step_base(g);
 #pragma unroll
-            for (int g32 = 0; g32 < KT / 32; ++g32) {
-                const int tok0 = kt * KT + 32 * g32;
-                if (tok0 > pw_max) break;  // uniform: past this wave's last position
-                // every operand read of the step first: K rows of both S^T
-                // tiles, then V^T rows d = 16v + r16 of keys tok0 + 8j .. + 7
-                // (16-key tile 2 g32 + j / 2, half j % 2)
-                u32x4 kf[2][NK];
+            for (int tt = 0; tt < 2; ++tt) {
+                const int r = 32 * (g % SPT) + 16 * tt + r16;
+                const unsigned char* krow = bk + r * ROWB;
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const int r = 32 * g32 + 16 * tt + r16;
-                    const unsigned char* krow = bk + r * ROWB;
+                for (int c = 0; c < NK; ++c)
+                    kf[tt][c] = *reinterpret_cast<const u32x4*>(krow + (((4 * c + j) ^ k_swz<D>(r)) << 4));
+            }
+        };
+        // V^T rows d = 16v + r16 of keys 32g + 8j .. + 7 (16-key tile
+        // 2 (g % SPT) + j / 2 of the buffer, half j % 2)
+        auto read_v = [&](int g, u32x4 (&vf)[NV]) {
+            const unsigned char* bv = step_base(g) + SH::K_BYTES;
+            const int vsub = 2 * (g % SPT) + (j >> 1);
+            const unsigned char* vrow = bv + (vsub * D + r16) * 32 + (((j & 1) ^ v_swz(r16)) << 4);
 #pragma unroll
-                    for (int c = 0; c < NK; ++c)
-                        kf[tt][c] = *reinterpret_cast<const u32x4*>(krow + (((4 * c + j) ^ k_swz<D>(r)) << 4));
-                }
-                u32x4 vf[NV];
-                {
-                    const int vsub = 2 * g32 + (j >> 1);
-                    const unsigned char* vrow = bv + (vsub * D + r16) * 32 + (((j & 1) ^ v_swz(r16)) << 4);
+            for (int v = 0; v < NV; ++v) vf[v] = *reinterpret_cast<const u32x4*>(vrow + 16 * v * 32);
+        };
+        // S^T = K Q^T: st[tt][n][r] is the unscaled logit of key 32g + 8j + 4tt + r
+        // and column r16 of block n
+        auto qk = [&](const u32x4 (&kf)[2][NK], f32x4_t (&st)[2][NC]) {
 #pragma unroll
-                    for (int v = 0; v < NV; ++v) vf[v] = *reinterpret_cast<const u32x4*>(vrow + 16 * v * 32);
-                }
-                f32x4_t st[2][NC];
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                    for (int n = 0; n < NC; ++n) {
-                        f32x4_t a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int c = 0; c < NK; ++c) a = mfma32<DT>(kf[tt][c], qf[n][c], a);
-                        st[tt][n] = a;
-                    }
-                // st[tt][n][r] is the unscaled logit of key tok0 + 8j + 4tt + r
-                // and column r16 of block n. Keys past a column's own position
-                // are masked; only the diagonal groups have any, and keys past
-                // the context are among them.
-                if (tok0 + 31 > pw_min) {
-#pragma unroll
-                    for (int n = 0; n < NC; ++n)
-#pragma unroll
-                        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (tok0 + 8 * j + 4 * tt + r > pcol[n]) st[tt][n][r] = -INFINITY;
-                }
-                float tmax[NC];
-                bool need_any = false;
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int n = 0; n < NC; ++n) {
-                    const f32x4_t a = st[0][n], b = st[1][n];
-                    float t = a[0] > a[1] ? a[0] : a[1];
-                    t = a[2] > t ? a[2] : t;
-                    t = a[3] > t ? a[3] : t;
-                    t = b[0] > t ? b[0] : t;
-                    t = b[1] > t ? b[1] : t;
-                    t = b[2] > t ? b[2] : t;
-                    t = b[3] > t ? b[3] : t;
-                    tmax[n] = column_max(t) * sc;
-                    need_any |= tmax[n] > m_run[n] + kLazy;
+                    f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < NK; ++c) a = mfma32<DT>(kf[tt][c], qf[n][c], a);
+                    st[tt][n] = a;
                 }
-                if (__any(need_any)) {
+        };
+        // keys past a column's own position are masked (only the diagonal
+        // steps have any; keys past the context are among them)
+        auto mask = [&](int g, f32x4_t (&st)[2][NC]) {
+            const int tok0 = 32 * g;
+            if (tok0 + 31 > pw_min) {
 #pragma unroll
-                    for (int n = 0; n < NC; ++n) {
-                        const float mn = tmax[n] > m_run[n] + kLazy ? tmax[n] : m_run[n];
-                        const float alpha = fast_exp2(m_run[n] - mn);
-#pragma unroll
-                        for (int v = 0; v < NV; ++v) acc[n][v] *= alpha;
-                        accl[n] *= alpha;
-                        m_run[n] = mn;
-                    }
-                }
-                u32x4 pb[NC];
-#pragma unroll
-                for (int n = 0; n < NC; ++n) {
-                    const float m = -m_run[n];
-                    float pr[8];
-                    float e[8];
+                for (int n = 0; n < NC; ++n)
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) e[4 * tt + r] = fast_exp2(fmaf(st[tt][n][r], sc, m));
-                    pb[n].x = pack2<DT>(e[0], e[1], pr[0], pr[1]);
-                    pb[n].y = pack2<DT>(e[2], e[3], pr[2], pr[3]);
-                    pb[n].z = pack2<DT>(e[4], e[5], pr[4], pr[5]);
-                    pb[n].w = pack2<DT>(e[6], e[7], pr[6], pr[7]);
-                }
-                // keys past the context may hold anything: zero their V
-                if (tok0 + 32 > L) {
-                    const int nv = L - (tok0 + 8 * j);
-                    const uint32_t lo = 0x0000ffffu, hi = 0xffff0000u;
-                    const u32x4 vm = {(nv > 0 ? lo : 0u) | (nv > 1 ? hi : 0u), (nv > 2 ? lo : 0u) | (nv > 3 ? hi : 0u),
-                                      (nv > 4 ? lo : 0u) | (nv > 5 ? hi : 0u), (nv > 6 ? lo : 0u) | (nv > 7 ? hi : 0u)};
-#pragma unroll
-                    for (int v = 0; v < NV; ++v) vf[v] &= vm;
-                }
-#pragma unroll
-                for (int n = 0; n < NC; ++n) accl[n] = mfma32<DT>(ones, pb[n], accl[n]);
-#pragma unroll
-                for (int v = 0; v < NV; ++v)
-#pragma unroll
-                    for (int n = 0; n < NC; ++n) acc[n][v] = mfma32<DT>(vf[v], pb[n], acc[n][v]);
+                        for (int r = 0; r < 4; ++r)
+                            if (tok0 + 8 * j + 4 * tt + r > pcol[n]) st[tt][n][r] = -INFINITY;
             }
         };
+        // probabilities of the step against the running max m_run as the PV
+        // operand (element type, rounded)
+        auto exps = [&](const f32x4_t (&st)[2][NC], u32x4 (&pb)[NC]) {
+#pragma unroll
+            for (int n = 0; n < NC; ++n) {
+                const float m = -m_run[n];
+                float pr[8];
+                float e[8];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) e[4 * tt + r] = fast_exp2(fmaf(st[tt][n][r], sc, m));
+                pb[n].x = pack2<DT>(e[0], e[1], pr[0], pr[1]);
+                pb[n].y = pack2<DT>(e[2], e[3], pr[2], pr[3]);
+                pb[n].z = pack2<DT>(e[4], e[5], pr[4], pr[5]);
+                pb[n].w = pack2<DT>(e[6], e[7], pr[6], pr[7]);
+            }
+        };
+        // online softmax: the probabilities are computed against the current
+        // running max first (valid whenever it does not grow by more than
+        // 2^8, which is the lazy-rescale rule) and only recomputed, after the
+        // accumulators are rescaled, in the rare step where it does
+        auto softmax = [&](const f32x4_t (&st)[2][NC], u32x4 (&pb)[NC], float (&tmax)[NC], bool& need_any) {
+            need_any = false;
+#pragma unroll
+            for (int n = 0; n < NC; ++n) {
+                const f32x4_t a = st[0][n], b = st[1][n];
+                const float t = max3(max3(a[0], a[1], a[2]), max3(a[3], b[0], b[1]), max3(b[2], b[3], -INFINITY));
+                tmax[n] = column_max(t) * sc;
+                need_any |= tmax[n] > m_run[n] + kLazy;
+            }
+            exps(st, pb);
+        };
+        auto rescale = [&](const f32x4_t (&st)[2][NC], u32x4 (&pb)[NC], const float (&tmax)[NC]) {
+#pragma unroll
+            for (int n = 0; n < NC; ++n) {
+                const float mn = tmax[n] > m_run[n] + kLazy ? tmax[n] : m_run[n];
+                const float alpha = fast_exp2(m_run[n] - mn);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) acc[n][v] *= alpha;
+                accl[n] *= alpha;
+                m_run[n] = mn;
+            }
+            exps(st, pb);
+        };
+        // O^T += V^T P^T and the denominator
+        auto pv = [&](int g, u32x4 (&vf)[NV], const u32x4 (&pb)[NC]) {
+            const int tok0 = 32 * g;
+            // keys past the context may hold anything: zero their V
+            if (tok0 + 32 > L) {
+                const int nv = L - (tok0 + 8 * j);
+                const uint32_t lo = 0x0000ffffu, hi = 0xffff0000u;
+                const u32x4 vm = {(nv > 0 ? lo : 0u) | (nv > 1 ? hi : 0u), (nv > 2 ? lo : 0u) | (nv > 3 ? hi : 0u),
+                                  (nv > 4 ? lo : 0u) | (nv > 5 ? hi : 0u), (nv > 6 ? lo : 0u) | (nv > 7 ? hi : 0u)};
+#pragma unroll
+                for (int v = 0; v < NV; ++v) vf[v] &= vm;
+            }
+#pragma unroll
+            for (int n = 0; n < NC; ++n) accl[n] = mfma32<DT>(ones, pb[n], accl[n]);
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int n = 0; n < NC; ++n) acc[n][v] = mfma32<DT>(vf[v], pb[n], acc[n][v]);
+        };
 
-        // ---- pipeline: the loads of tile kt+1 fly while tile kt is reduced;
-        // block ids run one tile further ahead through tbl[tile & 1]
+        // ---- pipeline. Tiles: the loads of tile t + 1 fly while tile t is
+        // reduced; block ids run one tile further ahead through tbl[tile & 1].
+        // Steps: the products S of step g + 1 are issued before the softmax
+        // of step g, so that the matrix pipe works on them while the vector
+        // ALU computes the exponentials; the operands of step g + 1 are read
+        // from LDS one step ahead.
+        const int nsteps = (nkeys + 31) / 32;
         if (tid < SH::TBL) tbl[tid] = clamp_pid(lookup(0));
         __syncthreads();
         issue(0, 0);
-        {
-            const int t1 = clamp_pid(lookup(min(1, nkt - 1)));
-            if (tid < SH::TBL) tbl[SH::TBL + tid] = t1;
-        }
+        // (a raw table entry: it is clamped only where it is stored, so that
+        // nothing waits for its load before the tile's own loads are issued)
+        int treg = lookup(min(1, nkt - 1));
+        if (tid < SH::TBL) tbl[SH::TBL + tid] = clamp_pid(treg);
         __syncthreads();
-        for (int kt = 0; kt < nkt; ++kt) {
-            if (kt + 1 < nkt) issue(kt + 1, (kt + 1) & 1);
-            const int tnext = lookup(min(kt + 2, nkt - 1));
-            compute(kt, kt & 1);
-            if (tid < SH::TBL) tbl[(kt & 1) * SH::TBL + tid] = clamp_pid(tnext);
-            __syncthreads();
+        if (1 < nkt) issue(1, 1);
+        treg = lookup(min(2, nkt - 1));
+
+        f32x4_t st_cur[2][NC], st_nxt[2][NC];
+        u32x4 vf[NV];
+        {
+            u32x4 kf[2][NK];
+            read_k(0, kf);
+            qk(kf, st_cur);
+            read_v(0, vf);
+        }
+        for (int g = 0; g < nsteps; ++g) {
+            const int g1 = g + 1;
+            if (g1 < nsteps && g1 % SPT == 0) {
+                // step g + 1 starts tile t1: wait for it, then reuse the
+                // buffer of tile t1 - 1 (its last operands are in registers)
+                // for tile t1 + 1
+                const int t1 = g1 / SPT;
+                if (tid < SH::TBL) tbl[((t1 + 1) & 1) * SH::TBL + tid] = clamp_pid(treg);
+                __syncthreads();
+                if (t1 + 1 < nkt) issue(t1 + 1, (t1 + 1) & 1);
+                treg = lookup(min(t1 + 2, nkt - 1));
+            }
+            // Every wave runs every step (a step past a wave's own positions
+            // is fully masked and adds nothing), so that the step below is
+            // one straight run in which the products of step g + 1 (the last
+            // step repeats its own) are in flight during the softmax of step g.
+            const int gn = g1 < nsteps ? g1 : g;
+            mask(g, st_cur);
+            u32x4 kf[2][NK];
+            read_k(gn, kf);
+            qk(kf, st_nxt);
+            u32x4 pb[NC];
+            float tmax[NC];
+            bool need_any;
+            softmax(st_cur, pb, tmax, need_any);
+            if (__any(need_any)) rescale(st_cur, pb, tmax);
+            pv(g, vf, pb);
+            read_v(gn, vf);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int n = 0; n < NC; ++n) st_cur[tt][n] = st_nxt[tt][n];
         }
     }
 
