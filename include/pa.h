@@ -183,13 +183,14 @@ pa_status_t pa_decode_merge(void* out, const void* q, const void* k_cache, const
  *     out[query_start[s] + i][h] = sum_{t <= p} exp(x_t - max x) v_t[kv] / sum_{t <= p} exp(x_t - max x),
  * kv = h / (num_heads / num_kv_heads). M = 1 is the decode of the same
  * sequence. A row whose position would be negative (M > L, an invalid input)
- * is written as zeros. Arithmetic is float32 on MFMA; the probabilities are
- * rounded to `dtype` before they weight V (the softmax denominator sums the
- * rounded values), and out is rounded to `dtype`.
+ * is written as zeros. Arithmetic is float32 on MFMA; for bfloat16 and
+ * float16 the probabilities are rounded to `dtype` before they weight V (the
+ * softmax denominator sums the rounded values), and out is rounded to
+ * `dtype`.
  *
  * Arguments: q and out hold num_tokens rows; query_start must be
  * non-decreasing from 0 to at most num_tokens (entries are clamped into
- * [0, num_tokens]). dtype bfloat16 or float16; head_dim 64, 128 or 256;
+ * [0, num_tokens]). dtype float32, bfloat16 or float16; head_dim 64, 128 or 256;
  * num_heads / num_kv_heads 1, 2, 4, 8 or 16; block_size a power of two from
  * 4 to 256; max_blocks_per_seq * block_size >= max_context_len.
  * max_query_len must be >= every M and max_context_len >= every L: a longer

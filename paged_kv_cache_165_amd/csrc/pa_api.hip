@@ -356,7 +356,7 @@ pa_status_t pa_prefill(void* out, const void* q, const void* k_cache, const void
     const int group = num_heads / num_kv_heads;
     if (!pa::prefill_supported(dtype, head_dim, group))
         return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for dtype=%d head_dim=%d group=%d "
-                    "(bfloat16 or float16; head_dim 64/128/256; group 1/2/4/8/16)",
+                    "(float32, bfloat16 or float16; head_dim 64/128/256; group 1/2/4/8/16)",
                     static_cast<int>(dtype), head_dim, group);
     if (!is_pow2(block_size) || block_size < 4 || block_size > 256)
         return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two in [4, 256]", block_size);

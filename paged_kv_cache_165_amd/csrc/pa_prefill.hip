@@ -587,6 +587,300 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
+// ---------------------------------------------------------------------------
+// float32 prefill
+// ---------------------------------------------------------------------------
+//
+// The same work decomposition, tile loads and online softmax as the 16-bit
+// kernel, on v_mfma_f32_16x16x4_f32. A lane reads 16-byte operand chunks (4
+// floats) and spends them on four products whose k index j stands for the
+// chunk's component: S^T = K Q^T over d = 16c + 4j + comp takes D/4 products
+// per 16x16 tile, and after the softmax the lane's four scores -- keys 4j+r,
+// r = 0..3, of column r16 -- are, one per product, the B operand of
+// O^T += V^T P^T over those keys, whose A operand component r is a plain
+// 16-byte read of the cache's V tile [D][16]. Probabilities stay in float32,
+// so the denominator is a plain sum. Steps are 16 keys; tiles 32 keys (16 at
+// head_dim 256).
+
+template <int D>
+struct PrefillShapeF32 {
+    static constexpr int NC = D >= 256 ? 1 : 2;    // 16-column blocks per wave
+    static constexpr int KT = D >= 256 ? 16 : 32;   // keys per LDS tile
+    static constexpr int ROWB = D * 4;              // bytes of one K row
+    static constexpr int K_BYTES = KT * ROWB;
+    static constexpr int V_BYTES = KT * ROWB;
+    static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
+    static constexpr int UK = K_BYTES / 1024 / kWaves;  // 16-byte loads per lane and tile
+    static constexpr int UV = V_BYTES / 1024 / kWaves;
+    static constexpr int TBL = 16;
+    static_assert(UK * kWaves * 1024 == K_BYTES && UV * kWaves * 1024 == V_BYTES, "whole loads");
+};
+
+template <int D>
+constexpr int prefill_query_tile_f32(int g) { return kWaves * 16 * PrefillShapeF32<D>::NC / g; }
+
+template <int D>
+constexpr size_t prefill_smem_f32() {
+    return 2 * static_cast<size_t>(PrefillShapeF32<D>::BUF_BYTES) + 2 * PrefillShapeF32<D>::TBL * sizeof(int);
+}
+
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void pa_prefill_f32(PrefillParams p) {
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
+    using SH = PrefillShapeF32<D>;
+    constexpr int NC = SH::NC, KT = SH::KT, ROWB = SH::ROWB;
+    constexpr int NQ = D / 16;          // 16-byte chunks of a row per lane (d = 16c + 4j + comp)
+    constexpr int NV = D / 16;          // 16-row blocks of O^T
+    constexpr int TPW = 16 * NC / G;
+    constexpr int QT = kWaves * TPW;
+    constexpr float kLazy = 8.f;
+    constexpr float kFloor = -1e30f;
+
+    extern __shared__ __align__(16) unsigned char lds[];
+    int* tbl = reinterpret_cast<int*>(lds + 2 * SH::BUF_BYTES);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, j = lane >> 4;
+
+    const int per_tile = p.num_seqs * p.num_kv_heads;
+    const int kq = blockIdx.x / per_tile;
+    const int rest = blockIdx.x - kq * per_tile;
+    const int s = rest / p.num_kv_heads;
+    const int kv = rest - s * p.num_kv_heads;
+
+    int L = p.context_lens[s];
+    L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
+    int q0 = p.query_start[s], q1 = p.query_start[s + 1];
+    q0 = q0 < 0 ? 0 : (q0 > p.num_tokens ? p.num_tokens : q0);
+    q1 = q1 < q0 ? q0 : (q1 > p.num_tokens ? p.num_tokens : q1);
+    const int M = min(q1 - q0, p.max_q);
+    const int e_lo = kq * QT;
+    if (e_lo >= M) return;
+    const int nrow = min(M - e_lo, QT);
+    const int pos0 = L - e_lo - nrow;
+    const int row0 = q1 - e_lo - nrow;
+    const int nkeys = max(0, L - e_lo);
+    const int nkt = (nkeys + KT - 1) / KT;
+    const int uw0 = wave * TPW;
+    const int uw1 = min(uw0 + TPW, nrow);
+    const int pw_min = pos0 + uw0;
+    const int pw_max = uw1 > uw0 ? pos0 + uw1 - 1 : -1;
+
+    const int hq = p.num_heads;
+    const uint32_t qsign = p.scale_log2 < 0.f ? 0x80000000u : 0u;
+    const float sc = fmaxf(fabsf(p.scale_log2), 1e-30f);
+    f32x4_t qf[NC][NQ];
+    int pcol[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const int c = 16 * n + r16;
+        const int u = min(uw0 + c / G, nrow - 1);
+        const int h = kv * G + c % G;
+        pcol[n] = pos0 + u;
+        const float* qrow = static_cast<const float*>(p.q) + (static_cast<size_t>(row0 + u) * hq + h) * D + 4 * j;
+#pragma unroll
+        for (int c2 = 0; c2 < NQ; ++c2)
+            qf[n][c2] = __builtin_bit_cast(f32x4_t, *reinterpret_cast<const u32x4*>(qrow + 16 * c2) ^ qsign);
+    }
+    f32x4_t acc[NC][NV];
+    float m_run[NC], lsum[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        m_run[n] = kFloor;
+        lsum[n] = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[n][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    if (nkt > 0) {
+        const int lb = p.log2_bs;
+        const int bs = 1 << lb;
+        const int lvt = p.log2_vt;
+        const int vt = 1 << lvt;
+        const int hkv = p.num_kv_heads;
+        const size_t blk_el = static_cast<size_t>(bs) * D;
+        const char* kbase = static_cast<const char*>(p.k_cache);
+        const char* vbase = static_cast<const char*>(p.v_cache);
+        const int* trow = p.block_tables + static_cast<size_t>(s) * p.max_blocks;
+        const int lastk = L - 1;
+        const int last_blk = lastk >> lb;
+        const int ntb = KT >= bs ? KT >> lb : 1;
+        auto clamp_pid = [&](int pid) { return pid < 0 ? 0 : (pid >= p.num_blocks ? p.num_blocks - 1 : pid); };
+        auto lookup = [&](int kt) {
+            const int e = min(((kt * KT) >> lb) + tid, last_blk);
+            return trow[tid < ntb ? e : 0];
+        };
+        auto head_el = [&](int pid) { return (static_cast<size_t>(pid) * hkv + kv) * blk_el; };
+
+        // LDS: K rows in key order, 16-byte chunk ch of row r at ch ^ (r & 15);
+        // V as the cache's 16-key tiles [D][16], chunk c4 (keys 4 c4 .. + 3)
+        // of row d at c4 ^ ((d >> 2) & 3). Keys past the context are read at
+        // the last key (masked).
+        auto issue = [&](int kt, int buf) {
+            unsigned char* bk = lds + buf * SH::BUF_BYTES;
+            unsigned char* bv = bk + SH::K_BYTES;
+            const int* tb = tbl + (kt & 1) * SH::TBL;
+            const int t0 = kt * KT;
+            const int blk0 = t0 >> lb;
+#pragma unroll
+            for (int i = 0; i < SH::UK; ++i) {
+                const int P = (wave * SH::UK + i) * 1024 + lane * 16;
+                const int r = P / ROWB;
+                const int ch = ((P % ROWB) >> 4) ^ (r & 15);
+                const int key = min(t0 + r, lastk);
+                const int pid = tb[(key >> lb) - blk0];
+                const char* src = kbase + (head_el(pid) + static_cast<size_t>(key & (bs - 1)) * D) * 4 + ch * 16;
+                dma<16>(src, bk + (wave * SH::UK + i) * 1024);
+            }
+#pragma unroll
+            for (int i = 0; i < SH::UV; ++i) {
+                const int P = (wave * SH::UV + i) * 1024 + lane * 16;
+                const int sub = P / (D * 64);
+                const int d = (P % (D * 64)) >> 6;
+                const int c4 = ((P >> 4) & 3) ^ ((d >> 2) & 3);
+                const int key = min(t0 + 16 * sub + 4 * c4, lastk & ~3);
+                const int pid = tb[(key >> lb) - blk0];
+                const int off = key & (bs - 1);
+                const size_t el = head_el(pid) + static_cast<size_t>(off >> lvt) * D * vt + static_cast<size_t>(d) * vt +
+                                  (off & (vt - 1));
+                dma<16>(vbase + el * 4, bv + (wave * SH::UV + i) * 1024);
+            }
+        };
+
+        auto compute = [&](int kt, int buf) {
+            const unsigned char* bk = lds + buf * SH::BUF_BYTES;
+            const unsigned char* bv = bk + SH::K_BYTES;
+#pragma unroll
+            for (int st16 = 0; st16 < KT / 16; ++st16) {
+                const int tok0 = kt * KT + 16 * st16;
+                if (tok0 > pw_max) break;  // uniform
+                const int r = 16 * st16 + r16;
+                const unsigned char* krow = bk + r * ROWB;
+                f32x4_t st[NC];
+#pragma unroll
+                for (int n = 0; n < NC; ++n) st[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) {
+                    const f32x4_t kf = *reinterpret_cast<const f32x4_t*>(krow + (((4 * c + j) ^ (r & 15)) << 4));
+#pragma unroll
+                    for (int n = 0; n < NC; ++n)
+#pragma unroll
+                        for (int comp = 0; comp < 4; ++comp) st[n] = mfma_f32(kf[comp], qf[n][c][comp], st[n]);
+                }
+                // st[n][rr] is the unscaled logit of key tok0 + 4j + rr, column r16
+                if (tok0 + 15 > pw_min) {
+#pragma unroll
+                    for (int n = 0; n < NC; ++n)
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            if (tok0 + 4 * j + rr > pcol[n]) st[n][rr] = -INFINITY;
+                }
+                float tmax[NC];
+                bool need_any = false;
+#pragma unroll
+                for (int n = 0; n < NC; ++n) {
+                    tmax[n] = column_max(max3(max3(st[n][0], st[n][1], st[n][2]), st[n][3], -INFINITY)) * sc;
+                    need_any |= tmax[n] > m_run[n] + kLazy;
+                }
+                if (__any(need_any)) {
+#pragma unroll
+                    for (int n = 0; n < NC; ++n) {
+                        const float mn = tmax[n] > m_run[n] + kLazy ? tmax[n] : m_run[n];
+                        const float alpha = fast_exp2(m_run[n] - mn);
+#pragma unroll
+                        for (int v = 0; v < NV; ++v) acc[n][v] *= alpha;
+                        lsum[n] *= alpha;
+                        m_run[n] = mn;
+                    }
+                }
+                f32x4_t pr[NC];
+#pragma unroll
+                for (int n = 0; n < NC; ++n) {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) pr[n][rr] = fast_exp2(fmaf(st[n][rr], sc, -m_run[n]));
+                    lsum[n] += (pr[n][0] + pr[n][1]) + (pr[n][2] + pr[n][3]);
+                }
+                // V^T rows d = 16v + r16, keys tok0 + 4j .. + 3 (chunk j of row d
+                // of 16-key tile st16); keys past the context are zeroed
+                const unsigned char* vrow = bv + (st16 * D + r16) * 64 + ((j ^ ((r16 >> 2) & 3)) << 4);
+                const int nv = L - (tok0 + 4 * j);
+                const bool vmask = tok0 + 16 > L;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    f32x4_t vf = *reinterpret_cast<const f32x4_t*>(vrow + 16 * v * 64);
+                    if (vmask) {
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) vf[rr] = nv > rr ? vf[rr] : 0.f;
+                    }
+#pragma unroll
+                    for (int n = 0; n < NC; ++n)
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) acc[n][v] = mfma_f32(vf[rr], pr[n][rr], acc[n][v]);
+                }
+            }
+        };
+
+        if (tid < SH::TBL) tbl[tid] = clamp_pid(lookup(0));
+        __syncthreads();
+        issue(0, 0);
+        {
+            const int t1 = lookup(min(1, nkt - 1));
+            if (tid < SH::TBL) tbl[SH::TBL + tid] = clamp_pid(t1);
+        }
+        __syncthreads();
+        for (int kt = 0; kt < nkt; ++kt) {
+            if (kt + 1 < nkt) issue(kt + 1, (kt + 1) & 1);
+            const int tnext = lookup(min(kt + 2, nkt - 1));
+            compute(kt, kt & 1);
+            if (tid < SH::TBL) tbl[(kt & 1) * SH::TBL + tid] = clamp_pid(tnext);
+            __syncthreads();
+        }
+    }
+
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const float l = column_sum(lsum[n]);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const int c = 16 * n + r16;
+        const int u = uw0 + c / G;
+        if (u < nrow) {
+            const int h = kv * G + c % G;
+            float* orow = static_cast<float*>(p.out) + (static_cast<size_t>(row0 + u) * hq + h) * D + 4 * j;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) *reinterpret_cast<f32x4_t*>(orow + 16 * v) = acc[n][v] * inv;
+        }
+    }
+}
+
+template <int D, int G>
+hipError_t launch_prefill_f32_g(const PrefillParams& p, hipStream_t stream) {
+    constexpr int QT = prefill_query_tile_f32<D>(G);
+    const long long qtiles = (static_cast<long long>(p.max_q) + QT - 1) / QT;
+    const long long grid = qtiles * p.num_seqs * p.num_kv_heads;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((pa_prefill_f32<D, G>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                       prefill_smem_f32<D>(), stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefill_f32_d(const PrefillParams& p, int group, hipStream_t stream) {
+    switch (group) {
+        case 1: return launch_prefill_f32_g<D, 1>(p, stream);
+        case 2: return launch_prefill_f32_g<D, 2>(p, stream);
+        case 4: return launch_prefill_f32_g<D, 4>(p, stream);
+        case 8: return launch_prefill_f32_g<D, 8>(p, stream);
+        case 16: return launch_prefill_f32_g<D, 16>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int DT, int D, int G>
 hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t stream) {
     constexpr int QT = prefill_query_tile<D>(G);
@@ -624,7 +918,7 @@ hipError_t launch_prefill_dt(const PrefillParams& p, int head_dim, int group, hi
 }  // namespace
 
 bool prefill_supported(pa_dtype_t dt, int head_dim, int group) {
-    if (dt != PA_BF16 && dt != PA_F16) return false;
+    if (dt != PA_BF16 && dt != PA_F16 && dt != PA_F32) return false;
     if (!(head_dim == 64 || head_dim == 128 || head_dim == 256)) return false;
     return group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
 }
@@ -633,6 +927,13 @@ hipError_t launch_prefill(const PrefillParams& p, pa_dtype_t dt, int head_dim, i
     switch (dt) {
         case PA_BF16: return launch_prefill_dt<PA_BF16>(p, head_dim, group, stream);
         case PA_F16: return launch_prefill_dt<PA_F16>(p, head_dim, group, stream);
+        case PA_F32:
+            switch (head_dim) {
+                case 64: return launch_prefill_f32_d<64>(p, group, stream);
+                case 128: return launch_prefill_f32_d<128>(p, group, stream);
+                case 256: return launch_prefill_f32_d<256>(p, group, stream);
+            }
+            break;
         default: break;
     }
     return hipErrorInvalidValue;

@@ -107,7 +107,7 @@ def _prefill(lib, **over):
 @pytest.mark.parametrize("over,status,msg", [
     (dict(Hq=7), 1, b"multiple of num_kv_heads"),
     (dict(Hq=64, Hkv=2), 2, b"no prefill kernel"),   # group 32
-    (dict(dtype=0), 2, b"no prefill kernel"),        # float32
+    (dict(dtype=0, Hq=64, Hkv=2), 2, b"no prefill kernel"),  # float32 group 32
     (dict(D=96), 2, b"no prefill kernel"),
     (dict(bs=12), 2, b"power of two"),
     (dict(bs=512), 2, b"power of two"),

@@ -4,7 +4,7 @@ float64 oracle (``oracle.paged_prefill``) on seeded inputs.
 Small cases compare every output element; they span several query tiles and
 key tiles with ragged tails, one-token chunks (decode), whole prompts and
 chunks after a cached history, empty sequences, every supported block size,
-head_dim and group size, and both 16-bit types. Unwritten slots and the
+head_dim and group size, and all three element types. Unwritten slots and the
 blocks the padding table entries point at hold NaN, so any read past what a
 row may see shows up. The two full-size workloads the prefill bench times are
 checked on sampled rows, each against the oracle's decode of the row's query
@@ -75,6 +75,10 @@ CASES = [
     ("f16", 128, 4, 16),
     ("f16", 64, 1, 4),
     ("f16", 256, 8, 32),
+    ("f32", 128, 4, 16),
+    ("f32", 64, 1, 4),
+    ("f32", 128, 16, 8),
+    ("f32", 256, 2, 64),
 ]
 
 

@@ -29,6 +29,7 @@ import numpy as np
 
 BF16 = "bf16"
 F16 = "f16"
+F32 = "f32"
 
 
 @dataclass
@@ -143,7 +144,7 @@ def make_values(w: PrefillWorkload, device="cpu", poison=True):
     slot that holds no token set to NaN when ``poison``."""
     import torch
 
-    tdt = {BF16: torch.bfloat16, F16: torch.float16}[w.dtype]
+    tdt = {BF16: torch.bfloat16, F16: torch.float16, F32: torch.float32}[w.dtype]
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed)
