@@ -227,11 +227,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int nkeys = max(0, L - e_lo);
     const int nkt = (nkeys + KT - 1) / KT;
 
-    // this wave's tokens [uw0, uw1) of the tile; positions pw_min..pw_max
+    // this wave's first token of the tile and its position
     const int uw0 = wave * TPW;
-    const int uw1 = min(uw0 + TPW, nrow);
     const int pw_min = pos0 + uw0;
-    const int pw_max = uw1 > uw0 ? pos0 + uw1 - 1 : -1;
 
     // ---- query fragments and positions of this lane's columns. A negative
     // scale is folded into q (a sign flip is exact), so that the running
