@@ -12,11 +12,11 @@
 // contiguous run of V bytes, and the MFMA operand of P.V is a plain load.
 //
 // Work decomposition. An item is (sequence, KV head, partition of `part`
-// tokens). A persistent grid of 256-thread workgroups walks the item list;
-// every workgroup first builds, in LDS, the prefix sum of partition counts
-// over the batch so that an item index maps to its sequence by binary search.
-// The four waves of a workgroup share one item and take its steps round
-// robin. The slice of the block table the partition reads is staged in LDS
+// tokens). A persistent grid of 256-thread workgroups walks the items largest
+// first; every workgroup first builds that order in LDS (a prefix sum of full
+// partitions, searched by bisection, then the partial partitions sorted by
+// size: see "Work order and assignment" below). The four waves of a
+// workgroup share one item and take its steps round robin. The slice of the block table the partition reads is staged in LDS
 // (cf-1.com blog, 2.2 and 5.4: table lookups served from shared memory, not
 // global memory). K/V are streamed with nontemporal 16-byte loads, the next
 // step always in flight while the current one is reduced (cf-1.com 5.1 and
