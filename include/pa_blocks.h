@@ -40,8 +40,9 @@ typedef struct pa_block_manager pa_block_manager_t;
  * A manager of num_blocks blocks of block_size tokens. free_order (nullable)
  * lists every block id once, in the order the free list hands them out;
  * NULL means 0, 1, 2, ... Blocks freed later go to the back of the list.
- * PA_ERR_INVALID_ARG for sizes <= 0 or a free_order that is not a
- * permutation of [0, num_blocks).
+ * PA_ERR_INVALID_ARG for sizes <= 0, for num_blocks * block_size above
+ * INT32_MAX (slots are int32), or a free_order that is not a permutation of
+ * [0, num_blocks).
  */
 pa_status_t pa_bm_create(int num_blocks, int block_size, const int32_t* free_order,
                          pa_block_manager_t** out);

@@ -58,6 +58,9 @@ pa_status_t pa_bm_create(int num_blocks, int block_size, const int32_t* free_ord
     *out = nullptr;
     if (num_blocks <= 0 || block_size <= 0)
         return fail(PA_ERR_INVALID_ARG, "invalid size (num_blocks=%d block_size=%d)", num_blocks, block_size);
+    if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
+        return fail(PA_ERR_INVALID_ARG, "num_blocks * block_size = %lld slots do not fit the int32 slot mapping",
+                    static_cast<long long>(num_blocks) * block_size);
     pa_block_manager* bm = new (std::nothrow) pa_block_manager;
     if (!bm) return fail(PA_ERR_INVALID_ARG, "out of host memory");
     bm->num_blocks = num_blocks;

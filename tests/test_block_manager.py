@@ -167,6 +167,8 @@ def test_errors():
         BlockManager(0, 16)
     with pytest.raises(ValueError):
         BlockManager(4, 16, free_order=[0, 1, 1, 3])
+    with pytest.raises(ValueError, match="int32"):
+        BlockManager(1 << 27, 32)  # 2^32 slots: past the int32 slot mapping
     bm = BlockManager(8, 4)
     bm.prefill(7, 3)
     with pytest.raises(ValueError, match="exists"):
