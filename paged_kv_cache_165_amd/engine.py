@@ -63,17 +63,31 @@ class PagedDecoder:
         return self._workspace
 
     # -- sequence operations ---------------------------------------------
-    def prefill(self, seq: int, k: torch.Tensor, v: torch.Tensor) -> np.ndarray:
-        """A new sequence whose prompt K/V rows are ``k``, ``v`` [T, Hkv, D];
-        returns the slot of every prompt token."""
+    def prefill(self, seq: int, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor = None, scale: float = None,
+                out: torch.Tensor = None):
+        """A new sequence whose prompt K/V rows are ``k``, ``v`` [T, Hkv, D].
+        Writes them into fresh blocks and returns the slot of every prompt
+        token; given the prompt's queries ``q`` [T, Hq, D] and ``scale`` it
+        also runs causal prefill attention over the prompt (``pa_prefill``)
+        and returns (slots, out)."""
         n = int(k.shape[0])
         self.blocks.prefill(seq, n)
-        table, _ = self.blocks.block_tables([seq], max(-(-n // self.block_size), 1), pad=0)
+        table, lens = self.blocks.block_tables([seq], max(-(-n // self.block_size), 1), pad=0)
         pos = np.arange(n)
         slots = (table[0][pos // self.block_size] * self.block_size + pos % self.block_size).astype(np.int32)
         if n:
             self._pa.write_cache(k, v, self.k_cache, self.v_cache, self._dev(slots))
-        return slots
+        if q is None:
+            return slots
+        if scale is None:
+            raise ValueError("prefill attention needs a scale")
+        if out is None:
+            out = torch.empty_like(q)
+        if n:
+            self._pa.prefill(out, q, self.k_cache, self.v_cache, self._dev(table), self._dev(lens),
+                             self._dev(np.array([0, n], dtype=np.int32)), scale, max_query_len=n,
+                             max_context_len=n)
+        return slots, out
 
     def fork(self, child: int, parent: int, num_tokens: int = None) -> None:
         """``child`` shares the first ``num_tokens`` tokens (default: all) of

@@ -86,3 +86,44 @@ def test_multi_step_decode_matches_oracle(dtype, bs, hq, hkv, d, part):
     # (37 tokens), 3 (20 tokens of 0) and 4/5 (5 tokens)
     assert copies == sum(n % bs != 0 for n in (37, 20, 5))
     assert raw_equal(eng.k_cache, kc_h) and raw_equal(eng.v_cache, vc_h)
+
+
+def test_prompt_attention_then_decode_steps_match_oracle():
+    """The whole path through the engine: prompts written and attended
+    causally (pa_prefill), a fork sharing a partly filled block, then decode
+    steps with copy-on-write; every output against the oracle."""
+    from paged_kv_cache_165_amd.engine import PagedDecoder
+    dtype, bs, hq, hkv, d = torch.bfloat16, 16, 16, 4, 128
+    g = torch.Generator(device=DEV).manual_seed(77)
+    rng = np.random.default_rng(77)
+    nb = 64
+    eng = PagedDecoder(nb, bs, hq, hkv, d, max_blocks_per_seq=24, dtype=dtype, free_order=rng.permutation(nb))
+    eng.k_cache.copy_(_rand(g, eng.k_cache.shape, dtype))
+    eng.v_cache.copy_(_rand(g, eng.v_cache.shape, dtype))
+    kc_h, vc_h = host_bits(eng.k_cache), host_bits(eng.v_cache)
+    scale = 1.0 / np.sqrt(d)
+    for seq, n in ((0, 45), (1, 130)):
+        q = _rand(g, (n, hq, d), dtype)
+        k, v = _rand(g, (n, hkv, d), dtype), _rand(g, (n, hkv, d), dtype)
+        slots, out = eng.prefill(seq, k, v, q=q, scale=scale)
+        torch.cuda.synchronize()
+        kc_h, vc_h = oracle.write_cache(host_bits(k), host_bits(v), kc_h, vc_h, slots, bs)
+        tables, lens = eng.tables([seq])
+        ref = oracle.paged_prefill(host_bits(q), kc_h, vc_h, tables, lens, [0, n], scale, bs, oracle.BF16)
+        stats = compare_attention(out, ref, f"prompt {seq}")
+        log(f"[engine] prompt {seq} ({n} tokens): {stats}")
+    eng.fork(2, 0)
+    batch = [0, 1, 2]
+    for step in range(6):
+        q = _rand(g, (3, hq, d), dtype)
+        k, v = _rand(g, (3, hkv, d), dtype), _rand(g, (3, hkv, d), dtype)
+        out, slots, pairs = eng.step(batch, q, k, v, scale)
+        torch.cuda.synchronize()
+        if len(pairs):
+            kc_h, vc_h = oracle.copy_blocks(kc_h, vc_h, pairs)
+        kc_h, vc_h = oracle.write_cache(host_bits(k), host_bits(v), kc_h, vc_h, slots, bs)
+        tables, lens = eng.tables(batch)
+        ref = oracle.paged_decode(host_bits(q), kc_h, vc_h, tables, lens, scale, bs, oracle.BF16)
+        compare_attention(out, ref, f"decode step {step}")
+    eng.blocks.check()
+    assert raw_equal(eng.k_cache, kc_h) and raw_equal(eng.v_cache, vc_h)

@@ -144,6 +144,24 @@ def test_all_sequences_empty_is_noop():
     assert torch.all(out == 7.0)
 
 
+def test_long_context_chunk_sampled_rows():
+    """A 256-token chunk after a 32k-token history (hundreds of key tiles,
+    a table slice per tile) and a short sequence beside it: sampled rows
+    against the oracle's decode over each row's first p + 1 tokens."""
+    w = P.make("long-chunk", [32768 + 256, 300], [256, 300], num_heads=16, num_kv_heads=2, head_dim=128,
+               block_size=32, seed=11)
+    v = P.make_values(w, device=DEV)
+    out = _run(w, v)
+    assert torch.isfinite(out.float()).all(), "non-finite output"
+    rows = np.array([0, 1, 63, 64, 127, 200, 255, 256, 300, 555])
+    pos = w.positions()
+    seq_of = np.repeat(np.arange(w.num_seqs), w.query_lens)
+    ref = oracle.paged_decode(host_bits(v["q"])[rows], host_bits(v["k_cache"]), host_bits(v["v_cache"]),
+                              w.block_tables[seq_of[rows]], pos[rows] + 1, w.scale, w.block_size, oracle.BF16)
+    stats = compare_attention(out[torch.from_numpy(rows).to(DEV)], ref, "long-chunk")
+    log(f"[prefill] long-chunk: {stats}")
+
+
 @pytest.mark.parametrize("name", ["chunked", "prompts"])
 def test_full_size_workload_sampled_rows(name):
     w = P.BUILDERS[name]()
