@@ -89,9 +89,22 @@ def _counter_rows(path, counter):
     return list(per.values())
 
 
-def summarize_counters(fetch_csv, write_csv, out_json, workload, calib_mb):
+def resolved_partition(w) -> int:
+    """Tokens per partition the decode of workload ``w`` runs with."""
+    import paged_kv_cache_165_amd as pa
+    return w.partition_size or pa.default_partition_size(w.num_seqs, w.num_kv_heads, w.max_context_len,
+                                                         w.block_size)
+
+
+def summarize_counters(fetch_csv, write_csv, out_json, workload, calib_mb, partition_size=0):
     """Scale per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the partition
-    kernel by what the same counters read for a copy of known size."""
+    kernel by what the same counters read for a copy of known size. The
+    record keeps the kernel source hash and the partition size the counters
+    were taken with; the bench reports them only while both still hold."""
+    import workloads as W
+    w = W.build(workload)
+    if partition_size:
+        w.partition_size = partition_size
     calib_bytes = calib_mb * (1 << 20)
     res = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -114,7 +127,7 @@ def summarize_counters(fetch_csv, write_csv, out_json, workload, calib_mb):
         "write_bytes": round(res["WRITE_SIZE"]["partition_bytes"]),
         "fetch_scale": res["FETCH_SIZE"]["scale"], "write_scale": res["WRITE_SIZE"]["scale"],
         "calibration_mb": calib_mb, "kernel_source_sha256_16": kernel_source_hash(),
-        "counters": res,
+        "partition_size": resolved_partition(w), "counters": res,
     }
     with open(out_json, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
@@ -394,7 +407,7 @@ def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.traffic_json,
-                           args.workload, args.copy_calibration_mb)
+                           args.workload, args.copy_calibration_mb, args.partition_size or 0)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this library has no multi-GPU path "
@@ -436,8 +449,8 @@ def main():
     pairs = torch.from_numpy(w.cow_pairs.astype(np.int32)).to(dev)
     slots = [torch.from_numpy(op.slots.astype(np.int32)).to(dev) for op in w.writes]
     out = torch.empty_like(q)
-    ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.head_dim, w.max_context_len, w.partition_size,
-                            device=dev)
+    ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_context_len,
+                            w.block_size, w.partition_size, device=dev)
     dargs = (out, q, kc, vc, tables, lens, w.scale, w.max_context_len, w.partition_size, ws)
 
     def step():
@@ -492,7 +505,8 @@ def main():
         try:
             with open(args.traffic_json) as f:
                 tj = json.load(f).get(w.name)
-            if tj and tj.get("kernel_source_sha256_16") == kernel_source_hash():
+            if (tj and tj.get("kernel_source_sha256_16") == kernel_source_hash()
+                    and tj.get("partition_size") == resolved_partition(w)):
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None
@@ -522,7 +536,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
-                   "partition_size": w.partition_size or pa.default_partition_size(), "ctx": w.ctx_recipe, "tokens": int(w.context_lens.sum()), "tail_waste": round(W.tail_waste(w), 5),
+                   "partition_size": resolved_partition(w), "ctx": w.ctx_recipe, "tokens": int(w.context_lens.sum()), "tail_waste": round(W.tail_waste(w), 5),
                    "kv_bytes": kv, "seed": w.seed, "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),

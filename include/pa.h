@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 typedef enum pa_dtype {
     PA_F32 = 0,  /* IEEE binary32 */
@@ -85,20 +85,30 @@ const char* pa_status_string(pa_status_t status);
 const char* pa_last_error(void);
 
 /*
- * Tokens per context partition when the caller passes partition_size = 0.
+ * Tokens per context partition that pa_decode uses when the caller passes
+ * partition_size = 0, a function of the batch's shape only (host code, no
+ * device query): 256 blocks (256 * block_size tokens; an item can stage
+ * up to 512 blocks, but longer default items unbalance skewed batches),
+ * halved while the batch would yield fewer than
+ * 512 items (num_seqs * num_kv_heads * ceil(max_context_len / size), two
+ * per compute unit of MI355X), but not below 512 tokens. Long partitions
+ * cost the fewest item switches and merges; the item count keeps every
+ * compute unit fed. Returns 0 for invalid arguments (sizes below zero,
+ * num_kv_heads or block_size not positive).
  */
-int pa_default_partition_size(void);
+int pa_default_partition_size(int num_seqs, int num_kv_heads, int max_context_len, int block_size);
 
 /*
  * Bytes of device workspace pa_decode needs: one (max, sum, output row)
  * record in float32 per sequence, query head and partition, or 0 when no
  * sequence can span more than one partition (max_context_len <=
  * partition_size). Returns 0 for invalid arguments too. partition_size = 0
- * selects the default. The workspace is caller-owned device memory with no
- * required contents; calls that share one must not overlap.
+ * selects pa_default_partition_size(num_seqs, num_kv_heads,
+ * max_context_len, block_size). The workspace is caller-owned device memory
+ * with no required contents; calls that share one must not overlap.
  */
-size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
-                                int max_context_len, int partition_size);
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                int max_context_len, int block_size, int partition_size);
 
 /*
  * Paged decode attention.
@@ -125,8 +135,8 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
  * query head per KV head or float32 elements the block must also hold at
  * least max(1024 / (head_dim * sizeof(dtype)), 4, 16 * head_dim * sizeof(dtype) / 1024)
  * tokens (PA_ERR_UNSUPPORTED names the bound);
- * partition_size (0 = default) a multiple of 16 and of block_size with
- * partition_size / block_size <= 256; num_seqs <= 8192;
+ * partition_size (0 = pa_default_partition_size) a multiple of 16 and of block_size with
+ * partition_size / block_size <= 512; num_seqs <= 8192;
  * max_blocks_per_seq * block_size >= max_context_len. workspace must hold
  * pa_decode_workspace_size(...) bytes for the same arguments.
  * max_context_len must be >= every context_lens[s]; a longer sequence is

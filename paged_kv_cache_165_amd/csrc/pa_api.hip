@@ -15,9 +15,19 @@
 
 namespace {
 
-constexpr int kDefaultPartition = 1024;
+// Shape of the default split: the longest default partition in blocks,
+// items wanted per launch (two per compute unit of MI355X) and the shortest
+// partition worth its item switch and merge. The default stops at 256 blocks
+// although an item can stage 512: on a skewed batch (lognormal lengths up to
+// 8192) the largest items then take most of a launch and the static deal
+// cannot even them out (measured on MI355X: 285 us against 255 us at 256
+// blocks for 256 sequences of 8 KV heads, and 562 against 465 us for 8
+// sequences of 32k-131k tokens).
+constexpr int kAutoMaxBlocks = 256;
+constexpr int kTargetItems = 512;
+constexpr int kMinAutoPartition = 512;
 constexpr int kMaxSeqs = 8192;
-constexpr int kMaxTableSlice = 256;
+using pa::kMaxTableSlice;
 
 thread_local std::string g_last_error;
 
@@ -85,8 +95,25 @@ pa_status_t num_cus(int* out) {
     return PA_OK;
 }
 
-int resolve_partition(int partition_size) {
-    return partition_size == 0 ? kDefaultPartition : partition_size;
+// The default split (pa_default_partition_size): start from the longest
+// partition one item can stage and halve it while the batch has too few
+// items to fill the chip. Block sizes are powers of two, so every halving
+// down to 512 stays a multiple of 16 and of block_size.
+int auto_partition(int num_seqs, int num_kv_heads, int max_context_len, int block_size) {
+    int part = kAutoMaxBlocks * block_size;
+    while (part > kMinAutoPartition) {
+        const long long items = static_cast<long long>(num_seqs) * num_kv_heads *
+                                ((static_cast<long long>(max_context_len) + part - 1) / part);
+        if (items >= kTargetItems) break;
+        part /= 2;
+    }
+    return part;
+}
+
+int resolve_partition(int partition_size, int num_seqs, int num_kv_heads, int max_context_len,
+                      int block_size) {
+    return partition_size == 0 ? auto_partition(num_seqs, num_kv_heads, max_context_len, block_size)
+                               : partition_size;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -141,7 +168,7 @@ pa_status_t prepare_decode(void* out, const void* q, const void* k_cache, const 
     if (block_size < min_bs)
         return fail(PA_ERR_UNSUPPORTED, "block_size %d < %d, the smallest block this dtype/head_dim/group supports",
                     block_size, min_bs);
-    const int part = resolve_partition(partition_size);
+    const int part = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len, block_size);
     if (part % 16 != 0 || part % block_size != 0 || part / block_size > kMaxTableSlice)
         return fail(PA_ERR_INVALID_ARG, "partition_size %d must be a multiple of 16 and of block_size %d "
                     "spanning at most %d blocks", part, block_size, kMaxTableSlice);
@@ -263,13 +290,17 @@ const char* pa_status_string(pa_status_t status) {
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
-int pa_default_partition_size(void) { return kDefaultPartition; }
+int pa_default_partition_size(int num_seqs, int num_kv_heads, int max_context_len, int block_size) {
+    if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 || block_size <= 0) return 0;
+    return auto_partition(num_seqs, num_kv_heads, max_context_len, block_size);
+}
 
-size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int max_context_len,
-                                int partition_size) {
-    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_size < 0)
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                int max_context_len, int block_size, int partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+        block_size <= 0 || partition_size < 0)
         return 0;
-    const int part = resolve_partition(partition_size);
+    const int part = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len, block_size);
     return ws_layout(num_seqs, num_heads, head_dim, pmax_of(max_context_len, part)).total;
 }
 

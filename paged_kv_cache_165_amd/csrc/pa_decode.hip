@@ -45,7 +45,8 @@ namespace pa {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kMaxTableSlice = 256;  // table entries one partition may span
+constexpr int kTblPerThread = kMaxTableSlice / kThreads;  // table entries each thread stages
+static_assert(kTblPerThread * kThreads == kMaxTableSlice, "whole table entries per thread");
 
 // Workgroups per compute unit of the persistent grid; 0 = as many as the
 // kernel's occupancy allows.
@@ -244,10 +245,10 @@ __device__ __forceinline__ int snake_item(const Sched& sc, int r) {
 }
 
 __device__ __forceinline__ void stage_table(const DecodeParams& p, const Item& it, int* tbl) {
-    if (static_cast<int>(threadIdx.x) < it.nblk) {
-        int pid = p.block_tables[static_cast<size_t>(it.s) * p.max_blocks + it.b0 + threadIdx.x];
+    for (int i = threadIdx.x; i < it.nblk; i += kThreads) {
+        int pid = p.block_tables[static_cast<size_t>(it.s) * p.max_blocks + it.b0 + i];
         pid = pid < 0 ? 0 : (pid >= p.num_blocks ? p.num_blocks - 1 : pid);
-        tbl[threadIdx.x] = pid;
+        tbl[i] = pid;
     }
 }
 
@@ -758,7 +759,10 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
                 pv_raw = *(next_tile ? trow + ((min(tt0 + 4 * j, last4_of(nxt)) >> p.log2_bs) - nxt.b0) : safe);
             }
         }
-        const int tbl_raw = *(has_next && tid < nxt.nblk ? trow + tid : safe);
+        int tbl_raw[kTblPerThread];
+#pragma unroll
+        for (int i = 0; i < kTblPerThread; ++i)
+            tbl_raw[i] = *(has_next && tid + i * kThreads < nxt.nblk ? trow + tid + i * kThreads : safe);
         uint32_t q_raw[QPT];
 #pragma unroll
         for (int i = 0; i < QPT; ++i) q_raw[i] = qwords[q_word0(nxt) + min(tid + i * kThreads, QW - 1)];
@@ -892,8 +896,9 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
             // unconditional (entries past the slice are never read; lanes past
             // the query block repeat its last word) so that every path
             // consumes the raw loads.
-            static_assert(kMaxTableSlice == kThreads, "one table entry per thread");
-            tbl2[(buf ^ 1) * kMaxTableSlice + tid] = clamp_pid(tbl_raw);
+#pragma unroll
+            for (int i = 0; i < kTblPerThread; ++i)
+                tbl2[(buf ^ 1) * kMaxTableSlice + tid + i * kThreads] = clamp_pid(tbl_raw[i]);
             uint32_t* qn = qs2 + (buf ^ 1) * ((QW + 3) & ~3);
 #pragma unroll
             for (int i = 0; i < QPT; ++i) qn[min(tid + i * kThreads, QW - 1)] = q_raw[i];

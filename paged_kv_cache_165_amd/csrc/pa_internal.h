@@ -13,6 +13,10 @@ namespace pa {
 // Set the calling thread's pa_last_error() message and return `st`.
 pa_status_t fail(pa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
+// Table entries (blocks) one decode partition may span: an item stages that
+// slice of its block table in LDS.
+constexpr int kMaxTableSlice = 512;
+
 // Everything one decode launch needs. Pointers are device pointers.
 struct DecodeParams {
     void* out;

@@ -40,21 +40,34 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(L.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 4
+    assert lib.pa_abi_version() == 5
 
 
 def test_status_strings_and_workspace_size():
     lib, L = _lib()
     assert lib.pa_status_string(0) == b"ok"
     assert lib.pa_status_string(3) == b"workspace missing or too small"
-    assert lib.pa_default_partition_size() == 1024
+    # default split: 256 blocks, halved while the batch has < 512 items, not below 512 tokens
+    dp = lib.pa_default_partition_size
+    assert dp(256, 8, 8192, 16) == 4096          # 2048 (seq, KV head) pairs: 4096 items
+    assert dp(8, 8, 131072, 32) == 8192          # 64 pairs x 16 partitions = 1024 items
+    assert dp(1, 8, 131072, 16) == 2048          # 8 pairs: halve until 8 x 64 = 512 items
+    assert dp(4, 4, 256, 16) == 512              # tiny batch: floor of 512 tokens
+    assert dp(64, 8, 1000, 4) == 1024            # 256 blocks of 4; 512 pairs suffice
+    assert dp(32, 8, 1000, 4) == 512             # 256 pairs: halved once
+    assert dp(2, 1, 4096, 256) == 512
+    assert dp(-1, 8, 100, 16) == 0 and dp(1, 0, 100, 16) == 0 and dp(1, 8, 100, 0) == 0
     # single partition: no workspace needed
-    assert lib.pa_decode_workspace_size(4, 8, 128, 1024, 0) == 0
+    assert lib.pa_decode_workspace_size(4, 8, 8, 128, 512, 16, 0) == 0
+    assert lib.pa_decode_workspace_size(4, 8, 8, 128, 1024, 16, 1024) == 0
     # records of (m, l, o[D]) floats, each region 256-byte aligned
     recs = 4 * 8 * 3
     a = lambda x: (x + 255) // 256 * 256
-    assert lib.pa_decode_workspace_size(4, 8, 128, 1100, 512) == a(recs * 4) * 2 + a(recs * 128 * 4)
-    assert lib.pa_decode_workspace_size(-1, 8, 128, 1100, 0) == 0
+    expect = a(recs * 4) * 2 + a(recs * 128 * 4)
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 512) == expect
+    # the default resolves as pa_default_partition_size does: 4 x 2 pairs, 1100 tokens -> 512
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 0) == expect
+    assert lib.pa_decode_workspace_size(-1, 8, 8, 128, 1100, 16, 0) == 0
 
 
 def _decode(lib, **over):
@@ -77,6 +90,7 @@ def _decode(lib, **over):
     (dict(S=-1), 1, b"zero size"),
     (dict(maxblk=3), 1, b"max_blocks_per_seq"),      # 3 * 16 < 64
     (dict(part=24), 1, b"partition_size"),
+    (dict(part=16 * 513), 1, b"partition_size"),    # 513 blocks: one more than an item stages
     (dict(dtype=7), 1, b"unknown dtype"),
     (dict(q=0), 1, b"null pointer"),
     (dict(out=8), 1, b"16-byte aligned"),

@@ -107,6 +107,18 @@ def test_partition_sizes(part):
     compare_attention(out, run_oracle(c, 0.09), f"part {part}")
 
 
+@pytest.mark.parametrize("dt,g", [(torch.bfloat16, 4), (torch.bfloat16, 1), (torch.float32, 2)])
+def test_full_table_slice_partitions(dt, g):
+    """Partitions of 512 blocks, the most one item stages (two table entries
+    per thread), with sequences just under, at and over one and two of them,
+    and the library's default split on the same batch."""
+    lens = [8191, 8192, 8193, 16385, 40]
+    c = make_case(lens, 2 * g, 2, 128, 16, dt, seed=513 + g)
+    ref = run_oracle(c, 0.07)
+    compare_attention(run_gpu(c, 0.07, part=8192), ref, f"{dt} g{g} part 8192")
+    compare_attention(run_gpu(c, 0.07, part=0), ref, f"{dt} g{g} default partition")
+
+
 @pytest.mark.parametrize("bs", [4, 8, 16, 32, 64, 128, 256])
 @pytest.mark.parametrize("g", [1, 4])
 def test_block_sizes(bs, g):
