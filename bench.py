@@ -487,9 +487,25 @@ def main():
     torch.cuda.synchronize()
     part_us = 1e3 * ka.elapsed_time(kb) / args.steps
     kv = w.kv_bytes()
+    unique = w.unique_kv_bytes()
     value = kv / (ms_step * 1e-3) / 1e9
     achieved = kv / (part_us * 1e-6) / 1e9
     progress(f"step {ms_step * 1e3:.1f} us, partition kernel {part_us:.1f} us per launch")
+
+    # On-box ceiling next to the peak: a plain device copy of 1 GiB (bytes
+    # read plus written, per time), after the timed region.
+    cbuf = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
+    cdst = torch.empty_like(cbuf)
+    for _ in range(3):
+        cdst.copy_(cbuf)
+    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ca.record()
+    for _ in range(10):
+        cdst.copy_(cbuf)
+    cb.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) / (ca.elapsed_time(cb) / 10 * 1e-3) / 1e9
+    del cbuf, cdst
 
     if args.copy_calibration_mb:
         n = args.copy_calibration_mb * (1 << 20) // 2
@@ -539,12 +555,17 @@ def main():
                    "partition_size": resolved_partition(w), "ctx": w.ctx_recipe, "tokens": int(w.context_lens.sum()), "tail_waste": round(W.tail_waste(w), 5),
                    "kv_bytes": kv, "seed": w.seed, "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "copy_ceiling": {"gbs": round(copy_gbs, 1), "pct_of_ceiling": round(100.0 * value / copy_gbs, 2),
+                         "what": "device copy of 1 GiB (bytes read + written per time), 10 launches, same run"},
+        "unique_kv_gbs": round(unique / (ms_step * 1e-3) / 1e9, 2),
+        "unique_kv_bytes": unique,
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "wall_ms_per_step": round(1e3 * t_wall / args.steps, 5),
         "roofline": {"bound": "hbm", "kernel": "pa_decode_partitions (pa_decode_mfma / pa_decode_valu)",
                      "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_us_mean": round(part_us, 2),
+                     "traffic_gbs": round(traffic / (part_us * 1e-6) / 1e9, 2) if traffic else None,
                      "kernel_timing": f"{args.steps} back-to-back launches between two HIP events on the launch stream",
                      "bytes_per_launch": kv},
         "cpu_baseline": cpu,
