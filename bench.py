@@ -91,9 +91,11 @@ def _counter_rows(path, counter):
 
 def resolved_partition(w) -> int:
     """Tokens per partition the decode of workload ``w`` runs with."""
+    import torch
     import paged_kv_cache_165_amd as pa
-    return w.partition_size or pa.default_partition_size(w.num_seqs, w.num_kv_heads, w.max_context_len,
-                                                         w.block_size)
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    return w.partition_size or pa.default_partition_size(w.num_seqs, w.num_heads, w.num_kv_heads,
+                                                         w.max_context_len, w.block_size, dt)
 
 
 def summarize_counters(fetch_csv, write_csv, out_json, workload, calib_mb, partition_size=0):
@@ -450,7 +452,7 @@ def main():
     slots = [torch.from_numpy(op.slots.astype(np.int32)).to(dev) for op in w.writes]
     out = torch.empty_like(q)
     ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_context_len,
-                            w.block_size, w.partition_size, device=dev)
+                            w.block_size, w.partition_size, q.dtype, device=dev)
     dargs = (out, q, kc, vc, tables, lens, w.scale, w.max_context_len, w.partition_size, ws)
 
     def step():

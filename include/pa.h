@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 5
+#define PA_ABI_VERSION 6
 
 typedef enum pa_dtype {
     PA_F32 = 0,  /* IEEE binary32 */
@@ -87,28 +87,33 @@ const char* pa_last_error(void);
 /*
  * Tokens per context partition that pa_decode uses when the caller passes
  * partition_size = 0, a function of the batch's shape only (host code, no
- * device query): 256 blocks (256 * block_size tokens; an item can stage
- * up to 512 blocks, but longer default items unbalance skewed batches),
- * halved while the batch would yield fewer than
- * 512 items (num_seqs * num_kv_heads * ceil(max_context_len / size), two
- * per compute unit of MI355X), but not below 512 tokens. Long partitions
- * cost the fewest item switches and merges; the item count keeps every
- * compute unit fed. Returns 0 for invalid arguments (sizes below zero,
- * num_kv_heads or block_size not positive).
+ * device query). With items = num_seqs * num_kv_heads *
+ * ceil(max_context_len / size):
+ *   - bfloat16 / float16 with 2 or more query heads per KV head (one wave
+ *     reduces an item): min(2048, 128 * block_size), halved while
+ *     items < 2048 (two per wave of MI355X's 256 compute units);
+ *   - otherwise (a workgroup reduces an item): 256 * block_size, halved
+ *     while items < 512;
+ * in both cases not below 512 tokens. Long partitions cost the fewest item
+ * switches and merges; the item count keeps every compute unit fed.
+ * Returns 0 for invalid arguments (sizes below zero, num_heads,
+ * num_kv_heads or block_size not positive, num_heads not a multiple of
+ * num_kv_heads, unknown dtype).
  */
-int pa_default_partition_size(int num_seqs, int num_kv_heads, int max_context_len, int block_size);
+int pa_default_partition_size(int num_seqs, int num_heads, int num_kv_heads, int max_context_len, int block_size,
+                              pa_dtype_t dtype);
 
 /*
  * Bytes of device workspace pa_decode needs: one (max, sum, output row)
  * record in float32 per sequence, query head and partition, or 0 when no
  * sequence can span more than one partition (max_context_len <=
  * partition_size). Returns 0 for invalid arguments too. partition_size = 0
- * selects pa_default_partition_size(num_seqs, num_kv_heads,
- * max_context_len, block_size). The workspace is caller-owned device memory
- * with no required contents; calls that share one must not overlap.
+ * selects pa_default_partition_size(num_seqs, num_heads, num_kv_heads,
+ * max_context_len, block_size, dtype). The workspace is caller-owned device
+ * memory with no required contents; calls that share one must not overlap.
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                                int max_context_len, int block_size, int partition_size);
+                                int max_context_len, int block_size, int partition_size, pa_dtype_t dtype);
 
 /*
  * Paged decode attention.
@@ -145,7 +150,8 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
  *
  * Work is split into items of (sequence, KV head, partition) that a
  * persistent grid processes largest first; an item's result does not depend
- * on which workgroup ran it.
+ * on which workgroup (or, for partitions of at most 128 blocks with 16-bit
+ * elements and grouped query heads, which wave) ran it.
  */
 pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens, float scale,

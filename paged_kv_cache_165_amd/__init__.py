@@ -102,21 +102,24 @@ def _check_caches(k_cache, v_cache):
     return nb, hkv, bs, d
 
 
-def default_partition_size(num_seqs: int, num_kv_heads: int, max_context_len: int, block_size: int) -> int:
+def default_partition_size(num_seqs: int, num_heads: int, num_kv_heads: int, max_context_len: int,
+                           block_size: int, dtype: torch.dtype) -> int:
     """Partition ``decode`` uses for ``partition_size=0`` on a batch of this shape."""
-    return int(library().pa_default_partition_size(num_seqs, num_kv_heads, max_context_len, block_size))
+    return int(library().pa_default_partition_size(num_seqs, num_heads, num_kv_heads, max_context_len,
+                                                   block_size, _DTYPES[dtype]))
 
 
 def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,
-                   block_size: int, partition_size: int = 0) -> int:
+                   block_size: int, partition_size: int, dtype: torch.dtype) -> int:
     return int(library().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                  max_context_len, block_size, partition_size))
+                                                  max_context_len, block_size, partition_size, _DTYPES[dtype]))
 
 
 def alloc_workspace(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,
-                    block_size: int, partition_size: int = 0, device="cuda") -> torch.Tensor:
+                    block_size: int, partition_size: int, dtype: torch.dtype, device="cuda") -> torch.Tensor:
     """Caller-owned workspace tensor (uint8) for ``decode``."""
-    n = workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size, partition_size)
+    n = workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size, partition_size,
+                       dtype)
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
@@ -141,7 +144,7 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
     if max_context_len is None:
         max_context_len = int(context_lens.max().item()) if s else 0  # device -> host read
     if workspace is None:
-        workspace = alloc_workspace(s, hq, hkv, d, max_context_len, bs, partition_size, device=q.device)
+        workspace = alloc_workspace(s, hq, hkv, d, max_context_len, bs, partition_size, q.dtype, device=q.device)
     else:
         _dev_tensor(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()

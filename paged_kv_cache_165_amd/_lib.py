@@ -57,9 +57,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.pa_last_error.restype = ctypes.c_char_p
         lib.pa_last_error.argtypes = []
         lib.pa_default_partition_size.restype = _i
-        lib.pa_default_partition_size.argtypes = [_i, _i, _i, _i]
+        lib.pa_default_partition_size.argtypes = [_i, _i, _i, _i, _i, _i]
         lib.pa_decode_workspace_size.restype = ctypes.c_size_t
-        lib.pa_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+        lib.pa_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
         for name in ("pa_decode", "pa_decode_partitions", "pa_decode_merge"):
             f = getattr(lib, name)
             f.restype = _i

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -15,16 +16,23 @@
 
 namespace {
 
-// Shape of the default split: the longest default partition in blocks,
-// items wanted per launch (two per compute unit of MI355X) and the shortest
-// partition worth its item switch and merge. The default stops at 256 blocks
-// although an item can stage 512: on a skewed batch (lognormal lengths up to
-// 8192) the largest items then take most of a launch and the static deal
-// cannot even them out (measured on MI355X: 285 us against 255 us at 256
-// blocks for 256 sequences of 8 KV heads, and 562 against 465 us for 8
-// sequences of 32k-131k tokens).
+// Shape of the default split.
+// Workgroup items (float32, or one query head per KV head): at most 256
+// blocks, and at least 512 items per launch (two per compute unit of
+// MI355X). The default stops at 256 blocks although an item can stage 512:
+// on a skewed batch (lognormal lengths up to 8192) the largest items then
+// take most of a launch and the static deal cannot even them out (measured
+// on MI355X: 285 us against 255 us at 256 blocks for 256 sequences of 8 KV
+// heads, and 562 against 465 us for 8 sequences of 32k-131k tokens).
+// Wave items (16-bit grouped heads): one wave reduces an item alone, four
+// times slower than a workgroup, so items stay at 2048 tokens or less (and
+// within the wave's table slice), at least 2048 of them (two per wave).
+// Neither goes below 512 tokens, the shortest partition worth its item
+// switch and merge.
 constexpr int kAutoMaxBlocks = 256;
 constexpr int kTargetItems = 512;
+constexpr int kWaveMaxPartition = 2048;
+constexpr int kWaveTargetItems = 2048;
 constexpr int kMinAutoPartition = 512;
 constexpr int kMaxSeqs = 8192;
 using pa::kMaxTableSlice;
@@ -96,24 +104,29 @@ pa_status_t num_cus(int* out) {
 }
 
 // The default split (pa_default_partition_size): start from the longest
-// partition one item can stage and halve it while the batch has too few
-// items to fill the chip. Block sizes are powers of two, so every halving
-// down to 512 stays a multiple of 16 and of block_size.
-int auto_partition(int num_seqs, int num_kv_heads, int max_context_len, int block_size) {
-    int part = kAutoMaxBlocks * block_size;
+// default partition of the kernel the shape runs on and halve it while the
+// batch has too few items to fill the chip. Block sizes are powers of two
+// up to 256, so every halving down to 512 stays a multiple of 16 and of
+// block_size.
+int auto_partition(int num_seqs, int num_heads, int num_kv_heads, int max_context_len, int block_size,
+                   pa_dtype_t dtype) {
+    const bool wave = pa::decode_uses_mfma(dtype, num_heads / num_kv_heads);
+    int part = wave ? std::min(kWaveMaxPartition, pa::kWaveSlice * block_size) : kAutoMaxBlocks * block_size;
+    const long long target = wave ? kWaveTargetItems : kTargetItems;
     while (part > kMinAutoPartition) {
         const long long items = static_cast<long long>(num_seqs) * num_kv_heads *
                                 ((static_cast<long long>(max_context_len) + part - 1) / part);
-        if (items >= kTargetItems) break;
+        if (items >= target) break;
         part /= 2;
     }
     return part;
 }
 
-int resolve_partition(int partition_size, int num_seqs, int num_kv_heads, int max_context_len,
-                      int block_size) {
-    return partition_size == 0 ? auto_partition(num_seqs, num_kv_heads, max_context_len, block_size)
-                               : partition_size;
+int resolve_partition(int partition_size, int num_seqs, int num_heads, int num_kv_heads, int max_context_len,
+                      int block_size, pa_dtype_t dtype) {
+    return partition_size == 0
+               ? auto_partition(num_seqs, num_heads, num_kv_heads, max_context_len, block_size, dtype)
+               : partition_size;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -168,7 +181,8 @@ pa_status_t prepare_decode(void* out, const void* q, const void* k_cache, const 
     if (block_size < min_bs)
         return fail(PA_ERR_UNSUPPORTED, "block_size %d < %d, the smallest block this dtype/head_dim/group supports",
                     block_size, min_bs);
-    const int part = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len, block_size);
+    const int part =
+        resolve_partition(partition_size, num_seqs, num_heads, num_kv_heads, max_context_len, block_size, dtype);
     if (part % 16 != 0 || part % block_size != 0 || part / block_size > kMaxTableSlice)
         return fail(PA_ERR_INVALID_ARG, "partition_size %d must be a multiple of 16 and of block_size %d "
                     "spanning at most %d blocks", part, block_size, kMaxTableSlice);
@@ -290,17 +304,21 @@ const char* pa_status_string(pa_status_t status) {
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
-int pa_default_partition_size(int num_seqs, int num_kv_heads, int max_context_len, int block_size) {
-    if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 || block_size <= 0) return 0;
-    return auto_partition(num_seqs, num_kv_heads, max_context_len, block_size);
+int pa_default_partition_size(int num_seqs, int num_heads, int num_kv_heads, int max_context_len, int block_size,
+                              pa_dtype_t dtype) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+        max_context_len < 0 || block_size <= 0 || !valid_dtype(dtype))
+        return 0;
+    return auto_partition(num_seqs, num_heads, num_kv_heads, max_context_len, block_size, dtype);
 }
 
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                                int max_context_len, int block_size, int partition_size) {
-    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
-        block_size <= 0 || partition_size < 0)
+                                int max_context_len, int block_size, int partition_size, pa_dtype_t dtype) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || head_dim <= 0 ||
+        max_context_len < 0 || block_size <= 0 || partition_size < 0 || !valid_dtype(dtype))
         return 0;
-    const int part = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len, block_size);
+    const int part =
+        resolve_partition(partition_size, num_seqs, num_heads, num_kv_heads, max_context_len, block_size, dtype);
     return ws_layout(num_seqs, num_heads, head_dim, pmax_of(max_context_len, part)).total;
 }
 

@@ -919,6 +919,317 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA kernel, one item per wave
+// ---------------------------------------------------------------------------
+//
+// The per-tile products and softmax of pa_decode_mfma, but each wave reduces
+// whole items on its own: after the schedule is built the waves of a
+// workgroup never wait for each other, and an item ends without a
+// cross-wave combine. Items are dealt to the waves of the grid (numbered
+// workgroup-major) in the same largest-first snake. Each wave keeps in LDS
+// its item's table slice and query block (double buffered: the next item's
+// are loaded raw during the current one and stored at its end) and its own
+// result ring, which it flushes itself.
+
+__host__ __device__ constexpr int wave_q_words(int g, int d) { return ((g * d / 2) + 3) & ~3; }
+
+template <int DT, int D, int G, bool BIGB>
+__global__ __launch_bounds__(kThreads) void pa_decode_mfma_wave(DecodeParams p) {
+    static_assert(DT == PA_BF16 || DT == PA_F16, "MFMA path is for 16-bit elements");
+    static_assert(G == 2 || G == 4 || G == 8 || G == 16, "group size");
+    using EL = Elem<DT>;
+    constexpr int E = 2;
+    constexpr int NK = D / 32;
+    constexpr int NV = D / 16;
+    constexpr int QW = G * D / 2;
+    constexpr int QWP = wave_q_words(G, D);
+    constexpr int QPL = (QW + 63) / 64;
+    constexpr int TPL = kWaveSlice / 64;
+    constexpr float kLazy = 8.f;
+    constexpr int SL = ring_slot_floats(G, D);
+
+    // LDS: schedule | tbl[kWaves][2][kWaveSlice] | qs[kWaves][2][QWP] | ring[kWaves][wring]
+    extern __shared__ __align__(16) unsigned char smem[];
+    Sched sc = sched_lds(p, reinterpret_cast<int*>(smem));
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int* tbl_all = reinterpret_cast<int*>(smem) + sched_ints(p.num_seqs);
+    uint32_t* qs_all = reinterpret_cast<uint32_t*>(tbl_all + kWaves * 2 * kWaveSlice);
+    float* ring_all = reinterpret_cast<float*>(qs_all + kWaves * 2 * QWP);
+    const int wring = p.ring_slots / kWaves;
+    int* tbl2 = tbl_all + wave * 2 * kWaveSlice;
+    uint32_t* qs2 = qs_all + wave * 2 * QWP;
+    float* ring = ring_all + wave * wring * SL;
+    int nring = 0;
+
+    const int r16 = lane & 15;
+    const int j = lane >> 4;
+    const int bs = 1 << p.log2_bs;
+    const int vt = 1 << p.log2_vt;
+    const int hkv = p.num_kv_heads;
+    const size_t blk_el = static_cast<size_t>(bs) * D;
+    const char* kbase = static_cast<const char*>(p.k_cache);
+    const char* vbase = static_cast<const char*>(p.v_cache);
+    const uint32_t* qwords = static_cast<const uint32_t*>(p.q);
+
+    build_schedule(p, sc);  // the last barrier of the kernel
+    const int W = gridDim.x * kWaves;
+    const int gw = blockIdx.x * kWaves + wave;
+    auto wave_item = [&](int r) -> int {
+        const int it = r * W + ((r & 1) ? (W - 1 - gw) : gw);
+        return it < sc.total ? it : -1;
+    };
+    const int item0 = wave_item(0);
+    if (item0 < 0) return;
+
+    struct Buf {
+        u32x4 k[NK];
+        u32x2 v[NV];
+    };
+    auto ntiles_of = [](const Item& x) { return x.t1 > x.t0 ? (x.t1 - x.t0 + 15) >> 4 : 0; };
+    auto last4_of = [](const Item& x) { return x.t1 > x.t0 ? ((x.t1 - 1) >> 2) << 2 : 0; };
+    auto q_word0 = [&](const Item& x) {
+        return (static_cast<size_t>(x.s) * p.num_heads + x.kv * G) * (D / 2);
+    };
+    auto clamp_pid = [&](int pid) { return pid < 0 ? 0 : (pid >= p.num_blocks ? p.num_blocks - 1 : pid); };
+
+    auto load_with = [&](const Item& x, int tile, int pk, int pv, Buf& b) {
+        const int t1 = x.t1;
+        const int tt0 = x.t0 + 16 * tile;
+        const int krow = min(tt0 + r16, t1 - 1);
+        const int vtok = min(tt0 + 4 * j, last4_of(x));
+        if constexpr (BIGB) {
+            const int pid = __builtin_amdgcn_readfirstlane(pk);
+            const size_t tile_el = (static_cast<size_t>(pid) * hkv + x.kv) * blk_el;
+            const char* kt = kbase + tile_el * E;
+            const char* vtp = vbase + (tile_el + static_cast<size_t>((tt0 & (bs - 1)) >> 4) * D * 16) * E;
+            const uint32_t ko = static_cast<uint32_t>(((krow & (bs - 1)) * D + 8 * j) * E);
+            const uint32_t vo = static_cast<uint32_t>(((vtok & 15) + 16 * r16) * E);
+#pragma unroll
+            for (int c = 0; c < NK; ++c) b.k[c] = nt_load<u32x4>(kt, ko + 64 * c);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) b.v[v] = nt_load<u32x2>(vtp, vo + 512 * v);
+        } else {
+            const size_t kel = (static_cast<size_t>(pk) * hkv + x.kv) * blk_el +
+                               static_cast<size_t>(krow & (bs - 1)) * D + 8 * j;
+#pragma unroll
+            for (int c = 0; c < NK; ++c) b.k[c] = nt_load<u32x4>(kbase, (kel + 32 * c) * E);
+            const int voff = vtok & (bs - 1);
+            const size_t vel = (static_cast<size_t>(pv) * hkv + x.kv) * blk_el +
+                               static_cast<size_t>(voff >> p.log2_vt) * D * vt + (voff & (vt - 1)) +
+                               static_cast<size_t>(r16) * vt;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                b.v[v] = nt_load<u32x2>(vbase, (vel + static_cast<size_t>(16 * v) * vt) * E);
+        }
+    };
+    auto tile_blocks = [&](const Item& x, const int* tbl, int tile, int& pk, int& pv) {
+        const int tt0 = x.t0 + 16 * tile;
+        if constexpr (BIGB) {
+            pk = pv = tbl[(min(tt0, x.t1 - 1) >> p.log2_bs) - x.b0];
+        } else {
+            pk = tbl[(min(tt0 + r16, x.t1 - 1) >> p.log2_bs) - x.b0];
+            pv = tbl[(min(tt0 + 4 * j, last4_of(x)) >> p.log2_bs) - x.b0];
+        }
+    };
+    auto stage_slice = [&](const Item& x, int* tbl) {
+        const int* trow = p.block_tables + static_cast<size_t>(x.s) * p.max_blocks + x.b0;
+#pragma unroll
+        for (int i = 0; i < TPL; ++i)
+            if (lane + 64 * i < x.nblk) tbl[lane + 64 * i] = clamp_pid(trow[lane + 64 * i]);
+    };
+
+    // prologue: the first item's table slice and query block, its first tile
+    Item cur = item_at(p, sc, item0);
+    int next_item = wave_item(1);
+    Item nxt = next_item >= 0 ? item_at(p, sc, next_item) : cur;
+    stage_slice(cur, tbl2);
+    for (int w = lane; w < QW; w += 64) qs2[w] = qwords[q_word0(cur) + w];
+    Buf A, B;
+    {
+        int pk = 0, pv = 0;
+        const bool real = ntiles_of(cur) > 0;
+        if (real) tile_blocks(cur, tbl2, 0, pk, pv);
+        load_with(cur, 0, pk, pv, A);
+    }
+
+    for (int k = 0;; ++k) {
+        const int buf = k & 1;
+        const int* tbl = tbl2 + buf * kWaveSlice;
+        const bool has_next = next_item >= 0;
+        const bool next_tile = has_next && ntiles_of(nxt) > 0;
+        // raw loads of the next item's metadata, consumed at the end
+        const int* trow = p.block_tables + static_cast<size_t>(nxt.s) * p.max_blocks + nxt.b0;
+        const int* safe = p.context_lens;
+        int pk_raw, pv_raw;
+        if constexpr (BIGB) {
+            pk_raw = *(next_tile ? trow : safe);
+            pv_raw = pk_raw;
+        } else {
+            pk_raw = *(next_tile ? trow + ((min(nxt.t0 + r16, nxt.t1 - 1) >> p.log2_bs) - nxt.b0) : safe);
+            pv_raw = *(next_tile ? trow + ((min(nxt.t0 + 4 * j, last4_of(nxt)) >> p.log2_bs) - nxt.b0) : safe);
+        }
+        int tbl_raw[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i)
+            tbl_raw[i] = *(has_next && lane + 64 * i < nxt.nblk ? trow + lane + 64 * i : safe);
+        uint32_t q_raw[QPL];
+#pragma unroll
+        for (int i = 0; i < QPL; ++i) q_raw[i] = qwords[q_word0(nxt) + min(lane + 64 * i, QW - 1)];
+
+        u32x4 qf[NK];
+        {
+            const uint32_t* qrow = qs2 + buf * QWP + (r16 % G) * (D / 2);
+#pragma unroll
+            for (int c = 0; c < NK; ++c) qf[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c + 4 * j);
+        }
+        f32x4_t acc[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        float m_run = -INFINITY, lsum = 0.f;
+        const int t1 = cur.t1;
+        const int ntiles = ntiles_of(cur);
+
+        auto compute_tile = [&](int tile, const Buf& b) {
+            const int tt0 = cur.t0 + 16 * tile;
+            f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NK; ++c) st = mfma_qk<DT>(b.k[c], qf[c], st);
+            float x[4];
+            bool valid[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                valid[r] = tt0 + 4 * j + r < t1;
+                x[r] = valid[r] ? st[r] * p.scale_log2 : -INFINITY;
+            }
+            float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const bool need = tmax > m_run + kLazy;
+            if (__any(need)) {
+                const float mn = need ? tmax : m_run;
+                const float alpha = fast_exp2(m_run - mn);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) acc[v] *= alpha;
+                lsum *= alpha;
+                m_run = mn;
+            }
+            float pr[4];
+            u32x2 pb;
+            pb.x = pack2<DT>(fast_exp2(x[0] - m_run), fast_exp2(x[1] - m_run), pr[0], pr[1]);
+            pb.y = pack2<DT>(fast_exp2(x[2] - m_run), fast_exp2(x[3] - m_run), pr[2], pr[3]);
+            lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            const uint32_t mask0 = (valid[0] ? 0xffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
+            const uint32_t mask1 = (valid[2] ? 0xffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                u32x2 a = b.v[v];
+                a.x &= mask0;
+                a.y &= mask1;
+                acc[v] = mfma_pv<DT>(a, pb, acc[v]);
+            }
+        };
+        auto load_tile = [&](int tile, Buf& b) {
+            int pk, pv;
+            tile_blocks(cur, tbl, tile, pk, pv);
+            load_with(cur, tile, pk, pv, b);
+        };
+        auto load_next = [&](Buf& b) {
+            int pk = pk_raw, pv = pv_raw;
+            asm volatile("" : "+v"(pk), "+v"(pv));
+            if (next_tile) load_with(nxt, 0, clamp_pid(pk), clamp_pid(pv), b);
+            else load_with(cur, 0, 0, 0, b);
+        };
+
+        // the item's tiles, two deep (the structure of pa_decode_mfma with
+        // one wave taking every tile)
+        int t = 0;
+        if (ntiles > 0) {
+            for (int i = 0; i < ((ntiles - 1) >> 1); ++i) {
+                load_tile(t + 1, B);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_tile(t, A);
+                __builtin_amdgcn_sched_barrier(0);
+                load_tile(t + 2, A);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_tile(t + 1, B);
+                t += 2;
+            }
+            if (ntiles & 1) {
+                compute_tile(t, A);
+            } else {
+                load_tile(t + 1, B);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_tile(t, A);
+                compute_tile(t + 1, B);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_next(A);
+        asm volatile("" ::"v"(pk_raw), "v"(pv_raw));
+
+        // acc[v][r] = O^T[d = 16v + 4j + r][head column r16]
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+        {
+            float* slot = ring + nring * SL;
+            if (r16 < G) {
+                const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    f32x4_t o = acc[v] * inv;
+                    *reinterpret_cast<f32x4_t*>(slot + r16 * D + 16 * v + 4 * j) = o;
+                }
+                if (j == 0) {
+                    slot[G * D + r16] = m_run;
+                    slot[G * D + G + r16] = lsum;
+                }
+            }
+            if (lane == 0) {
+                int* meta = reinterpret_cast<int*>(slot + G * D + 2 * G);
+                meta[0] = cur.s;
+                meta[1] = cur.kv;
+                meta[2] = cur.pidx;
+                meta[3] = cur.nparts;
+            }
+        }
+        // the next item's table slice and query block (unconditional stores:
+        // every path consumes the raw loads)
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) tbl2[(buf ^ 1) * kWaveSlice + lane + 64 * i] = clamp_pid(tbl_raw[i]);
+#pragma unroll
+        for (int i = 0; i < QPL; ++i) qs2[(buf ^ 1) * QWP + min(lane + 64 * i, QW - 1)] = q_raw[i];
+        ++nring;
+        if (nring == wring || !has_next) {
+            for (int i = 0; i < nring; ++i) {
+                const float* sl = ring + i * SL;
+                const int* meta = reinterpret_cast<const int*>(sl + G * D + 2 * G);
+                const int s = meta[0], kv = meta[1], pidx = meta[2], nparts = meta[3];
+                const size_t row0 = static_cast<size_t>(s) * p.num_heads + kv * G;
+                if (nparts == 1) {
+                    for (int idx = lane; idx < G * D; idx += 64) EL::store(p.out, row0 * D + idx, sl[idx]);
+                } else {
+                    for (int idx = lane; idx < G * D; idx += 64) {
+                        const int h = idx / D;
+                        const int d = idx - h * D;
+                        p.ws_o[((row0 + h) * p.pmax + pidx) * D + d] = sl[idx];
+                    }
+                    if (lane < G) {
+                        const size_t rec = (row0 + lane) * p.pmax + pidx;
+                        p.ws_m[rec] = sl[G * D + lane];
+                        p.ws_l[rec] = sl[G * D + G + lane];
+                    }
+                }
+            }
+            nring = 0;
+        }
+        if (!has_next) break;
+        cur = nxt;
+        next_item = wave_item(k + 2);
+        if (next_item >= 0) nxt = item_at(p, sc, next_item);
+    }
+}
+
 // Log-sum-exp merge of the partition records of one (sequence, query head).
 template <int DT, int D>
 __global__ __launch_bounds__(64) void pa_merge(DecodeParams p) {
@@ -1009,7 +1320,7 @@ size_t decode_smem_mfma(int num_seqs, int d, int g) {
 // refused with hipErrorInvalidConfiguration before anything is launched.
 template <typename K>
 hipError_t launch_persistent(K kern, DecodeParams p, size_t fixed_smem, int d, int g, int num_cus,
-                             int max_per_cu, hipStream_t stream) {
+                             int max_per_cu, hipStream_t stream, int ring_multiple = 1) {
     hipFuncAttributes attr{};
     hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kern));
     if (e != hipSuccess) return e;
@@ -1020,7 +1331,7 @@ hipError_t launch_persistent(K kern, DecodeParams p, size_t fixed_smem, int d, i
     if (occ < 1) occ = 1;
     if (max_per_cu > 0 && occ > max_per_cu) occ = max_per_cu;
     if (PA_WG_PER_CU > 0 && occ > PA_WG_PER_CU) occ = PA_WG_PER_CU;
-    p.ring_slots = ring_slots_for(static_lds + fixed_smem, d, g, occ);
+    p.ring_slots = ring_slots_for(static_lds + fixed_smem, d, g, occ) / ring_multiple * ring_multiple;
     if (p.ring_slots < 1) return hipErrorInvalidConfiguration;
     const size_t smem = fixed_smem + static_cast<size_t>(p.ring_slots) * ring_slot_floats(g, d) * sizeof(float);
     const size_t alloc = lds_alloc(static_lds + smem);
@@ -1049,8 +1360,22 @@ hipError_t launch_valu(const DecodeParams& p, int num_cus, hipStream_t stream) {
     return launch_persistent(pa_decode_valu<DT, D, G, false>, p, fixed, D, G, num_cus, 0, stream);
 }
 
+size_t decode_smem_mfma_wave(int num_seqs, int d, int g) {
+    // prefix | per wave: two table slices, two query blocks
+    return (sched_ints(num_seqs) + static_cast<size_t>(kWaves) * 2 * kWaveSlice) * sizeof(int) +
+           static_cast<size_t>(kWaves) * 2 * wave_q_words(g, d) * sizeof(uint32_t);
+}
+
 template <int DT, int D, int G>
 hipError_t launch_mfma(const DecodeParams& p, int num_cus, hipStream_t stream) {
+    if ((p.part >> p.log2_bs) <= kWaveSlice) {
+        const size_t fixed = decode_smem_mfma_wave(p.num_seqs, D, G);
+        if ((1 << p.log2_bs) >= 16)
+            return launch_persistent(pa_decode_mfma_wave<DT, D, G, true>, p, fixed, D, G, num_cus, kMfmaWgPerCu,
+                                     stream, kWaves);
+        return launch_persistent(pa_decode_mfma_wave<DT, D, G, false>, p, fixed, D, G, num_cus, kMfmaWgPerCu,
+                                 stream, kWaves);
+    }
     const size_t fixed = decode_smem_mfma(p.num_seqs, D, G);
     if ((1 << p.log2_bs) >= 16)
         return launch_persistent(pa_decode_mfma<DT, D, G, true>, p, fixed, D, G, num_cus, kMfmaWgPerCu, stream);
@@ -1103,6 +1428,10 @@ hipError_t launch_merge_d(const DecodeParams& p, int head_dim, hipStream_t strea
 }  // namespace
 
 bool decode_uses_mfma(pa_dtype_t dt, int group) { return dt != PA_F32 && group >= 2; }
+
+bool decode_wave_items(pa_dtype_t dt, int group, int part_blocks) {
+    return decode_uses_mfma(dt, group) && part_blocks <= kWaveSlice;
+}
 
 int decode_min_block_size(pa_dtype_t dt, int head_dim, int group) {
     if (decode_uses_mfma(dt, group)) return 4;

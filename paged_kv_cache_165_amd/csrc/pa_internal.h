@@ -16,6 +16,9 @@ pa_status_t fail(pa_status_t st, const char* fmt, ...) __attribute__((format(pri
 // Table entries (blocks) one decode partition may span: an item stages that
 // slice of its block table in LDS.
 constexpr int kMaxTableSlice = 512;
+// Partitions of at most this many blocks run on the MFMA kernel that gives
+// each wave whole items (bfloat16 / float16 with grouped query heads).
+constexpr int kWaveSlice = 128;
 
 // Everything one decode launch needs. Pointers are device pointers.
 struct DecodeParams {
@@ -83,6 +86,8 @@ hipError_t launch_decode_merge(const DecodeParams& p, pa_dtype_t dt, int head_di
                                hipStream_t stream);
 bool decode_supported(pa_dtype_t dt, int head_dim, int group);
 bool decode_uses_mfma(pa_dtype_t dt, int group);
+// Whether a partition of `part_blocks` blocks runs one item per wave.
+bool decode_wave_items(pa_dtype_t dt, int group, int part_blocks);
 int decode_min_block_size(pa_dtype_t dt, int head_dim, int group);
 
 bool prefill_supported(pa_dtype_t dt, int head_dim, int group);

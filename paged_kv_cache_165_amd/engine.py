@@ -55,9 +55,8 @@ class PagedDecoder:
         return torch.from_numpy(np.ascontiguousarray(a)).pin_memory().to(self.device, non_blocking=True)
 
     def _workspace_for(self, num_seqs: int, max_ctx: int) -> torch.Tensor:
-        need = int(_lib.load().pa_decode_workspace_size(num_seqs, self.num_heads, self.num_kv_heads,
-                                                        self.head_dim, max_ctx, self.block_size,
-                                                        self.partition_size))
+        need = self._pa.workspace_size(num_seqs, self.num_heads, self.num_kv_heads, self.head_dim, max_ctx,
+                                       self.block_size, self.partition_size, self.k_cache.dtype)
         if need > self._workspace.numel():
             self._workspace = torch.empty(max(need, 2 * self._workspace.numel()), dtype=torch.uint8,
                                           device=self.device)

@@ -84,7 +84,8 @@ class DeviceCase:
         self.slots = [torch.from_numpy(op.slots.astype(np.int32)).to(device) for op in w.writes]
         self.out = torch.empty_like(self.q)
         self.workspace = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
-                                            w.max_context_len, w.block_size, w.partition_size, device=device)
+                                            w.max_context_len, w.block_size, w.partition_size, self.q.dtype,
+                                            device=device)
 
     def gpu_step(self, partition_size=None, decode=True):
         w = self.w
@@ -96,7 +97,7 @@ class DeviceCase:
             part = w.partition_size if partition_size is None else partition_size
             ws = self.workspace
             need = pa.workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_context_len,
-                                     w.block_size, part)
+                                     w.block_size, part, self.q.dtype)
             if need > ws.numel():
                 ws = torch.empty(need, dtype=torch.uint8, device=self.q.device)
             pa.decode(self.out, self.q, self.k_cache, self.v_cache, self.tables, self.lens, w.scale,

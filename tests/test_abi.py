@@ -40,34 +40,48 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(L.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 5
+    assert lib.pa_abi_version() == 6
 
 
 def test_status_strings_and_workspace_size():
     lib, L = _lib()
     assert lib.pa_status_string(0) == b"ok"
     assert lib.pa_status_string(3) == b"workspace missing or too small"
-    # default split: 256 blocks, halved while the batch has < 512 items, not below 512 tokens
     dp = lib.pa_default_partition_size
-    assert dp(256, 8, 8192, 16) == 4096          # 2048 (seq, KV head) pairs: 4096 items
-    assert dp(8, 8, 131072, 32) == 8192          # 64 pairs x 16 partitions = 1024 items
-    assert dp(1, 8, 131072, 16) == 2048          # 8 pairs: halve until 8 x 64 = 512 items
-    assert dp(4, 4, 256, 16) == 512              # tiny batch: floor of 512 tokens
-    assert dp(64, 8, 1000, 4) == 1024            # 256 blocks of 4; 512 pairs suffice
-    assert dp(32, 8, 1000, 4) == 512             # 256 pairs: halved once
-    assert dp(2, 1, 4096, 256) == 512
-    assert dp(-1, 8, 100, 16) == 0 and dp(1, 0, 100, 16) == 0 and dp(1, 8, 100, 0) == 0
+    F32, BF16, F16 = 0, 1, 2
+    # workgroup items (float32, or one query head per KV head): 256 blocks,
+    # halved while the batch has < 512 items, not below 512 tokens
+    assert dp(64, 32, 32, 4096, 16, BF16) == 4096     # 2048 pairs, one partition each
+    assert dp(256, 8, 8, 8192, 16, F32) == 4096
+    assert dp(8, 8, 8, 131072, 32, F32) == 8192       # 64 pairs x 16 partitions = 1024 items
+    assert dp(1, 8, 8, 131072, 16, F32) == 2048       # 8 pairs: halve until 8 x 64 = 512 items
+    assert dp(4, 4, 4, 256, 16, F32) == 512           # tiny batch: floor of 512 tokens
+    assert dp(64, 8, 8, 1000, 4, BF16) == 1024        # 256 blocks of 4; 512 pairs suffice
+    assert dp(32, 8, 8, 1000, 4, F16) == 512          # 256 pairs: halved once
+    assert dp(2, 1, 1, 4096, 256, BF16) == 512
+    # wave items (16-bit, grouped heads): min(2048, 128 blocks), halved while < 2048 items
+    assert dp(256, 32, 8, 8192, 16, BF16) == 2048     # 2048 pairs x 4 partitions
+    assert dp(8, 64, 8, 131072, 32, BF16) == 2048     # 64 pairs x 64 partitions
+    assert dp(1, 64, 8, 131072, 32, F16) == 512       # 8 pairs: halve to the floor
+    assert dp(256, 32, 8, 1000, 8, BF16) == 1024      # 128 blocks of 8
+    assert dp(256, 32, 8, 1000, 4, BF16) == 512       # 128 blocks of 4
+    assert dp(64, 32, 8, 2000, 16, BF16) == 512       # 512 pairs: halve until 512 x 4 items
+    for bad in [(-1, 8, 8, 100, 16, 1), (1, 8, 0, 100, 16, 1), (1, 8, 8, 100, 0, 1), (1, 8, 3, 100, 16, 1),
+                (1, 8, 8, 100, 16, 7)]:
+        assert dp(*bad) == 0, bad
     # single partition: no workspace needed
-    assert lib.pa_decode_workspace_size(4, 8, 8, 128, 512, 16, 0) == 0
-    assert lib.pa_decode_workspace_size(4, 8, 8, 128, 1024, 16, 1024) == 0
+    assert lib.pa_decode_workspace_size(4, 8, 8, 128, 512, 16, 0, BF16) == 0
+    assert lib.pa_decode_workspace_size(4, 8, 8, 128, 1024, 16, 1024, BF16) == 0
     # records of (m, l, o[D]) floats, each region 256-byte aligned
     recs = 4 * 8 * 3
     a = lambda x: (x + 255) // 256 * 256
     expect = a(recs * 4) * 2 + a(recs * 128 * 4)
-    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 512) == expect
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 512, BF16) == expect
     # the default resolves as pa_default_partition_size does: 4 x 2 pairs, 1100 tokens -> 512
-    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 0) == expect
-    assert lib.pa_decode_workspace_size(-1, 8, 8, 128, 1100, 16, 0) == 0
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 0, BF16) == expect
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 0, F32) == expect
+    assert lib.pa_decode_workspace_size(-1, 8, 8, 128, 1100, 16, 0, BF16) == 0
+    assert lib.pa_decode_workspace_size(4, 8, 8, 128, 1100, 16, 0, 9) == 0
 
 
 def _decode(lib, **over):

@@ -119,6 +119,19 @@ def test_full_table_slice_partitions(dt, g):
     compare_attention(run_gpu(c, 0.07, part=0), ref, f"{dt} g{g} default partition")
 
 
+@pytest.mark.parametrize("bs", [4, 8, 16, 32])
+@pytest.mark.parametrize("dt,g", [(torch.bfloat16, 4), (torch.float16, 8)])
+def test_wave_and_workgroup_mfma_kernels(dt, g, bs):
+    """16-bit grouped heads run one item per wave when a partition spans at
+    most 128 blocks and one item per workgroup above that: both, at every
+    small block size, and the library's default split."""
+    lens = [1, 5, 16, 31, 700, 2049, 5000]
+    c = make_case(lens, 2 * g, 2, 128, bs, dt, seed=40 + bs + g)
+    ref = run_oracle(c, 0.08)
+    for part, kind in ((128 * bs, "wave"), (256 * bs, "workgroup"), (0, "default")):
+        compare_attention(run_gpu(c, 0.08, part=part), ref, f"{dt} g{g} bs{bs} part {part} ({kind})")
+
+
 @pytest.mark.parametrize("bs", [4, 8, 16, 32, 64, 128, 256])
 @pytest.mark.parametrize("g", [1, 4])
 def test_block_sizes(bs, g):
