@@ -8,7 +8,9 @@
  *                   the cached tokens up to its own position;
  *   pa_write_cache  write each new token's K and V rows into the slot given by
  *                   a slot mapping;
- *   pa_copy_blocks  whole-block copies, the copy half of copy-on-write.
+ *   pa_copy_blocks  whole-block copies, the copy half of copy-on-write;
+ *   pa_append_block_tables  record each sequence's newest block in its
+ *                   device block-table row after a decode append.
  *
  * Pages the operations are defined by (cited below by short name):
  *   [aiqz]     aiqz.cc/article/paged-attention-mechanism.html (PagedAttention
@@ -58,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 6
+#define PA_ABI_VERSION 7
 
 typedef enum pa_dtype {
     PA_F32 = 0,  /* IEEE binary32 */
@@ -272,6 +274,22 @@ pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_
  * is those calls, num_layers = 0 a no-op, at most 65535 layers
  * (PA_ERR_UNSUPPORTED beyond).
  */
+/*
+ * Keep device block tables in step with a decode append, without sending
+ * rows from the host: for each sequence i with L = context_lens[i] >= 1 and
+ * slot_mapping[i] >= 0, block_tables[i][(L - 1) / block_size] =
+ * slot_mapping[i] / block_size -- the physical block of its newest token
+ * (token L - 1) in its table row ([aiqz] section 块表映射机制: a sequence
+ * takes a new block when its last one is full; [aiqz] section 前缀共享机制:
+ * a copy-on-write replaces the block the write goes to). Every other entry
+ * is left as it is. block_tables is int32 [num_seqs][max_blocks_per_seq],
+ * context_lens and slot_mapping int32 [num_seqs] (lengths including the new
+ * token), all device memory. A column past max_blocks_per_seq skips the
+ * sequence. block_size a power of two up to 256.
+ */
+pa_status_t pa_append_block_tables(int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                                   const int32_t* slot_mapping, int num_seqs, int block_size, void* stream);
+
 pa_status_t pa_write_cache_layers(const void* k, const void* v, void* k_cache, void* v_cache,
                                   const int32_t* slot_mapping, int num_tokens, int num_layers,
                                   int num_kv_heads, int head_dim, int block_size, int num_blocks,

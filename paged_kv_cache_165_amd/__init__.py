@@ -31,7 +31,7 @@ from . import _lib
 __all__ = [
     "PaError", "library", "default_partition_size", "workspace_size", "alloc_workspace",
     "v_tile", "v_cache_shape", "alloc_cache",
-    "decode", "decode_partitions", "decode_merge", "prefill", "write_cache", "copy_blocks",
+    "decode", "decode_partitions", "decode_merge", "append_block_tables", "prefill", "write_cache", "copy_blocks",
     "alloc_cache_layers", "write_cache_layers", "copy_blocks_layers",
 ]
 
@@ -246,6 +246,20 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs):
     _check(library().pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src_dst_pairs.data_ptr(),
                                     src_dst_pairs.shape[0], hkv, bs, d, nb, _DTYPES[k_cache.dtype],
                                     _stream(k_cache)))
+
+
+def append_block_tables(block_tables, context_lens, slot_mapping, block_size: int):
+    """Record each sequence's newest block in its device table row
+    (``pa_append_block_tables``): block_tables[i][(L - 1) // B] =
+    slot_mapping[i] // B for L = context_lens[i] >= 1 and a slot >= 0."""
+    _dev_tensor(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev_tensor(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _dev_tensor(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
+    n = block_tables.shape[0]
+    if context_lens.shape[0] != n or slot_mapping.shape[0] != n:
+        raise ValueError("one context length and one slot per table row")
+    _check(library().pa_append_block_tables(block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+                                            slot_mapping.data_ptr(), n, int(block_size), _stream(block_tables)))
 
 
 def alloc_cache_layers(num_layers: int, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,

@@ -475,4 +475,19 @@ pa_status_t pa_copy_blocks_layers(void* k_cache, void* v_cache, const int32_t* s
                               head_dim, num_blocks, dtype, stream);
 }
 
+pa_status_t pa_append_block_tables(int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                                   const int32_t* slot_mapping, int num_seqs, int block_size, void* stream) {
+    if (num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_seqs=%d max_blocks_per_seq=%d block_size=%d)",
+                    num_seqs, max_blocks_per_seq, block_size);
+    if (!is_pow2(block_size) || block_size > 256)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two up to 256", block_size);
+    if (num_seqs == 0) return PA_OK;
+    if (!block_tables || !context_lens || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    hipError_t e = pa::launch_table_append(block_tables, max_blocks_per_seq, context_lens, slot_mapping, num_seqs,
+                                           block_size, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "table append kernel launch");
+    return PA_OK;
+}
+
 }  // extern "C"

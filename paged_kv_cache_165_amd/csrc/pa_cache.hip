@@ -138,6 +138,33 @@ __global__ __launch_bounds__(256) void pa_copy_kernel(u32x4* __restrict__ kc, u3
     for (; x < block16; x += 256) __builtin_nontemporal_store(from[x], to + x);
 }
 
+// One thread per sequence: the block that holds the sequence's newest token
+// (token L - 1, at the slot the append gave it) goes into its table row, at
+// column (L - 1) / B. The entry changes only when the token opened a block or
+// a copy-on-write moved it; writing it every step keeps the table in step
+// with the slots without the host sending rows.
+__global__ __launch_bounds__(256) void pa_table_append_kernel(int32_t* __restrict__ tables, int max_blocks,
+                                                              const int32_t* __restrict__ lens,
+                                                              const int32_t* __restrict__ slots, int num_seqs,
+                                                              int log2_bs) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= num_seqs) return;
+    const int L = lens[i];
+    const int slot = slots[i];
+    if (L <= 0 || slot < 0) return;
+    const int col = (L - 1) >> log2_bs;
+    if (col >= max_blocks) return;
+    tables[static_cast<size_t>(i) * max_blocks + col] = slot >> log2_bs;
+}
+
+hipError_t launch_table_append(int32_t* tables, int max_blocks, const int32_t* lens, const int32_t* slots,
+                               int num_seqs, int block_size, hipStream_t stream) {
+    if (num_seqs == 0) return hipSuccess;
+    hipLaunchKernelGGL(pa_table_append_kernel, dim3(static_cast<unsigned>((num_seqs + 255) / 256)), dim3(256), 0,
+                       stream, tables, max_blocks, lens, slots, num_seqs, ilog2(block_size));
+    return hipGetLastError();
+}
+
 hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                               const int32_t* slots, int num_tokens, int num_layers, int num_kv_heads,
                               int head_dim, int elem_bytes, int block_size, int num_blocks,

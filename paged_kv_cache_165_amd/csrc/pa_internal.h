@@ -99,6 +99,8 @@ hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void*
                               const int32_t* slots, int num_tokens, int num_layers, int num_kv_heads,
                               int head_dim, int elem_bytes, int block_size, int num_blocks,
                               hipStream_t stream);
+hipError_t launch_table_append(int32_t* tables, int max_blocks, const int32_t* lens, const int32_t* slots,
+                               int num_seqs, int block_size, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
                               int num_layers, size_t block_bytes, int num_blocks, hipStream_t stream);
 

@@ -4,12 +4,18 @@ include/pa.h in the order the copy-on-write scheme needs them -- copy the
 shared blocks a write would touch, write the new tokens, decode.
 
 Host work per step is the block manager's bookkeeping and one upload of the
-step's slot mapping, copy pairs, block tables and lengths, which the native
-manager writes straight into a pinned staging buffer; every byte of K/V is
-moved and reduced by the library's kernels. The upload runs on a copy stream
-of its own (default priority, ordered against the compute stream by events),
-so it overlaps the previous step's kernels, and nothing in a step waits for
-the GPU unless the host is two steps ahead.
+step's slot mapping, lengths and copy pairs, which the native manager writes
+straight into a pinned staging buffer; every byte of K/V is moved and
+reduced by the library's kernels. The block tables stay on the device: when
+a step decodes the same sequences as the step before, the only table entry
+that can change per sequence is the one of its newest token (a new block,
+or a copy-on-write), and pa_append_block_tables writes it from the slot
+mapping on the device. Any other change (a new batch, a prefill, fork or
+free) uploads the tables in full once. The upload runs on a copy stream of
+its own (default priority, ordered against the compute stream by events);
+the few KB of a step with the same sequences go in order on the compute
+stream. Nothing in a step waits for the GPU unless the host is two steps
+ahead.
 """
 
 from __future__ import annotations
@@ -44,8 +50,11 @@ class PagedDecoder:
         self._workspace = torch.empty(16, dtype=torch.uint8, device=self.device)
         self._staging = []   # two staging sets, used in turn (see _staging_for)
         self._turn = 0
-        self._cap = 0        # batch size the staging buffers hold
+        self._cap = 0        # batch size the staging buffers and the device tables hold
         self._copy_stream = torch.cuda.Stream(device=self.device)
+        self._dtables = None  # device block tables [cap, max_blocks] of the rows in self._rows
+        self._rows = None     # int64 sequence ids of those rows, or None once any table may differ
+        self._lens = None     # host copy of the rows' context lengths
 
     # -- host -> device -----------------------------------------------------
     def _dev(self, a: np.ndarray) -> torch.Tensor:
@@ -72,6 +81,7 @@ class PagedDecoder:
         and returns (slots, out)."""
         n = int(k.shape[0])
         self.blocks.prefill(seq, n)
+        self._rows = None
         table, lens = self.blocks.block_tables([seq], max(-(-n // self.block_size), 1), pad=0)
         pos = np.arange(n)
         slots = (table[0][pos // self.block_size] * self.block_size + pos % self.block_size).astype(np.int32)
@@ -94,9 +104,11 @@ class PagedDecoder:
         ``parent``'s blocks."""
         n = self.blocks.seq_tokens(parent) if num_tokens is None else int(num_tokens)
         self.blocks.share(child, parent, n)
+        self._rows = None
 
     def free(self, seq: int) -> None:
         self.blocks.free(seq)
+        self._rows = None
 
     def _staging_for(self, n: int):
         """The next staging set, holding at least n sequences: a pinned host
@@ -111,6 +123,9 @@ class PagedDecoder:
                                   dev=torch.empty(words, dtype=torch.int32, device=self.device),
                                   copied=torch.cuda.Event(), consumed=torch.cuda.Event())
                              for _ in range(2)]
+            self._dtables = torch.empty(cap, self.max_blocks, dtype=torch.int32, device=self.device)
+            self._lens = np.zeros(cap, np.int32)
+            self._rows = None
             self._cap = cap
         st = self._staging[self._turn]
         self._turn ^= 1
@@ -131,19 +146,39 @@ class PagedDecoder:
         h = host.numpy()
         slots, lens = h[:n], h[n:2 * n]
         pairs = h[2 * n:4 * n].reshape(n, 2)
-        tables = h[4 * n:4 * n + n * self.max_blocks].reshape(n, self.max_blocks)
         npairs = self.blocks.append_into(s, slots, pairs)
-        self.blocks.block_tables_into(s, tables, lens, pad=0)
-        words = 4 * n + n * self.max_blocks
+        same_rows = self._rows is not None and len(self._rows) == n and np.array_equal(self._rows, s)
+        if same_rows:
+            # every row grew by one token; its newest block follows from its slot
+            self._lens[:n] += 1
+            lens[:] = self._lens[:n]
+            words = 4 * n
+        else:
+            tables = h[4 * n:4 * n + n * self.max_blocks].reshape(n, self.max_blocks)
+            self.blocks.block_tables_into(s, tables, lens, pad=0)
+            self._lens[:n] = lens
+            words = 4 * n + n * self.max_blocks
         compute = torch.cuda.current_stream(self.device)
-        self._copy_stream.wait_event(st["consumed"])  # kernels of two steps ago have read dev
-        with torch.cuda.stream(self._copy_stream):
+        if same_rows:
+            # a few KB: in order on the compute stream, which costs less than
+            # a hand-over between two queues
             dev[:words].copy_(host[:words], non_blocking=True)
-            st["copied"].record(self._copy_stream)
-        compute.wait_event(st["copied"])
+            st["copied"].record(compute)
+        else:
+            # the full tables go on the copy stream, which moves them faster
+            self._copy_stream.wait_event(st["consumed"])  # kernels of two steps ago have read dev
+            with torch.cuda.stream(self._copy_stream):
+                dev[:words].copy_(host[:words], non_blocking=True)
+                st["copied"].record(self._copy_stream)
+            compute.wait_event(st["copied"])
         d_slots, d_lens = dev[:n], dev[n:2 * n]
         d_pairs = dev[2 * n:2 * n + 2 * npairs].view(npairs, 2)
-        d_tables = dev[4 * n:4 * n + n * self.max_blocks].view(n, self.max_blocks)
+        d_tables = self._dtables[:n]
+        if same_rows:
+            self._pa.append_block_tables(d_tables, d_lens, d_slots, self.block_size)
+        else:
+            d_tables.copy_(dev[4 * n:4 * n + n * self.max_blocks].view(n, self.max_blocks))
+            self._rows = s.copy()
         if npairs:
             self._pa.copy_blocks(self.k_cache, self.v_cache, d_pairs)
         self._pa.write_cache(k, v, self.k_cache, self.v_cache, d_slots)

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(L.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 6
+    assert lib.pa_abi_version() == 7
 
 
 def test_status_strings_and_workspace_size():
@@ -207,3 +207,17 @@ def test_missing_library_fails_loudly(tmp_path):
             L.load(str(tmp_path / "libpa.so"))
         finally:
             L._lib = saved
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((16, 4, 32, 48, -1, 16), 1, b"zero size"),
+    ((16, 0, 32, 48, 2, 16), 1, b"zero size"),
+    ((16, 4, 32, 48, 2, 12), 2, b"power of two"),
+    ((16, 4, 32, 48, 2, 512), 2, b"power of two"),
+    ((0, 4, 32, 48, 2, 16), 1, b"null pointer"),
+])
+def test_append_block_tables_rejects_before_launch(args, status, msg):
+    lib, _ = _lib()
+    assert lib.pa_append_block_tables(*args, None) == status
+    assert msg in lib.pa_last_error()
+    assert lib.pa_append_block_tables(0, 4, 0, 0, 0, 16, None) == 0   # empty batch: nothing to do
