@@ -15,14 +15,16 @@
 // tokens). A persistent grid of 256-thread workgroups walks the items largest
 // first; every workgroup first builds that order in LDS (a prefix sum of full
 // partitions, searched by bisection, then the partial partitions sorted by
-// size: see "Work order and assignment" below). The four waves of a
-// workgroup share one item and take its steps round robin. The slice of the block table the partition reads is staged in LDS
-// (cf-1.com blog, 2.2 and 5.4: table lookups served from shared memory, not
-// global memory). K/V are streamed with nontemporal 16-byte loads, the next
-// step always in flight while the current one is reduced (cf-1.com 5.1 and
-// 6.2: prefetch the next physical block).
+// size: see "Work order and assignment" below). Either the four waves of a
+// workgroup share one item and take its steps round robin, or (the
+// wave-item kernel) each wave reduces whole items alone. The slice of the
+// block table the partition reads is staged in LDS (cf-1.com blog, 2.2 and
+// 5.4: table lookups served from shared memory, not global memory). K/V are
+// streamed with nontemporal 16-byte loads, the next step always in flight
+// while the current one is reduced (cf-1.com 5.1 and 6.2: prefetch the next
+// physical block).
 //
-// Two inner loops:
+// Two inner loops, three kernels:
 //  * pa_decode_valu (one query head per KV head, and float32): q.k is a
 //    per-lane partial dot product finished by a DPP butterfly over the lanes
 //    that hold one K row; each lane keeps an online softmax over its rows and
@@ -33,8 +35,12 @@
 //    query rows as B columns), and O^T += V^T P^T is D/16 v_mfma_f32_16x16x16
 //    whose B operand is exactly the lane layout of S^T after exp2, so P never
 //    leaves registers. The softmax max is rescaled lazily (only when a tile's
-//    max exceeds the running max by more than 2^8).
-// Lanes, then waves (through LDS), are merged by the log-sum-exp rule.
+//    max exceeds the running max by more than 2^8). pa_decode_mfma_wave runs
+//    the same tile code with one item per wave, for partitions of at most
+//    kWaveSlice blocks; pa_decode_mfma shares an item among the workgroup's
+//    waves, for longer partitions.
+// Lanes, then (workgroup items) waves through LDS, are merged by the
+// log-sum-exp rule.
 // A sequence that fits one partition is written straight to `out`; longer
 // ones leave one (m, l, o) record per partition for the merge kernel.
 
