@@ -934,9 +934,11 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma(DecodeParams p) {
 // workgroup never wait for each other, and an item ends without a
 // cross-wave combine. Items are dealt to the waves of the grid (numbered
 // workgroup-major) in the same largest-first snake. Each wave keeps in LDS
-// its item's table slice and query block (double buffered: the next item's
-// are loaded raw during the current one and stored at its end) and its own
-// result ring, which it flushes itself.
+// its item's table slice and query block and its own result ring, which it
+// flushes itself. The next item's slice and query block are loaded raw
+// during the current item and stored over the current ones at its end,
+// when the tile loop no longer reads the slice and the query fragments are
+// in registers.
 
 __host__ __device__ constexpr int wave_q_words(int g, int d) { return ((g * d / 2) + 3) & ~3; }
 
@@ -955,16 +957,16 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma_wave(DecodeParams p) 
     constexpr float kLazy = 8.f;
     constexpr int SL = ring_slot_floats(G, D);
 
-    // LDS: schedule | tbl[kWaves][2][kWaveSlice] | qs[kWaves][2][QWP] | ring[kWaves][wring]
+    // LDS: schedule | tbl[kWaves][kWaveSlice] | qs[kWaves][QWP] | ring[kWaves][wring]
     extern __shared__ __align__(16) unsigned char smem[];
     Sched sc = sched_lds(p, reinterpret_cast<int*>(smem));
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int* tbl_all = reinterpret_cast<int*>(smem) + sched_ints(p.num_seqs);
-    uint32_t* qs_all = reinterpret_cast<uint32_t*>(tbl_all + kWaves * 2 * kWaveSlice);
-    float* ring_all = reinterpret_cast<float*>(qs_all + kWaves * 2 * QWP);
+    uint32_t* qs_all = reinterpret_cast<uint32_t*>(tbl_all + kWaves * kWaveSlice);
+    float* ring_all = reinterpret_cast<float*>(qs_all + kWaves * QWP);
     const int wring = p.ring_slots / kWaves;
-    int* tbl2 = tbl_all + wave * 2 * kWaveSlice;
-    uint32_t* qs2 = qs_all + wave * 2 * QWP;
+    int* tbl = tbl_all + wave * kWaveSlice;
+    uint32_t* qs = qs_all + wave * QWP;
     float* ring = ring_all + wave * wring * SL;
     int nring = 0;
 
@@ -1049,19 +1051,17 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma_wave(DecodeParams p) 
     Item cur = item_at(p, sc, item0);
     int next_item = wave_item(1);
     Item nxt = next_item >= 0 ? item_at(p, sc, next_item) : cur;
-    stage_slice(cur, tbl2);
-    for (int w = lane; w < QW; w += 64) qs2[w] = qwords[q_word0(cur) + w];
+    stage_slice(cur, tbl);
+    for (int w = lane; w < QW; w += 64) qs[w] = qwords[q_word0(cur) + w];
     Buf A, B;
     {
         int pk = 0, pv = 0;
         const bool real = ntiles_of(cur) > 0;
-        if (real) tile_blocks(cur, tbl2, 0, pk, pv);
+        if (real) tile_blocks(cur, tbl, 0, pk, pv);
         load_with(cur, 0, pk, pv, A);
     }
 
     for (int k = 0;; ++k) {
-        const int buf = k & 1;
-        const int* tbl = tbl2 + buf * kWaveSlice;
         const bool has_next = next_item >= 0;
         const bool next_tile = has_next && ntiles_of(nxt) > 0;
         // raw loads of the next item's metadata, consumed at the end
@@ -1085,7 +1085,7 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma_wave(DecodeParams p) 
 
         u32x4 qf[NK];
         {
-            const uint32_t* qrow = qs2 + buf * QWP + (r16 % G) * (D / 2);
+            const uint32_t* qrow = qs + (r16 % G) * (D / 2);
 #pragma unroll
             for (int c = 0; c < NK; ++c) qf[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c + 4 * j);
         }
@@ -1202,9 +1202,9 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma_wave(DecodeParams p) 
         // the next item's table slice and query block (unconditional stores:
         // every path consumes the raw loads)
 #pragma unroll
-        for (int i = 0; i < TPL; ++i) tbl2[(buf ^ 1) * kWaveSlice + lane + 64 * i] = clamp_pid(tbl_raw[i]);
+        for (int i = 0; i < TPL; ++i) tbl[lane + 64 * i] = clamp_pid(tbl_raw[i]);
 #pragma unroll
-        for (int i = 0; i < QPL; ++i) qs2[(buf ^ 1) * QWP + min(lane + 64 * i, QW - 1)] = q_raw[i];
+        for (int i = 0; i < QPL; ++i) qs[min(lane + 64 * i, QW - 1)] = q_raw[i];
         ++nring;
         if (nring == wring || !has_next) {
             for (int i = 0; i < nring; ++i) {
@@ -1367,20 +1367,25 @@ hipError_t launch_valu(const DecodeParams& p, int num_cus, hipStream_t stream) {
 }
 
 size_t decode_smem_mfma_wave(int num_seqs, int d, int g) {
-    // prefix | per wave: two table slices, two query blocks
-    return (sched_ints(num_seqs) + static_cast<size_t>(kWaves) * 2 * kWaveSlice) * sizeof(int) +
-           static_cast<size_t>(kWaves) * 2 * wave_q_words(g, d) * sizeof(uint32_t);
+    // prefix | per wave: a table slice and a query block
+    return (sched_ints(num_seqs) + static_cast<size_t>(kWaves) * kWaveSlice) * sizeof(int) +
+           static_cast<size_t>(kWaves) * wave_q_words(g, d) * sizeof(uint32_t);
 }
 
 template <int DT, int D, int G>
 hipError_t launch_mfma(const DecodeParams& p, int num_cus, hipStream_t stream) {
     if ((p.part >> p.log2_bs) <= kWaveSlice) {
         const size_t fixed = decode_smem_mfma_wave(p.num_seqs, D, G);
-        if ((1 << p.log2_bs) >= 16)
-            return launch_persistent(pa_decode_mfma_wave<DT, D, G, true>, p, fixed, D, G, num_cus, kMfmaWgPerCu,
-                                     stream, kWaves);
-        return launch_persistent(pa_decode_mfma_wave<DT, D, G, false>, p, fixed, D, G, num_cus, kMfmaWgPerCu,
-                                 stream, kWaves);
+        const hipError_t e =
+            (1 << p.log2_bs) >= 16
+                ? launch_persistent(pa_decode_mfma_wave<DT, D, G, true>, p, fixed, D, G, num_cus, kMfmaWgPerCu,
+                                    stream, kWaves)
+                : launch_persistent(pa_decode_mfma_wave<DT, D, G, false>, p, fixed, D, G, num_cus, kMfmaWgPerCu,
+                                    stream, kWaves);
+        // hipErrorInvalidConfiguration: the four waves' buffers and rings do
+        // not fit next to this batch's schedule (nothing was launched); one
+        // item per workgroup needs less LDS
+        if (e != hipErrorInvalidConfiguration) return e;
     }
     const size_t fixed = decode_smem_mfma(p.num_seqs, D, G);
     if ((1 << p.log2_bs) >= 16)
