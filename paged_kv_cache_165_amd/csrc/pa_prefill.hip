@@ -292,6 +292,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             return trow[tid < ntb ? e : 0];
         };
         auto head_el = [&](int pid) { return (static_cast<size_t>(pid) * hkv + kv) * blk_el; };
+        // byte address of (block pid, this KV head) for a wave-uniform pid:
+        // one 32 x 32 -> 64-bit product on the scalar unit (a block's heads
+        // span hkv * B * D * E < 2^32 bytes)
+        const uint32_t blk_bytes = static_cast<uint32_t>(hkv * blk_el * E);
+        const char* kbase_kv = kbase + kv * blk_el * E;
+        const char* vbase_kv = vbase + kv * blk_el * E;
+        auto head_bytes = [&](int pid) {
+            return static_cast<uint64_t>(static_cast<uint32_t>(pid)) * blk_bytes;
+        };
 
         // Static part of this lane's loads. LDS row r of K holds key
         // 32 (r / 32) + 8 ((r % 16) / 4) + 4 ((r / 16) % 2) + r % 4 of the tile,
@@ -337,20 +346,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     const int sub = (wave * SH::UV + i) * 1024 / (D * 32);
                     vpid[i] = tb[(min(t0 + 16 * sub, lastk & ~15) >> lb) - blk0];
                 }
+                // a wave-uniform block base plus a 32-bit lane offset, the
+                // form the load takes with its base in scalar registers
 #pragma unroll
                 for (int i = 0; i < SH::UK; ++i) {
                     const int pid = __builtin_amdgcn_readfirstlane(kpid[i]);
+                    const char* blk = kbase_kv + head_bytes(pid);
                     const int key = min(t0 + k_key(i), lastk);
-                    const char* src = kbase + (head_el(pid) + static_cast<size_t>(key & (bs - 1)) * D) * E + k_chb(i);
-                    dma<16>(src, bk + (wave * SH::UK + i) * 1024);
+                    const uint32_t off = static_cast<uint32_t>((key & (bs - 1)) * (D * E) + k_chb(i));
+                    dma<16>(blk + off, bk + (wave * SH::UK + i) * 1024);
                 }
 #pragma unroll
                 for (int i = 0; i < SH::UV; ++i) {
                     const int sub = (wave * SH::UV + i) * 1024 / (D * 32);
                     const int key = min(t0 + 16 * sub, lastk & ~15);
                     const int pid = __builtin_amdgcn_readfirstlane(vpid[i]);
-                    const size_t el = head_el(pid) + static_cast<size_t>((key & (bs - 1)) >> 4) * D * 16;
-                    dma<16>(vbase + el * E + v_d(i) * 32 + v_half(i) * 16, bv + (wave * SH::UV + i) * 1024);
+                    const char* blk = vbase_kv + head_bytes(pid) + static_cast<uint32_t>(((key & (bs - 1)) >> 4) * D * 16 * E);
+                    const uint32_t off = static_cast<uint32_t>(v_d(i) * 32 + v_half(i) * 16);
+                    dma<16>(blk + off, bv + (wave * SH::UV + i) * 1024);
                 }
             } else {
 #pragma unroll
