@@ -78,6 +78,24 @@ struct PrefillShape {
 template <int D>
 constexpr int prefill_query_tile(int g) { return kWaves * 16 * PrefillShape<D>::NC / g; }
 
+// Key (within the tile) that LDS row r of K holds: the rows of a 32-key
+// group are permuted so that each lane's eight S^T scores are eight
+// consecutive keys.
+__host__ __device__ constexpr int k_key_of_row(int r) {
+    return 32 * (r >> 5) + 8 * ((r & 15) >> 2) + 4 * ((r >> 4) & 1) + (r & 3);
+}
+
+// First LDS row of K load instruction i of wave w when every block holds
+// whole 16-key groups: wave w fills exactly the rows of keys KT/4 * w ..
+// KT/4 * (w + 1) - 1 (16 keys, 8 at D = 256), so all its K loads (and its
+// V loads, the 16-key tile holding those keys) read one block.
+template <int D>
+__host__ __device__ constexpr int k_row0(int w, int i) {
+    if constexpr (D == 64) return 32 * (w >> 1) + 16 * i + 8 * (w & 1);
+    else if constexpr (D == 128) return 32 * (w >> 1) + 16 * (i >> 1) + 8 * (w & 1) + 4 * (i & 1);
+    else return 16 * (i >> 1) + 4 * w + 2 * (i & 1);
+}
+
 template <int D>
 constexpr size_t prefill_smem() {
     return 2 * static_cast<size_t>(PrefillShape<D>::BUF_BYTES) + 2 * PrefillShape<D>::TBL * sizeof(int);
@@ -332,38 +350,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const int t0 = kt * KT;
             const int blk0 = t0 >> lb;
             if (big) {
-                // one block per load instruction: its id is wave-uniform. All
-                // ids are read from LDS first, then the loads are issued.
-                int kpid[SH::UK], vpid[SH::UV];
+                // This wave's keys (one aligned 16-key group, 8 keys at
+                // D = 256) and their V tile lie in one block: one id, read
+                // from LDS once, and wave-uniform bases. Keys past the
+                // context are read from the block that holds the last key
+                // (in bounds; masked: scores to -inf, V to zero).
+                constexpr int KPW = KT / kWaves;
+                const int g0 = t0 + KPW * wave;
+                const int pid = __builtin_amdgcn_readfirstlane(tb[(min(g0, lastk) >> lb) - blk0]);
+                const char* blk = kbase_kv + head_bytes(pid);
+                const uint32_t k0 = static_cast<uint32_t>((g0 & (bs - 1)) * (D * E));
 #pragma unroll
                 for (int i = 0; i < SH::UK; ++i) {
-                    const int g16 = (wave * SH::UK + i) * 1024 / ROWB;  // first LDS row of the instruction
-                    const int gkey = min(t0 + 32 * (g16 >> 5) + 4 * ((g16 >> 4) & 1) + 8 * ((g16 & 15) >> 2), lastk);
-                    kpid[i] = tb[(gkey >> lb) - blk0];
+                    const int r0 = k_row0<D>(wave, i);
+                    const int r = r0 + lane * 16 / ROWB;
+                    const int ch = ((lane * 16) % ROWB >> 4) ^ k_swz<D>(r);
+                    const uint32_t off = k0 + static_cast<uint32_t>((k_key_of_row(r) - KPW * wave) * (D * E) + ch * 16);
+                    dma<16>(blk + off, bk + r0 * ROWB);
                 }
+                const char* vblk = vbase_kv + head_bytes(pid);
 #pragma unroll
                 for (int i = 0; i < SH::UV; ++i) {
                     const int sub = (wave * SH::UV + i) * 1024 / (D * 32);
-                    vpid[i] = tb[(min(t0 + 16 * sub, lastk & ~15) >> lb) - blk0];
-                }
-                // a wave-uniform block base plus a 32-bit lane offset, the
-                // form the load takes with its base in scalar registers
-#pragma unroll
-                for (int i = 0; i < SH::UK; ++i) {
-                    const int pid = __builtin_amdgcn_readfirstlane(kpid[i]);
-                    const char* blk = kbase_kv + head_bytes(pid);
-                    const int key = min(t0 + k_key(i), lastk);
-                    const uint32_t off = static_cast<uint32_t>((key & (bs - 1)) * (D * E) + k_chb(i));
-                    dma<16>(blk + off, bk + (wave * SH::UK + i) * 1024);
-                }
-#pragma unroll
-                for (int i = 0; i < SH::UV; ++i) {
-                    const int sub = (wave * SH::UV + i) * 1024 / (D * 32);
-                    const int key = min(t0 + 16 * sub, lastk & ~15);
-                    const int pid = __builtin_amdgcn_readfirstlane(vpid[i]);
-                    const char* blk = vbase_kv + head_bytes(pid) + static_cast<uint32_t>(((key & (bs - 1)) >> 4) * D * 16 * E);
-                    const uint32_t off = static_cast<uint32_t>(v_d(i) * 32 + v_half(i) * 16);
-                    dma<16>(blk + off, bv + (wave * SH::UV + i) * 1024);
+                    const uint32_t off = static_cast<uint32_t>((((t0 + 16 * sub) & (bs - 1)) >> 4) * (D * 16 * E) +
+                                                               v_d(i) * 32 + v_half(i) * 16);
+                    dma<16>(vblk + off, bv + (wave * SH::UV + i) * 1024);
                 }
             } else {
 #pragma unroll
