@@ -563,7 +563,7 @@ def main():
         "unique_kv_bytes": unique,
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "wall_ms_per_step": round(1e3 * t_wall / args.steps, 5),
-        "roofline": {"bound": "hbm", "kernel": "pa_decode_partitions (pa_decode_mfma / pa_decode_valu)",
+        "roofline": {"bound": "hbm", "kernel": "pa_decode_partitions (pa_decode_mfma_wave / pa_decode_mfma / pa_decode_valu)",
                      "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_us_mean": round(part_us, 2),
