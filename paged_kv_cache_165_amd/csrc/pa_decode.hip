@@ -54,12 +54,6 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kTblPerThread = kMaxTableSlice / kThreads;  // table entries each thread stages
 static_assert(kTblPerThread * kThreads == kMaxTableSlice, "whole table entries per thread");
 
-// Workgroups per compute unit of the persistent grid; 0 = as many as the
-// kernel's occupancy allows.
-#ifndef PA_WG_PER_CU
-#define PA_WG_PER_CU 0
-#endif
-
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -1336,7 +1330,6 @@ hipError_t launch_persistent(K kern, DecodeParams p, size_t fixed_smem, int d, i
     if (e != hipSuccess) return e;
     if (occ < 1) occ = 1;
     if (max_per_cu > 0 && occ > max_per_cu) occ = max_per_cu;
-    if (PA_WG_PER_CU > 0 && occ > PA_WG_PER_CU) occ = PA_WG_PER_CU;
     p.ring_slots = ring_slots_for(static_lds + fixed_smem, d, g, occ) / ring_multiple * ring_multiple;
     if (p.ring_slots < 1) return hipErrorInvalidConfiguration;
     const size_t smem = fixed_smem + static_cast<size_t>(p.ring_slots) * ring_slot_floats(g, d) * sizeof(float);

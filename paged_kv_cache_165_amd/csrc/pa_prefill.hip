@@ -57,11 +57,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // Tile geometry for one head_dim.
 template <int D>
 struct PrefillShape {
-#ifndef PA_PREFILL_NC
     static constexpr int NC = D >= 256 ? 1 : 2;    // 16-column blocks per wave
-#else
-    static constexpr int NC = D >= 256 ? 1 : PA_PREFILL_NC;
-#endif
     static constexpr int KT = D >= 256 ? 32 : 64;   // keys per LDS tile
     static constexpr int ROWB = D * 2;              // bytes of one K row
     static constexpr int K_BYTES = KT * ROWB;       // K of a tile

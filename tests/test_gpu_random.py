@@ -1,0 +1,126 @@
+"""Seeded random configurations of decode and prefill against the float64
+oracle: the shape choices the fixed cases do not combine (batch, group,
+head_dim, block size, element type, partition, lengths with block-boundary
+and partition-boundary values, scale sign) drawn from one generator, each
+compared element by element. Every slot a sequence may not see holds NaN."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from harness import ORACLE_DTYPE, compare_attention, host_bits, log
+from workloads import prefill as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+DTYPES = [torch.float32, torch.bfloat16, torch.float16]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_165_amd as pa
+    pa.library()
+
+
+def _decode_case(rng):
+    dt = DTYPES[rng.integers(3)]
+    d = int(rng.choice([64, 128, 256]))
+    groups = [1, 2, 4, 8] + ([16] if dt != torch.float32 else [])
+    g = int(rng.choice(groups))
+    hkv = int(rng.choice([1, 2, 3]))
+    bs = int(rng.choice([4, 8, 16, 32, 64]))
+    # the smallest block this element type, head_dim and group support
+    # (pa_decode rejects smaller ones with PA_ERR_UNSUPPORTED)
+    e = 4 if dt == torch.float32 else 2
+    if not (dt != torch.float32 and g >= 2):
+        lpr = d // (16 // e)
+        rpi = 64 // lpr
+        u = 4 if rpi >= 4 else 16 // rpi
+        bs = max(bs, rpi, u)
+    s = int(rng.integers(1, 12))
+    special = [1, bs - 1, bs, bs + 1, 16, 512, 513, 2048]
+    lens = [int(rng.choice(special)) if rng.random() < 0.4 else int(rng.integers(0, 3000)) for _ in range(s)]
+    part = int(rng.choice([0, 0, 256, 1024, 2048])) if max(lens) > 0 else 0
+    if part and part % bs:
+        part = 0
+    scale = float(rng.choice([1.0, -1.0])) / np.sqrt(d)
+    return dt, d, g, hkv, bs, lens, part, scale
+
+
+def _make_decode(dt, d, g, hkv, bs, lens, seed):
+    rng = np.random.default_rng(seed)
+    need = [-(-L // bs) for L in lens]
+    nb = max(sum(need) + 2, int(sum(need) * 1.3) + 2)
+    perm = rng.permutation(nb)
+    trap = int(perm[-1])
+    maxb = max(max(need), 1)
+    tables = np.full((len(lens), maxb), trap, np.int32)
+    valid = np.zeros((nb, bs), bool)
+    k = 0
+    for i, (L, n) in enumerate(zip(lens, need)):
+        tables[i, :n] = perm[k:k + n]
+        k += n
+        t = np.arange(L)
+        valid[tables[i, t // bs], t % bs] = True
+    gen = torch.Generator(device=DEV).manual_seed(seed)
+    rn = lambda *sh: torch.randn(*sh, generator=gen, device=DEV).to(dt)
+    tv = min(bs, 16)
+    q = rn(len(lens), hkv * g, d)
+    kc = rn(nb, hkv, bs, d)
+    vc = rn(nb, hkv, bs // tv, d, tv)
+    m = torch.from_numpy(valid).to(DEV)
+    nan = torch.full((), float("nan"), dtype=dt, device=DEV)
+    kc = torch.where(m.view(nb, 1, bs, 1), kc, nan).contiguous()
+    vc = torch.where(m.view(nb, 1, bs // tv, 1, tv), vc, nan).contiguous()
+    return q, kc, vc, tables
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_decode_matches_oracle(seed):
+    import paged_kv_cache_165_amd as pa
+    rng = np.random.default_rng(9000 + seed)
+    dt, d, g, hkv, bs, lens, part, scale = _decode_case(rng)
+    log(f"[random decode {seed}] {dt} D{d} g{g} hkv{hkv} B{bs} part {part} scale {scale:+.4f} lens {lens}")
+    q, kc, vc, tables = _make_decode(dt, d, g, hkv, bs, lens, 9100 + seed)
+    out = torch.full_like(q, 3.0)
+    pa.decode(out, q, kc, vc, torch.from_numpy(tables).to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV),
+              scale, max_context_len=max(lens), partition_size=part)
+    torch.cuda.synchronize()
+    ref = oracle.paged_decode(host_bits(q), host_bits(kc), host_bits(vc), tables, np.array(lens, np.int32), scale,
+                              bs, ORACLE_DTYPE[dt])
+    compare_attention(out, ref, f"random decode {seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_prefill_matches_oracle(seed):
+    import paged_kv_cache_165_amd as pa
+    rng = np.random.default_rng(9500 + seed)
+    dt = ["bf16", "f16", "f32"][rng.integers(3)]
+    d = int(rng.choice([64, 128, 256]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    bs = int(rng.choice([4, 8, 16, 32, 64]))
+    if dt == "f32" and d == 256 and bs < 16:
+        bs = 16
+    s = int(rng.integers(1, 6))
+    lens, news = [], []
+    for _ in range(s):
+        L = int(rng.integers(0, 700))
+        lens.append(L)
+        news.append(int(rng.integers(0, L + 1)) if L else 0)
+    w = P.make(f"random-{seed}", lens, news, num_heads=2 * g, num_kv_heads=2, head_dim=d, block_size=bs, dtype=dt,
+               seed=9600 + seed, scale=float(rng.choice([1.0, -1.0])) / np.sqrt(d))
+    log(f"[random prefill {seed}] {dt} D{d} g{g} B{bs} lens {lens} new {news}")
+    v = P.make_values(w, device=DEV)
+    if w.num_tokens == 0:
+        return
+    out = torch.full_like(v["q"], float("nan"))
+    pa.prefill(out, v["q"], v["k_cache"], v["v_cache"], torch.from_numpy(w.block_tables).to(DEV),
+               torch.from_numpy(w.context_lens).to(DEV), torch.from_numpy(w.query_start).to(DEV), w.scale,
+               max_query_len=w.max_query_len, max_context_len=w.max_context_len)
+    torch.cuda.synchronize()
+    ref = oracle.paged_prefill(host_bits(v["q"]), host_bits(v["k_cache"]), host_bits(v["v_cache"]), w.block_tables,
+                               w.context_lens, w.query_start, w.scale, w.block_size, ORACLE_DTYPE[v["q"].dtype])
+    compare_attention(out, ref, f"random prefill {seed}")
