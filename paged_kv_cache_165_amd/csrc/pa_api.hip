@@ -437,6 +437,15 @@ pa_status_t pa_prefill(void* out, const void* q, const void* k_cache, const void
     p.num_tokens = num_tokens;
     p.log2_bs = log2i(block_size);
     p.log2_vt = log2i(pa::v_tile_tokens(block_size));
+    // The K/V rows the batch attends to, at most: when they cannot stay in
+    // half of MI355X's 256 MB last-level cache, the query tiles of one
+    // (sequence, KV head) pair are kept together on one XCD so that they
+    // share its L2 (measured: 503 against 589 us on 32 chunks of 512 tokens
+    // after histories of up to 3072; whole 2048-token prompts, whose 67 MB
+    // stay cached, run about 3 % faster tile-major).
+    const double kv_bound = static_cast<double>(num_seqs) * num_kv_heads * max_context_len * head_dim *
+                            elem_bytes(dtype) * 2.0;
+    p.pair_major = kv_bound > 128.0 * (1 << 20) ? 1 : 0;
     hipError_t e = pa::launch_prefill(p, dtype, head_dim, group, static_cast<hipStream_t>(stream));
     if (e == hipErrorInvalidConfiguration)
         return fail(PA_ERR_UNSUPPORTED, "num_seqs %d x num_kv_heads %d x query tiles of max_query_len %d "

@@ -66,6 +66,7 @@ struct PrefillParams {
     int num_tokens;     // rows of q and out
     int log2_bs;
     int log2_vt;
+    int pair_major;     // 1: each XCD runs all query tiles of a (sequence, KV head) pair together
 };
 
 // Tokens per transposed V tile: V rows of a block are stored as tiles of

@@ -74,6 +74,8 @@ struct PrefillShape {
 template <int D>
 constexpr int prefill_query_tile(int g) { return kWaves * 16 * PrefillShape<D>::NC / g; }
 
+constexpr int kXcds = 8;  // XCDs of MI355X, which take consecutive workgroup ids in turn
+
 // Key (within the tile) that LDS row r of K holds: the rows of a 32-key
 // group are permuted so that each lane's eight S^T scores are eight
 // consecutive keys.
@@ -220,12 +222,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, j = lane >> 4;
 
-    // ---- the item: query tile kq (counted from the end), sequence, KV head
+    // ---- the item: query tile kq (counted from the end), sequence, KV head.
+    // Tile-major by default: the last tile of every pair (the most keys)
+    // first. Workgroup ids go to the XCDs in turn; with pair_major set and
+    // the (sequence, KV head) pairs splitting evenly over the XCDs, each XCD
+    // takes whole pairs instead, one after the other with all query tiles of
+    // a pair in a row (its last tile first): the tiles of a pair run side by
+    // side on one XCD and read the pair's K/V rows through that XCD's L2
+    // instead of each from memory.
     const int per_tile = p.num_seqs * p.num_kv_heads;
-    const int kq = blockIdx.x / per_tile;
-    const int rest = blockIdx.x - kq * per_tile;
-    const int s = rest / p.num_kv_heads;
-    const int kv = rest - s * p.num_kv_heads;
+    int kq, pair;
+    if (p.pair_major && per_tile % kXcds == 0) {
+        const int tiles = gridDim.x / per_tile;
+        const int k = blockIdx.x / kXcds;  // index on this XCD
+        const int pl = k / tiles;
+        kq = k - pl * tiles;
+        pair = blockIdx.x % kXcds + kXcds * pl;
+    } else {
+        kq = blockIdx.x / per_tile;
+        pair = blockIdx.x - kq * per_tile;
+    }
+    const int s = pair / p.num_kv_heads;
+    const int kv = pair - s * p.num_kv_heads;
 
     int L = p.context_lens[s];
     L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
