@@ -299,8 +299,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr uint32_t kOne2 = DT == PA_BF16 ? 0x3f803f80u : 0x3c003c00u;  // two 1.0 elements
     const u32x4 ones = r16 == 0 ? u32x4{kOne2, kOne2, kOne2, kOne2} : u32x4{0u, 0u, 0u, 0u};
     float m_run[NC];  // running max of the scaled logits, log2 units
+    float thr[NC];    // (m_run + 8) / scale: unscaled logits above it trigger a rescale
 #pragma unroll
-    for (int n = 0; n < NC; ++n) m_run[n] = kFloor;
+    for (int n = 0; n < NC; ++n) {
+        m_run[n] = kFloor;
+        thr[n] = (kFloor + kLazy) / sc;
+    }
 
     if (nkt > 0) {
         const int lb = p.log2_bs;
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
         // Issue the loads of tile kt into buffer `buf`; keys past the context
         // are read at the last key's position (their values are masked).
-        auto issue = [&](int kt, int buf) {
+        auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
             unsigned char* bk = lds + buf * SH::BUF_BYTES;
             unsigned char* bv = bk + SH::K_BYTES;
             const int* tb = tbl + (kt & 1) * SH::TBL;
@@ -497,27 +501,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // online softmax: the probabilities are computed against the current
         // running max first (valid whenever it does not grow by more than
         // 2^8, which is the lazy-rescale rule) and only recomputed, after the
-        // accumulators are rescaled, in the rare step where it does
-        auto softmax = [&](const f32x4_t (&st)[2][NC], u32x4 (&pb)[NC], float (&tmax)[NC], bool& need_any) {
+        // accumulators are rescaled, in the rare step where it does. Whether
+        // it does is decided on each lane's own eight logits against
+        // thr = (m_run + 8) / scale: a column's max passes the threshold iff
+        // one of its four lanes does, so the cross-lane max is only needed
+        // in that rare step.
+        auto softmax = [&](const f32x4_t (&st)[2][NC], u32x4 (&pb)[NC], float (&tl)[NC], bool& need_any) {
             need_any = false;
 #pragma unroll
             for (int n = 0; n < NC; ++n) {
                 const f32x4_t a = st[0][n], b = st[1][n];
-                const float t = max3(max3(a[0], a[1], a[2]), max3(a[3], b[0], b[1]), max3(b[2], b[3], -INFINITY));
-                tmax[n] = column_max(t) * sc;
-                need_any |= tmax[n] > m_run[n] + kLazy;
+                tl[n] = max3(max3(a[0], a[1], a[2]), max3(a[3], b[0], b[1]), max3(b[2], b[3], -INFINITY));
+                need_any |= tl[n] > thr[n];
             }
             exps(st, pb);
         };
-        auto rescale = [&](const f32x4_t (&st)[2][NC], u32x4 (&pb)[NC], const float (&tmax)[NC]) {
+        auto rescale = [&](const f32x4_t (&st)[2][NC], u32x4 (&pb)[NC], const float (&tl)[NC]) {
 #pragma unroll
             for (int n = 0; n < NC; ++n) {
-                const float mn = tmax[n] > m_run[n] + kLazy ? tmax[n] : m_run[n];
+                const float tmax = column_max(tl[n]) * sc;
+                const float mn = tmax > m_run[n] + kLazy ? tmax : m_run[n];
                 const float alpha = fast_exp2(m_run[n] - mn);
 #pragma unroll
                 for (int v = 0; v < NV; ++v) acc[n][v] *= alpha;
                 accl[n] *= alpha;
                 m_run[n] = mn;
+                thr[n] = (mn + kLazy) / sc;
             }
             exps(st, pb);
         };
@@ -559,15 +568,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (1 < nkt) issue(1, 1);
         treg = lookup(min(2, nkt - 1));
 
-        f32x4_t st_cur[2][NC], st_nxt[2][NC];
+        f32x4_t st_a[2][NC], st_b[2][NC];
         u32x4 vf[NV];
         {
             u32x4 kf[2][NK];
             read_k(0, kf);
-            qk(kf, st_cur);
+            qk(kf, st_a);
             read_v(0, vf);
         }
-        for (int g = 0; g < nsteps; ++g) {
+        // Every wave runs every step (a step past a wave's own positions is
+        // fully masked and adds nothing), so that a step is one straight run
+        // in which the products of step g + 1 (the last step repeats its own)
+        // are in flight during the softmax of step g. The loop is unrolled
+        // by two so that the two score buffers trade roles instead of being
+        // copied.
+        auto step = [&](int g, f32x4_t (&st_cur)[2][NC], f32x4_t (&st_nxt)[2][NC]) __attribute__((always_inline)) {
             const int g1 = g + 1;
             if (g1 < nsteps && g1 % SPT == 0) {
                 // step g + 1 starts tile t1: wait for it, then reuse the
@@ -579,26 +594,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 if (t1 + 1 < nkt) issue(t1 + 1, (t1 + 1) & 1);
                 treg = lookup(min(t1 + 2, nkt - 1));
             }
-            // Every wave runs every step (a step past a wave's own positions
-            // is fully masked and adds nothing), so that the step below is
-            // one straight run in which the products of step g + 1 (the last
-            // step repeats its own) are in flight during the softmax of step g.
             const int gn = g1 < nsteps ? g1 : g;
             mask(g, st_cur);
             u32x4 kf[2][NK];
             read_k(gn, kf);
             qk(kf, st_nxt);
             u32x4 pb[NC];
-            float tmax[NC];
+            float tl[NC];
             bool need_any;
-            softmax(st_cur, pb, tmax, need_any);
-            if (__any(need_any)) rescale(st_cur, pb, tmax);
+            softmax(st_cur, pb, tl, need_any);
+            if (__any(need_any)) rescale(st_cur, pb, tl);
             pv(g, vf, pb);
             read_v(gn, vf);
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int n = 0; n < NC; ++n) st_cur[tt][n] = st_nxt[tt][n];
+        };
+        for (int g = 0; g < nsteps; g += 2) {
+            step(g, st_a, st_b);
+            if (g + 1 < nsteps) step(g + 1, st_b, st_a);
         }
     }
 
