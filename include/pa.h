@@ -11,6 +11,8 @@
  *   pa_copy_blocks  whole-block copies, the copy half of copy-on-write;
  *   pa_append_block_tables  record each sequence's newest block in its
  *                   device block-table row after a decode append.
+ *   pa_append_block_tables_host  the same, taking the step's lengths and
+ *                   slots from host memory in the launch arguments.
  *
  * Pages the operations are defined by (cited below by short name):
  *   [aiqz]     aiqz.cc/article/paged-attention-mechanism.html (PagedAttention
@@ -60,7 +62,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 7
+#define PA_ABI_VERSION 8
 
 typedef enum pa_dtype {
     PA_F32 = 0,  /* IEEE binary32 */
@@ -289,6 +291,22 @@ pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_
  */
 pa_status_t pa_append_block_tables(int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
                                    const int32_t* slot_mapping, int num_seqs, int block_size, void* stream);
+
+/*
+ * pa_append_block_tables with the step's lengths and slots read from HOST
+ * memory: host_context_lens and host_slot_mapping (int32 [num_seqs], any host
+ * memory) are read during the call and reach the device inside the kernel's
+ * launch arguments, so no copy command or staging buffer is involved and the
+ * caller may reuse both arrays as soon as the call returns. The kernel also
+ * stores them to context_lens_out and slot_mapping_out (int32 [num_seqs],
+ * device memory), where the step's cache write and decode read them. Same
+ * table update, argument rules and errors as pa_append_block_tables (the
+ * host arrays need no particular alignment); one launch per 448 sequences.
+ */
+pa_status_t pa_append_block_tables_host(int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* host_context_lens, const int32_t* host_slot_mapping,
+                                        int32_t* context_lens_out, int32_t* slot_mapping_out, int num_seqs,
+                                        int block_size, void* stream);
 
 pa_status_t pa_write_cache_layers(const void* k, const void* v, void* k_cache, void* v_cache,
                                   const int32_t* slot_mapping, int num_tokens, int num_layers,

@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import ctypes
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -31,7 +32,7 @@ from . import _lib
 __all__ = [
     "PaError", "library", "default_partition_size", "workspace_size", "alloc_workspace",
     "v_tile", "v_cache_shape", "alloc_cache",
-    "decode", "decode_partitions", "decode_merge", "append_block_tables", "prefill", "write_cache", "copy_blocks",
+    "decode", "decode_partitions", "decode_merge", "append_block_tables", "append_block_tables_host", "prefill", "write_cache", "copy_blocks",
     "alloc_cache_layers", "write_cache_layers", "copy_blocks_layers",
 ]
 
@@ -260,6 +261,38 @@ def append_block_tables(block_tables, context_lens, slot_mapping, block_size: in
         raise ValueError("one context length and one slot per table row")
     _check(library().pa_append_block_tables(block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
                                             slot_mapping.data_ptr(), n, int(block_size), _stream(block_tables)))
+
+
+def _host_int32(a, name: str) -> np.ndarray:
+    if isinstance(a, torch.Tensor):
+        if a.device.type != "cpu":
+            raise ValueError(f"{name} must be in host memory")
+        a = a.numpy()
+    a = np.asarray(a)
+    if a.dtype != np.int32 or a.ndim != 1:
+        raise ValueError(f"{name} must be a 1-D int32 host array")
+    return np.ascontiguousarray(a)
+
+
+def append_block_tables_host(block_tables, context_lens, slot_mapping, context_lens_out, slot_mapping_out,
+                             block_size: int):
+    """``append_block_tables`` with the lengths and slots given as host int32
+    arrays (``pa_append_block_tables_host``): they travel in the launch
+    arguments, are stored to the device tensors ``context_lens_out`` and
+    ``slot_mapping_out``, and the host arrays may be reused as soon as this
+    returns."""
+    _dev_tensor(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev_tensor(context_lens_out, "context_lens_out", dtype=torch.int32, ndim=1)
+    _dev_tensor(slot_mapping_out, "slot_mapping_out", dtype=torch.int32, ndim=1)
+    lens = _host_int32(context_lens, "context_lens")
+    slots = _host_int32(slot_mapping, "slot_mapping")
+    n = block_tables.shape[0]
+    if lens.shape[0] != n or slots.shape[0] != n or context_lens_out.shape[0] != n or slot_mapping_out.shape[0] != n:
+        raise ValueError("one context length and one slot per table row")
+    _check(library().pa_append_block_tables_host(block_tables.data_ptr(), block_tables.shape[1],
+                                                 lens.ctypes.data, slots.ctypes.data, context_lens_out.data_ptr(),
+                                                 slot_mapping_out.data_ptr(), n, int(block_size),
+                                                 _stream(block_tables)))
 
 
 def alloc_cache_layers(num_layers: int, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,

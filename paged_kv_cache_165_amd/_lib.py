@@ -22,7 +22,7 @@ EXPORTED = (
     "pa_abi_version", "pa_status_string", "pa_last_error", "pa_default_partition_size",
     "pa_decode_workspace_size", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
     "pa_prefill", "pa_write_cache", "pa_copy_blocks", "pa_write_cache_layers", "pa_copy_blocks_layers",
-    "pa_append_block_tables",
+    "pa_append_block_tables", "pa_append_block_tables_host",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_prefill", "pa_bm_share", "pa_bm_append", "pa_bm_free",
     "pa_bm_block_tables", "pa_bm_num_free", "pa_bm_blocks_in_use", "pa_bm_refcount", "pa_bm_seq_tokens",
     "pa_bm_blocks_without_sharing", "pa_bm_check",
@@ -76,6 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.pa_copy_blocks_layers.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
         lib.pa_append_block_tables.restype = _i
         lib.pa_append_block_tables.argtypes = [_vp, _i, _vp, _vp, _i, _i, _vp]
+        lib.pa_append_block_tables_host.restype = _i
+        lib.pa_append_block_tables_host.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _vp]
         lib.pa_copy_blocks.restype = _i
         lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
         _i64 = ctypes.c_int64

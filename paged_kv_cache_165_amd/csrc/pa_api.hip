@@ -499,4 +499,23 @@ pa_status_t pa_append_block_tables(int32_t* block_tables, int max_blocks_per_seq
     return PA_OK;
 }
 
+pa_status_t pa_append_block_tables_host(int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* host_context_lens, const int32_t* host_slot_mapping,
+                                        int32_t* context_lens_out, int32_t* slot_mapping_out, int num_seqs,
+                                        int block_size, void* stream) {
+    if (num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_seqs=%d max_blocks_per_seq=%d block_size=%d)",
+                    num_seqs, max_blocks_per_seq, block_size);
+    if (!is_pow2(block_size) || block_size > 256)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two up to 256", block_size);
+    if (num_seqs == 0) return PA_OK;
+    if (!block_tables || !host_context_lens || !host_slot_mapping || !context_lens_out || !slot_mapping_out)
+        return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    hipError_t e = pa::launch_stage_append(block_tables, max_blocks_per_seq, host_context_lens, host_slot_mapping,
+                                           context_lens_out, slot_mapping_out, num_seqs, block_size,
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "table append kernel launch");
+    return PA_OK;
+}
+
 }  // extern "C"

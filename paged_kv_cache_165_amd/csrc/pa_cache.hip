@@ -10,6 +10,9 @@
 // The slot of a token is its (physical block, offset) pair of the block-table
 // equation (aiqz.cc, section 块表映射机制) flattened as pid * B + off.
 
+#include <algorithm>
+#include <cstring>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -163,6 +166,58 @@ hipError_t launch_table_append(int32_t* tables, int max_blocks, const int32_t* l
     hipLaunchKernelGGL(pa_table_append_kernel, dim3(static_cast<unsigned>((num_seqs + 255) / 256)), dim3(256), 0,
                        stream, tables, max_blocks, lens, slots, num_seqs, ilog2(block_size));
     return hipGetLastError();
+}
+
+// The same append with the step's lengths and slots carried in the launch
+// arguments (host values copied into the dispatch's argument buffer by the
+// runtime): each thread stores its sequence's length and slot to the device
+// arrays the step's later kernels read, then updates the table row. One
+// launch covers kStageSeqs sequences.
+struct StageArgs {
+    int32_t* tables;
+    int32_t* lens_out;
+    int32_t* slots_out;
+    int max_blocks;
+    int num_seqs;
+    int log2_bs;
+    int32_t lens[kStageSeqs];
+    int32_t slots[kStageSeqs];
+};
+static_assert(sizeof(StageArgs) <= 4000, "kernel arguments are limited to 4 KB");
+
+__global__ __launch_bounds__(kStageSeqs) void pa_stage_append_kernel(StageArgs a) {
+    const int i = threadIdx.x;
+    if (i >= a.num_seqs) return;
+    const int L = a.lens[i];
+    const int slot = a.slots[i];
+    a.lens_out[i] = L;
+    a.slots_out[i] = slot;
+    if (L <= 0 || slot < 0) return;
+    const int col = (L - 1) >> a.log2_bs;
+    if (col >= a.max_blocks) return;
+    a.tables[static_cast<size_t>(i) * a.max_blocks + col] = slot >> a.log2_bs;
+}
+
+hipError_t launch_stage_append(int32_t* tables, int max_blocks, const int32_t* host_lens,
+                               const int32_t* host_slots, int32_t* lens_out, int32_t* slots_out, int num_seqs,
+                               int block_size, hipStream_t stream) {
+    const int log2_bs = ilog2(block_size);
+    for (int i0 = 0; i0 < num_seqs; i0 += kStageSeqs) {
+        StageArgs a;
+        const int n = std::min(kStageSeqs, num_seqs - i0);
+        a.tables = tables + static_cast<size_t>(i0) * max_blocks;
+        a.lens_out = lens_out + i0;
+        a.slots_out = slots_out + i0;
+        a.max_blocks = max_blocks;
+        a.num_seqs = n;
+        a.log2_bs = log2_bs;
+        std::memcpy(a.lens, host_lens + i0, sizeof(int32_t) * n);
+        std::memcpy(a.slots, host_slots + i0, sizeof(int32_t) * n);
+        hipLaunchKernelGGL(pa_stage_append_kernel, dim3(1), dim3(kStageSeqs), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,

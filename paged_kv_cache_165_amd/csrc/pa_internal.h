@@ -102,6 +102,12 @@ hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void*
                               hipStream_t stream);
 hipError_t launch_table_append(int32_t* tables, int max_blocks, const int32_t* lens, const int32_t* slots,
                                int num_seqs, int block_size, hipStream_t stream);
+// Sequences per launch of the append that carries lengths and slots in its
+// launch arguments (two int32 arrays of this size fit in the 4 KB limit).
+constexpr int kStageSeqs = 448;
+hipError_t launch_stage_append(int32_t* tables, int max_blocks, const int32_t* host_lens,
+                               const int32_t* host_slots, int32_t* lens_out, int32_t* slots_out, int num_seqs,
+                               int block_size, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
                               int num_layers, size_t block_bytes, int num_blocks, hipStream_t stream);
 

@@ -9,13 +9,15 @@ straight into a pinned staging buffer; every byte of K/V is moved and
 reduced by the library's kernels. The block tables stay on the device: when
 a step decodes the same sequences as the step before, the only table entry
 that can change per sequence is the one of its newest token (a new block,
-or a copy-on-write), and pa_append_block_tables writes it from the slot
-mapping on the device. Any other change (a new batch, a prefill, fork or
-free) uploads the tables in full once. The upload runs on a copy stream of
-its own (default priority, ordered against the compute stream by events);
-the few KB of a step with the same sequences go in order on the compute
-stream. Nothing in a step waits for the GPU unless the host is two steps
-ahead.
+or a copy-on-write), and pa_append_block_tables_host writes it from the
+slot on the device. That call also carries the step's lengths and slots in
+its launch arguments, so a step with the same sequences as the step before
+issues no copy at all unless a copy-on-write needs its pairs. Any other
+change (a new batch, a prefill, fork or free) uploads the tables in full
+once, on a copy stream of its own (default priority, ordered against the
+compute stream by events). A step with the same sequences records no event
+at all, and the host waits for the GPU only before it rewrites a staging
+buffer that a copy two steps ago may still be reading.
 """
 
 from __future__ import annotations
@@ -113,15 +115,15 @@ class PagedDecoder:
     def _staging_for(self, n: int):
         """The next staging set, holding at least n sequences: a pinned host
         and a device int32 buffer [slots n | lens n | pairs 2n | tables
-        n * max_blocks], the event after its upload (copy stream) and the
-        event after the kernels that read it (compute stream)."""
+        n * max_blocks], and the event after the last copy that read its host
+        buffer (``pending`` while such a copy may still be queued)."""
         if n > self._cap:
             torch.cuda.synchronize(self.device)  # nothing may still read the old buffers
             cap = max(n, 2 * self._cap)
             words = cap * (4 + self.max_blocks)
             self._staging = [dict(host=torch.empty(words, dtype=torch.int32, pin_memory=True),
                                   dev=torch.empty(words, dtype=torch.int32, device=self.device),
-                                  copied=torch.cuda.Event(), consumed=torch.cuda.Event())
+                                  copied=torch.cuda.Event(), pending=False)
                              for _ in range(2)]
             self._dtables = torch.empty(cap, self.max_blocks, dtype=torch.int32, device=self.device)
             self._lens = np.zeros(cap, np.int32)
@@ -129,7 +131,9 @@ class PagedDecoder:
             self._cap = cap
         st = self._staging[self._turn]
         self._turn ^= 1
-        st["copied"].synchronize()  # the upload that last read the host buffer has run
+        if st["pending"]:
+            st["copied"].synchronize()  # the upload that last read the host buffer has run
+            st["pending"] = False
         return st
 
     def step(self, seqs, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
@@ -152,7 +156,6 @@ class PagedDecoder:
             # every row grew by one token; its newest block follows from its slot
             self._lens[:n] += 1
             lens[:] = self._lens[:n]
-            words = 4 * n
         else:
             tables = h[4 * n:4 * n + n * self.max_blocks].reshape(n, self.max_blocks)
             self.blocks.block_tables_into(s, tables, lens, pad=0)
@@ -160,22 +163,30 @@ class PagedDecoder:
             words = 4 * n + n * self.max_blocks
         compute = torch.cuda.current_stream(self.device)
         if same_rows:
-            # a few KB: in order on the compute stream, which costs less than
-            # a hand-over between two queues
-            dev[:words].copy_(host[:words], non_blocking=True)
-            st["copied"].record(compute)
+            # lengths and slots travel in the table kernel's launch arguments
+            # (below), so the step records no event (a marker between two
+            # kernels costs several microseconds of queue time); only the
+            # pairs of a copy-on-write, rare, need a copy, in order on the
+            # compute stream
+            if npairs:
+                dev[2 * n:2 * n + 2 * npairs].copy_(host[2 * n:2 * n + 2 * npairs], non_blocking=True)
+                st["copied"].record(compute)
+                st["pending"] = True
         else:
-            # the full tables go on the copy stream, which moves them faster
-            self._copy_stream.wait_event(st["consumed"])  # kernels of two steps ago have read dev
+            # the full tables go on the copy stream, which moves them faster,
+            # once every kernel queued so far (those of two steps ago read
+            # this staging set's device buffer) has run
+            self._copy_stream.wait_stream(compute)
             with torch.cuda.stream(self._copy_stream):
                 dev[:words].copy_(host[:words], non_blocking=True)
                 st["copied"].record(self._copy_stream)
+            st["pending"] = True
             compute.wait_event(st["copied"])
         d_slots, d_lens = dev[:n], dev[n:2 * n]
         d_pairs = dev[2 * n:2 * n + 2 * npairs].view(npairs, 2)
         d_tables = self._dtables[:n]
         if same_rows:
-            self._pa.append_block_tables(d_tables, d_lens, d_slots, self.block_size)
+            self._pa.append_block_tables_host(d_tables, lens, slots, d_lens, d_slots, self.block_size)
         else:
             d_tables.copy_(dev[4 * n:4 * n + n * self.max_blocks].view(n, self.max_blocks))
             self._rows = s.copy()
@@ -188,7 +199,6 @@ class PagedDecoder:
         self._pa.decode(out, q, self.k_cache, self.v_cache, d_tables, d_lens, scale,
                         max_context_len=max_ctx, partition_size=self.partition_size,
                         workspace=self._workspace_for(n, max_ctx))
-        st["consumed"].record(compute)
         return out, slots, pairs[:npairs]
 
     def tables(self, seqs):

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(L.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 7
+    assert lib.pa_abi_version() == 8
 
 
 def test_status_strings_and_workspace_size():
@@ -221,3 +221,24 @@ def test_append_block_tables_rejects_before_launch(args, status, msg):
     assert lib.pa_append_block_tables(*args, None) == status
     assert msg in lib.pa_last_error()
     assert lib.pa_append_block_tables(0, 4, 0, 0, 0, 16, None) == 0   # empty batch: nothing to do
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((16, 4, 32, 48, 64, 80, -1, 16), 1, b"zero size"),
+    ((16, 0, 32, 48, 64, 80, 2, 16), 1, b"zero size"),
+    ((16, 4, 32, 48, 64, 80, 2, 12), 2, b"power of two"),
+    ((16, 4, 32, 48, 64, 80, 2, 512), 2, b"power of two"),
+    ((0, 4, 32, 48, 64, 80, 2, 16), 1, b"null pointer"),
+    ((16, 4, 0, 48, 64, 80, 2, 16), 1, b"null pointer"),
+    ((16, 4, 32, 0, 64, 80, 2, 16), 1, b"null pointer"),
+    ((16, 4, 32, 48, 0, 80, 2, 16), 1, b"null pointer"),
+    ((16, 4, 32, 48, 64, 0, 2, 16), 1, b"null pointer"),
+])
+def test_append_block_tables_host_rejects_before_launch(args, status, msg):
+    """The host-argument append checks its arguments like the device one;
+    the pointer values here are never dereferenced (the call fails first)."""
+    lib, _ = _lib()
+    assert lib.pa_append_block_tables_host(*args, None) == status
+    assert msg in lib.pa_last_error()
+    assert lib.pa_append_block_tables_host(0, 4, 0, 0, 0, 0, 0, 16, None) == 0   # empty batch: nothing to do
+

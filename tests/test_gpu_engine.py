@@ -159,3 +159,34 @@ def test_append_block_tables_matches_manager(bs):
             assert len(pairs) == 1, "one copy-on-write: sequence 3 or 7 copies the shared partial block"
     bm.check()
     bm.close()
+
+
+@pytest.mark.parametrize("n", [1, 300, 448, 449, 1000])
+def test_append_block_tables_host_matches_device_call(n):
+    """pa_append_block_tables_host gives the tables pa_append_block_tables
+    gives from the same lengths and slots in device memory, bit for bit, and
+    stores those lengths and slots to its device outputs; batches over 448
+    sequences take several launches. Rows with no token, a negative slot or
+    a column past the table width keep their entries."""
+    import paged_kv_cache_165_amd as pa
+    rng = np.random.default_rng(n)
+    bs, maxb = 16, 9
+    lens = rng.integers(0, maxb * bs + 20, size=n).astype(np.int32)
+    slots = rng.integers(0, 5000 * bs, size=n).astype(np.int32)
+    slots[rng.random(n) < 0.1] = -1
+    tab0 = rng.integers(0, 5000, size=(n, maxb)).astype(np.int32)
+    ref = torch.from_numpy(tab0).to(DEV)
+    pa.append_block_tables(ref, torch.from_numpy(lens).to(DEV), torch.from_numpy(slots).to(DEV), bs)
+    got = torch.from_numpy(tab0).to(DEV)
+    lens_out = torch.full((n,), -9, dtype=torch.int32, device=DEV)
+    slots_out = torch.full((n,), -9, dtype=torch.int32, device=DEV)
+    host_lens, host_slots = lens.copy(), slots.copy()
+    pa.append_block_tables_host(got, host_lens, host_slots, lens_out, slots_out, bs)
+    host_lens[:] = 0          # the call has read them: reusing the arrays changes nothing
+    host_slots[:] = -1
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    assert np.array_equal(lens_out.cpu().numpy(), lens) and np.array_equal(slots_out.cpu().numpy(), slots)
+    changed = (got.cpu().numpy() != tab0).any(axis=1)
+    expect = (lens > 0) & (slots >= 0) & ((lens - 1) // bs < maxb)
+    assert not (changed & ~expect).any()
