@@ -55,6 +55,10 @@ def parse():
                     help="instead of the headline line, drive the workload's sequences through the "
                          "multi-step decoder (native block manager + the three device calls) for this "
                          "many steps and report host and device time per step")
+    ap.add_argument("--engine-layers", type=int, default=1,
+                    help="with --engine-steps: caches of this many layers sharing one block table per "
+                         "sequence; each step runs the block manager, tables and copies once and each "
+                         "layer's write + decode")
     ap.add_argument("--prefill", choices=["prompts", "chunked"], default=None,
                     help="instead of the headline line, time paged prefill attention (cache write of the "
                          "new tokens + pa_prefill) on this workload and print its own line")
@@ -187,22 +191,33 @@ def engine_bench(args, dev):
     maxb = int(max(-(-(int(L) + total) // bs) for L in lens0))
     dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
     rng = np.random.default_rng(w.seed)
+    nl = max(1, args.engine_layers)
     eng = PagedDecoder(need + 8, bs, w.num_heads, w.num_kv_heads, w.head_dim, max_blocks_per_seq=maxb,
                        dtype=dtype, device=dev, partition_size=w.partition_size,
-                       free_order=rng.permutation(need + 8))
+                       free_order=rng.permutation(need + 8), num_layers=nl)
+    lead = (nl,) if nl > 1 else ()
     g = torch.Generator(device=dev).manual_seed(w.seed)
     progress(f"engine: prefilling {n} sequences ({int(lens0.sum())} tokens)")
     for s, L in enumerate(lens0):
-        k = torch.randn(int(L), w.num_kv_heads, w.head_dim, generator=g, device=dev).to(dtype)
-        v = torch.randn(int(L), w.num_kv_heads, w.head_dim, generator=g, device=dev).to(dtype)
+        k = torch.randn(*lead, int(L), w.num_kv_heads, w.head_dim, generator=g, device=dev).to(dtype)
+        v = torch.randn(*lead, int(L), w.num_kv_heads, w.head_dim, generator=g, device=dev).to(dtype)
         eng.prefill(s, k, v)
     seqs = list(range(n))
     q = torch.randn(n, w.num_heads, w.head_dim, generator=g, device=dev).to(dtype)
     kn = torch.randn(n, w.num_kv_heads, w.head_dim, generator=g, device=dev).to(dtype)
     vn = torch.randn(n, w.num_kv_heads, w.head_dim, generator=g, device=dev).to(dtype)
     out = torch.empty_like(q)
+
+    def one_step():
+        if nl == 1:
+            eng.step(seqs, q, kn, vn, w.scale, out=out)
+            return
+        st = eng.begin_step(seqs)
+        for layer in range(nl):
+            eng.decode_layer(st, layer, q, kn, vn, w.scale, out=out)
+
     for _ in range(args.warmup):
-        eng.step(seqs, q, kn, vn, w.scale, out=out)
+        one_step()
     torch.cuda.synchronize()
     host = []
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -210,21 +225,24 @@ def engine_bench(args, dev):
     start.record()
     for _ in range(args.engine_steps):
         th = time.perf_counter()
-        eng.step(seqs, q, kn, vn, w.scale, out=out)
+        one_step()
         host.append(time.perf_counter() - th)
     end.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.engine_steps
     dev_ms = start.elapsed_time(end) / args.engine_steps
     eng.blocks.check()
-    kv = int(2 * (int(lens0.sum()) + n * (total + 1) // 2) * w.num_kv_heads * w.head_dim * (4 if w.dtype == "f32" else 2))
+    kv = nl * int(2 * (int(lens0.sum()) + n * (total + 1) // 2) * w.num_kv_heads * w.head_dim *
+                  (4 if w.dtype == "f32" else 2))
     print(json.dumps({
         "metric": "multi-step paged decode through the block manager: wall time per step",
         "value": round(wall * 1e6, 1), "unit": "us", "n_gpus": 1, "steps": args.engine_steps,
         "warmup": args.warmup, "higher_is_better": False, "data": "synthetic", "dtype": w.dtype,
-        "config": {"workload": w.name, "num_seqs": n, "block_size": bs, "prompt_tokens": int(lens0.sum())},
+        "config": {"workload": w.name, "num_seqs": n, "block_size": bs, "prompt_tokens": int(lens0.sum()),
+                   "num_layers": nl},
         "host_us_per_step": round(1e6 * float(np.mean(host)), 1),
         "gpu_stream_us_per_step": round(1e3 * dev_ms, 1),
+        "wall_us_per_layer": round(wall * 1e6 / nl, 1),
         "kv_gb_per_s_wall": round(kv / wall / 1e9, 1),
     }), flush=True)
 

@@ -3,10 +3,12 @@ block manager (include/pa_blocks.h) and, per step, the three device calls of
 include/pa.h in the order the copy-on-write scheme needs them -- copy the
 shared blocks a write would touch, write the new tokens, decode.
 
-Host work per step is the block manager's bookkeeping and one upload of the
-step's slot mapping, lengths and copy pairs, which the native manager writes
-straight into a pinned staging buffer; every byte of K/V is moved and
-reduced by the library's kernels. The block tables stay on the device: when
+Host work per step is the block manager's bookkeeping, which the native
+manager writes straight into a pinned staging buffer (slots, lengths, copy
+pairs, and the tables when they must go up whole); every byte of K/V is
+moved and reduced by the library's kernels. With several layers
+(``num_layers``) the step's bookkeeping, tables and copies are done once
+for all of them, and each layer adds its own write and decode. The block tables stay on the device: when
 a step decodes the same sequences as the step before, the only table entry
 that can change per sequence is the one of its newest token (a new block,
 or a copy-on-write), and pa_append_block_tables_host writes it from the
@@ -29,14 +31,33 @@ from . import _lib
 from .blocks import BlockManager
 
 
+class Step:
+    """What a decode step shares across a model's layers: the device slot
+    mapping, lengths and block tables of its sequences and the host views of
+    its slots and copy pairs (valid until the step after next)."""
+
+    __slots__ = ("n", "slots", "pairs", "d_slots", "d_lens", "d_tables", "max_ctx")
+
+    def __init__(self, n, slots, pairs, d_slots, d_lens, d_tables, max_ctx):
+        self.n, self.slots, self.pairs = n, slots, pairs
+        self.d_slots, self.d_lens, self.d_tables, self.max_ctx = d_slots, d_lens, d_tables, max_ctx
+
+
 class PagedDecoder:
     """Sequences decoded one token per step over a paged KV cache of
     ``num_blocks`` blocks of ``block_size`` tokens. ``max_blocks_per_seq``
-    bounds every sequence (it sizes the block tables passed to decode)."""
+    bounds every sequence (it sizes the block tables passed to decode).
+
+    With ``num_layers`` > 1 the caches hold that many layers in one
+    allocation each ([L, NB, ...], the layout of the multi-layer calls) and
+    all layers share one block table per sequence: a step is ``begin_step``
+    (slots, copy-on-write of every layer in one launch, tables) followed by
+    ``decode_layer`` for each layer (that layer's cache write and decode),
+    which is the order a model's layers produce their K/V rows in."""
 
     def __init__(self, num_blocks: int, block_size: int, num_heads: int, num_kv_heads: int, head_dim: int,
                  max_blocks_per_seq: int, dtype=torch.bfloat16, device="cuda", partition_size: int = 0,
-                 free_order=None):
+                 free_order=None, num_layers: int = 1):
         import paged_kv_cache_165_amd as pa
         self._pa = pa
         self.block_size = int(block_size)
@@ -46,8 +67,15 @@ class PagedDecoder:
         self.max_blocks = int(max_blocks_per_seq)
         self.partition_size = int(partition_size)
         self.device = torch.device(device)
-        self.k_cache, self.v_cache = pa.alloc_cache(num_blocks, num_kv_heads, block_size, head_dim, dtype,
-                                                    device=self.device)
+        self.num_layers = int(num_layers)
+        if self.num_layers < 1:
+            raise ValueError("num_layers must be at least 1")
+        if self.num_layers == 1:
+            self.k_cache, self.v_cache = pa.alloc_cache(num_blocks, num_kv_heads, block_size, head_dim, dtype,
+                                                        device=self.device)
+        else:
+            self.k_cache, self.v_cache = pa.alloc_cache_layers(self.num_layers, num_blocks, num_kv_heads,
+                                                               block_size, head_dim, dtype, device=self.device)
         self.blocks = BlockManager(num_blocks, block_size, free_order)
         self._workspace = torch.empty(16, dtype=torch.uint8, device=self.device)
         self._staging = []   # two staging sets, used in turn (see _staging_for)
@@ -73,22 +101,33 @@ class PagedDecoder:
                                           device=self.device)
         return self._workspace
 
+    def layer_caches(self, layer: int):
+        """(k_cache, v_cache) of one layer, in the one-layer layout."""
+        if not 0 <= layer < self.num_layers:
+            raise ValueError(f"layer {layer} out of range [0, {self.num_layers})")
+        if self.num_layers == 1:
+            return self.k_cache, self.v_cache
+        return self.k_cache[layer], self.v_cache[layer]
+
     # -- sequence operations ---------------------------------------------
     def prefill(self, seq: int, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor = None, scale: float = None,
                 out: torch.Tensor = None):
-        """A new sequence whose prompt K/V rows are ``k``, ``v`` [T, Hkv, D].
-        Writes them into fresh blocks and returns the slot of every prompt
-        token; given the prompt's queries ``q`` [T, Hq, D] and ``scale`` it
-        also runs causal prefill attention over the prompt (``pa_prefill``)
-        and returns (slots, out)."""
-        n = int(k.shape[0])
+        """A new sequence whose prompt K/V rows are ``k``, ``v`` [T, Hkv, D]
+        ([L, T, Hkv, D] with several layers, written in one launch). Writes
+        them into fresh blocks and returns the slot of every prompt token;
+        given the prompt's queries ``q`` [T, Hq, D] ([L, T, Hq, D]) and
+        ``scale`` it also runs causal prefill attention over the prompt
+        (``pa_prefill``, once per layer) and returns (slots, out)."""
+        layered = self.num_layers > 1
+        n = int(k.shape[1] if layered else k.shape[0])
         self.blocks.prefill(seq, n)
         self._rows = None
         table, lens = self.blocks.block_tables([seq], max(-(-n // self.block_size), 1), pad=0)
         pos = np.arange(n)
         slots = (table[0][pos // self.block_size] * self.block_size + pos % self.block_size).astype(np.int32)
         if n:
-            self._pa.write_cache(k, v, self.k_cache, self.v_cache, self._dev(slots))
+            write = self._pa.write_cache_layers if layered else self._pa.write_cache
+            write(k, v, self.k_cache, self.v_cache, self._dev(slots))
         if q is None:
             return slots
         if scale is None:
@@ -96,9 +135,12 @@ class PagedDecoder:
         if out is None:
             out = torch.empty_like(q)
         if n:
-            self._pa.prefill(out, q, self.k_cache, self.v_cache, self._dev(table), self._dev(lens),
-                             self._dev(np.array([0, n], dtype=np.int32)), scale, max_query_len=n,
-                             max_context_len=n)
+            d_table, d_lens = self._dev(table), self._dev(lens)
+            d_qs = self._dev(np.array([0, n], dtype=np.int32))
+            for layer in range(self.num_layers):
+                kc, vc = self.layer_caches(layer)
+                self._pa.prefill(out[layer] if layered else out, q[layer] if layered else q, kc, vc, d_table,
+                                 d_lens, d_qs, scale, max_query_len=n, max_context_len=n)
         return slots, out
 
     def fork(self, child: int, parent: int, num_tokens: int = None) -> None:
@@ -136,13 +178,11 @@ class PagedDecoder:
             st["pending"] = False
         return st
 
-    def step(self, seqs, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
-             out: torch.Tensor = None):
-        """Append one token to each of ``seqs`` (its K/V rows ``k``, ``v``
-        [n, Hkv, D]) and decode: attention of ``q`` [n, Hq, D] over each
-        sequence's cache including the new token. Returns (out, slots,
-        copy pairs); the last two are views of a staging buffer, valid until
-        the step after next."""
+    def begin_step(self, seqs) -> Step:
+        """Append one token to each of ``seqs``: reserve its slot (copying a
+        shared partly filled block first, in every layer) and bring the
+        device block tables and lengths up to date. The step's K/V rows and
+        attention follow per layer in ``decode_layer``."""
         s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
         n = len(s)
         st = self._staging_for(n)
@@ -191,15 +231,39 @@ class PagedDecoder:
             d_tables.copy_(dev[4 * n:4 * n + n * self.max_blocks].view(n, self.max_blocks))
             self._rows = s.copy()
         if npairs:
-            self._pa.copy_blocks(self.k_cache, self.v_cache, d_pairs)
-        self._pa.write_cache(k, v, self.k_cache, self.v_cache, d_slots)
+            copy = self._pa.copy_blocks_layers if self.num_layers > 1 else self._pa.copy_blocks
+            copy(self.k_cache, self.v_cache, d_pairs)
         max_ctx = int(lens.max()) if n else 0
+        return Step(n, slots, pairs[:npairs], d_slots, d_lens, d_tables, max_ctx)
+
+    def decode_layer(self, step: Step, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     scale: float, out: torch.Tensor = None) -> torch.Tensor:
+        """One layer of a step begun by ``begin_step``: write the new
+        tokens' K/V rows ``k``, ``v`` [n, Hkv, D] into this layer's cache and
+        decode: attention of ``q`` [n, Hq, D] over each sequence's tokens,
+        the new one included. Layers may run in any order, each once."""
+        kc, vc = self.layer_caches(layer)
+        self._pa.write_cache(k, v, kc, vc, step.d_slots)
         if out is None:
             out = torch.empty_like(q)
-        self._pa.decode(out, q, self.k_cache, self.v_cache, d_tables, d_lens, scale,
-                        max_context_len=max_ctx, partition_size=self.partition_size,
-                        workspace=self._workspace_for(n, max_ctx))
-        return out, slots, pairs[:npairs]
+        self._pa.decode(out, q, kc, vc, step.d_tables, step.d_lens, scale,
+                        max_context_len=step.max_ctx, partition_size=self.partition_size,
+                        workspace=self._workspace_for(step.n, step.max_ctx))
+        return out
+
+    def step(self, seqs, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
+             out: torch.Tensor = None):
+        """Append one token to each of ``seqs`` (its K/V rows ``k``, ``v``
+        [n, Hkv, D]) and decode: attention of ``q`` [n, Hq, D] over each
+        sequence's cache including the new token. Returns (out, slots,
+        copy pairs); the last two are views of a staging buffer, valid until
+        the step after next. One-layer caches only; with several layers use
+        ``begin_step`` and ``decode_layer``."""
+        if self.num_layers != 1:
+            raise ValueError("step() is for one layer; use begin_step() and decode_layer() per layer")
+        st = self.begin_step(seqs)
+        out = self.decode_layer(st, 0, q, k, v, scale, out)
+        return out, st.slots, st.pairs
 
     def tables(self, seqs):
         return self.blocks.block_tables(seqs, self.max_blocks, pad=0)
