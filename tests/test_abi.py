@@ -242,3 +242,28 @@ def test_append_block_tables_host_rejects_before_launch(args, status, msg):
     assert msg in lib.pa_last_error()
     assert lib.pa_append_block_tables_host(0, 4, 0, 0, 0, 0, 0, 16, None) == 0   # empty batch: nothing to do
 
+
+
+def test_headers_and_library_usable_from_plain_c(tmp_path):
+    """include/pa.h and include/pa_blocks.h compile as strict C99 (and as
+    C++17), and a C program linked against libpa.so drives the host-side
+    calls: version, status strings, the default partition, rejection before
+    any launch, and the block manager's copy-on-write append
+    (tests/c/abi_from_c.c)."""
+    import shutil
+    import subprocess
+    from paged_kv_cache_165_amd import _lib as L
+    gcc, gxx = shutil.which("gcc"), shutil.which("g++")
+    if gcc is None or gxx is None:
+        pytest.skip("no host C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    inc = os.path.join(root, "include")
+    src = os.path.join(root, "tests", "c", "abi_from_c.c")
+    libdir = os.path.dirname(L.LIB_PATH)
+    strict = ["-Wall", "-Wextra", "-pedantic", "-Werror", f"-I{inc}"]
+    subprocess.run([gxx, "-std=c++17", *strict, "-x", "c++", "-c", src, "-o", str(tmp_path / "cxx.o")], check=True)
+    exe = str(tmp_path / "abi_from_c")
+    subprocess.run([gcc, "-std=c99", *strict, src, f"-L{libdir}", "-lpa", f"-Wl,-rpath,{libdir}", "-o", exe],
+                   check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
