@@ -78,7 +78,7 @@ def _make_decode(dt, d, g, hkv, bs, lens, seed):
     return q, kc, vc, tables
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_decode_matches_oracle(seed):
     import paged_kv_cache_165_amd as pa
     rng = np.random.default_rng(9000 + seed)
@@ -94,7 +94,7 @@ def test_random_decode_matches_oracle(seed):
     compare_attention(out, ref, f"random decode {seed}")
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_prefill_matches_oracle(seed):
     import paged_kv_cache_165_amd as pa
     rng = np.random.default_rng(9500 + seed)
