@@ -32,11 +32,23 @@ __host__ __device__ constexpr int write_lds_row(int head_dim, int elem_bytes) {
 // K: each token's row is one contiguous run in the cache, copied as 16-byte
 // vectors. V: the cache holds each block's rows as tiles of vt tokens stored
 // head_dim-major ([NB][Hkv][B/vt][D][vt]), so element d of a token at offset
-// off goes to row d, column off % vt of its tile. The chunk's V rows are
-// staged in LDS and written with the token index fastest across lanes:
-// tokens at consecutive offsets of one tile (a prompt or a tail appended in
-// order) then leave each wave as one contiguous run of whole tile rows
-// instead of isolated elements. Slots outside [0, pool_slots) skip the token.
+// off goes to row d, column off % vt of its tile, and a tile row is only
+// vt elements (32 bytes for 16 bf16 tokens). HBM writes such a row at full
+// speed only when it is written whole: two workgroups writing two parts of
+// one row at different times cost nearly twice as much (measured on MI355X:
+// 64k tokens in runs that start at a tile boundary, 80 us; the same runs
+// shifted by a few slots, 144 us). The V rows therefore go by runs: a run is
+// a stretch of slot-mapping entries whose slots are consecutive within one
+// tile (at most vt tokens), and the workgroup whose chunk holds a run's
+// first entry writes the whole run, reaching up to vt - 1 entries into the
+// next chunk, whose workgroup skips them. The V rows of those tokens are
+// staged in LDS and written with the token index fastest across lanes, so a
+// run that fills a tile leaves the wave as whole tile rows. Rows too wide
+// for a window of 2^log2_win = 32 staged tokens in LDS go by plain chunks
+// instead (log2_win = log2_chunk, fewer than 16 entries: every workgroup
+// writes exactly its chunk's V rows). Slots outside [0, pool_slots) skip the
+// token (and end any run).
+
 template <typename EW>
 __global__ __launch_bounds__(256) void pa_write_kernel(const u32x4* __restrict__ k,
                                                        const u32x4* __restrict__ v,
@@ -45,7 +57,7 @@ __global__ __launch_bounds__(256) void pa_write_kernel(const u32x4* __restrict__
                                                        const int32_t* __restrict__ slots,
                                                        int num_tokens, int num_kv_heads, int head_dim,
                                                        int row16, int log2_bs, int log2_vt, int log2_chunk,
-                                                       long long pool_slots) {
+                                                       int log2_win, long long pool_slots) {
     constexpr int E = sizeof(EW);
     {
         // this workgroup's layer: pool_slots is also the cache's layer
@@ -60,29 +72,54 @@ __global__ __launch_bounds__(256) void pa_write_kernel(const u32x4* __restrict__
     }
     extern __shared__ __align__(16) unsigned char smem[];
     const int chunk = 1 << log2_chunk;
+    const bool runs = log2_win > log2_chunk;
     const int ld = write_lds_row(head_dim, E);  // padded row (elements): odd dword stride
-    EW* vs = reinterpret_cast<EW*>(smem);
-    int* sl = reinterpret_cast<int*>(smem + static_cast<size_t>(chunk) * ld * E);
+    EW* vs = reinterpret_cast<EW*>(smem);      // [2^log2_win][ld]
     const int i0 = blockIdx.x << log2_chunk;
     const int kvh = blockIdx.y;
     const int n = min(chunk, num_tokens - i0);
     const int bs = 1 << log2_bs, vt = 1 << log2_vt;
+    const int lane = threadIdx.x & 63;
 
-    for (int c = threadIdx.x; c < n * row16; c += blockDim.x) {
+    // Every wave holds the slot window in its lanes: lane j has the slot of
+    // entry i0 - 1 + j (j <= chunk + 16; -1 outside the mapping or the pool).
+    int my_slot = -1;
+    if (lane <= chunk + 16) {
+        const int i = i0 - 1 + lane;
+        const int sv = i >= 0 && i < num_tokens ? slots[i] : -1;
+        my_slot = (sv < 0 || static_cast<long long>(sv) >= pool_slots) ? -1 : sv;
+    }
+    auto slot_of = [&](int j) { return __shfl(my_slot, j); };  // slot of entry i0 - 1 + j
+    // This chunk's V tokens: from its first run start (skipping p entries
+    // that continue a run of the chunk before) to the end of its last run
+    // (q entries into the next chunk). One ballot evaluates whether entry
+    // i0 - 1 + j continues the run of the entry before it, for every j at
+    // once; the next workgroup finds p = q on the same slots.
+    int p = 0, q = 0;
+    {
+        const int prev = __shfl_up(my_slot, 1);
+        const bool c = lane >= 1 && lane <= chunk + 16 && prev >= 0 && my_slot >= 0 && my_slot == prev + 1 &&
+                       (my_slot & (vt - 1)) != 0;
+        const unsigned long long mask = __ballot(c);
+        if (runs) {
+            p = min(n, __builtin_ctzll(~(mask >> 1)));
+            if (n == chunk && p < n) q = min(vt - 1, __builtin_ctzll(~(mask >> (1 + n))));
+        }
+    }
+    const int m = n - p + q;  // V tokens, at most chunk + vt - 1 <= 2^log2_win
+
+    // their rows, staged in LDS (row t: entry i0 + p + t)
+    for (int c = threadIdx.x; c < m * row16; c += blockDim.x) {
         const int t = c / row16;
         const int r = c - t * row16;
-        const u32x4 w = v[(static_cast<size_t>(i0 + t) * num_kv_heads + kvh) * row16 + r];
+        const u32x4 w = v[(static_cast<size_t>(i0 + p + t) * num_kv_heads + kvh) * row16 + r];
         uint32_t* dst = reinterpret_cast<uint32_t*>(vs + static_cast<size_t>(t) * ld) + 4 * r;
         dst[0] = w.x;
         dst[1] = w.y;
         dst[2] = w.z;
         dst[3] = w.w;
     }
-    if (static_cast<int>(threadIdx.x) < n) {
-        const int slot = slots[i0 + threadIdx.x];
-        sl[threadIdx.x] = (slot < 0 || static_cast<long long>(slot) >= pool_slots) ? -1 : slot;
-    }
-    __syncthreads();
+
     // All stores are nontemporal. A token's V elements touch every line of
     // its tile, each partially; left dirty in L2, such lines slow down the
     // decode that reads them next (measured: +12 us on the batch-256
@@ -90,28 +127,33 @@ __global__ __launch_bounds__(256) void pa_write_kernel(const u32x4* __restrict__
     // MI355X against ordinary stores, and against K rows loaded before the
     // barrier, this is the fastest both for one new token per sequence and
     // for long runs of consecutive tokens.
-    for (int c = threadIdx.x; c < n * row16; c += blockDim.x) {
+    for (int c = threadIdx.x; c < ((n * row16 + 63) & ~63); c += blockDim.x) {
         const int t = c / row16;
+        const int slot = slot_of(1 + min(t, n - 1));  // every lane takes part in the shuffle
+        if (c >= n * row16 || slot < 0) continue;
         const int r = c - t * row16;
-        const int slot = sl[t];
-        if (slot < 0) continue;
         const int pid = slot >> log2_bs;
         const int off = slot & (bs - 1);
         __builtin_nontemporal_store(k[(static_cast<size_t>(i0 + t) * num_kv_heads + kvh) * row16 + r],
                                     kc + ((static_cast<size_t>(pid) * num_kv_heads + kvh) * bs + off) * row16 + r);
     }
-    // this thread's token is the same in every pass below (blockDim is a
-    // multiple of the chunk)
-    const int t = threadIdx.x & (chunk - 1);
-    const int slot = t < n ? sl[t] : -1;
-    if (slot < 0) return;
+    // lanes per token group: 16 unless more than 16 tokens are to be
+    // written (a group of 16 lanes stores a whole tile row of 16 tokens, and
+    // a wave four consecutive rows); this thread's token is the same in
+    // every pass below (blockDim is a multiple of the group)
+    const int log2_tw = m > 16 ? log2_win : min(log2_win, 4);
+    const int t = threadIdx.x & ((1 << log2_tw) - 1);
+    const int slot = slot_of(1 + p + min(t, chunk + 15 - p));
+    __syncthreads();
+    if (t >= m || slot < 0) return;
+    const EW* vsrc = vs + static_cast<size_t>(t) * ld;
     const int pid = slot >> log2_bs;
     const int off = slot & (bs - 1);
     EW* vrow = vc + (static_cast<size_t>(pid) * num_kv_heads + kvh) * bs * head_dim +
                static_cast<size_t>(off >> log2_vt) * head_dim * vt + (off & (vt - 1));
-    for (int e = threadIdx.x; e < (head_dim << log2_chunk); e += blockDim.x) {
-        const int d = e >> log2_chunk;
-        __builtin_nontemporal_store(vs[static_cast<size_t>(t) * ld + d], vrow + static_cast<size_t>(d) * vt);
+    for (int e = threadIdx.x; e < (head_dim << log2_tw); e += blockDim.x) {
+        const int d = e >> log2_tw;
+        __builtin_nontemporal_store(vsrc[d], vrow + static_cast<size_t>(d) * vt);
     }
 }
 
@@ -227,11 +269,16 @@ hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void*
     if (num_tokens == 0 || num_layers == 0) return hipSuccess;
     const int row16 = head_dim * elem_bytes / 16;
     const int ld = write_lds_row(head_dim, elem_bytes);
-    // tokens per workgroup: 16, fewer for rows so wide that 16 would not fit
-    // in 32 KB of LDS
-    int log2_chunk = 4;
-    while (log2_chunk > 0 && (static_cast<size_t>(1) << log2_chunk) * ld * elem_bytes > 32 * 1024) --log2_chunk;
-    const size_t smem = (static_cast<size_t>(1) << log2_chunk) * (static_cast<size_t>(ld) * elem_bytes + 4);
+    // Run mode: 16 entries per workgroup, V staging for up to 31 tokens (the
+    // chunk and the rest of its last run) when 32 rows fit in 64 KB of LDS.
+    // Otherwise plain chunks of 16 entries, fewer for rows so wide that 16
+    // would not fit in 32 KB.
+    int log2_chunk = 4, log2_win = 5;
+    if ((static_cast<size_t>(1) << log2_win) * ld * elem_bytes > 64 * 1024) {
+        while (log2_chunk > 0 && (static_cast<size_t>(1) << log2_chunk) * ld * elem_bytes > 32 * 1024) --log2_chunk;
+        log2_win = log2_chunk;
+    }
+    const size_t smem = (static_cast<size_t>(1) << log2_win) * ld * elem_bytes;
     if (smem > 64 * 1024) return hipErrorInvalidConfiguration;
     const int log2_bs = ilog2(block_size);
     const int log2_vt = ilog2(v_tile_tokens(block_size));
@@ -242,12 +289,12 @@ hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void*
         hipLaunchKernelGGL(pa_write_kernel<uint16_t>, grid, dim3(256), smem, stream,
                            static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
                            static_cast<u32x4*>(k_cache), static_cast<uint16_t*>(v_cache), slots, num_tokens,
-                           num_kv_heads, head_dim, row16, log2_bs, log2_vt, log2_chunk, pool_slots);
+                           num_kv_heads, head_dim, row16, log2_bs, log2_vt, log2_chunk, log2_win, pool_slots);
     } else {
         hipLaunchKernelGGL(pa_write_kernel<uint32_t>, grid, dim3(256), smem, stream,
                            static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
                            static_cast<u32x4*>(k_cache), static_cast<uint32_t*>(v_cache), slots, num_tokens,
-                           num_kv_heads, head_dim, row16, log2_bs, log2_vt, log2_chunk, pool_slots);
+                           num_kv_heads, head_dim, row16, log2_bs, log2_vt, log2_chunk, log2_win, pool_slots);
     }
     return hipGetLastError();
 }

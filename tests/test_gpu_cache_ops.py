@@ -135,6 +135,53 @@ def test_write_cache_full_tiles_in_order():
     assert raw_equal(kc, kc_o) and raw_equal(vc, vc_o)
 
 
+@pytest.mark.parametrize("dt,bs,d", [(torch.bfloat16, 16, 128), (torch.bfloat16, 4, 64), (torch.float16, 8, 128),
+                                     (torch.float32, 32, 256), (torch.bfloat16, 64, 128)])
+def test_write_cache_runs_at_every_tile_offset(dt, bs, d):
+    """Runs of consecutive slots starting at every offset of a V tile and
+    crossing the 16-entry chunks of the slot mapping at every position (the
+    workgroup that holds a run's first entry writes the whole run, into the
+    next chunk), with a skipped token and a slot past the pool inside runs;
+    bit for bit against the oracle."""
+    pa = _pa()
+    rng = np.random.default_rng(bs * 31 + d)
+    g = torch.Generator(device=DEV).manual_seed(bs * 31 + d)
+    t = min(bs, 16)
+    hkv, nb = 2, 160
+    kc = _rand((nb, hkv, bs, d), dt, g)
+    vc = _rand((nb, hkv, bs // t, d, t), dt, g)
+    blocks = rng.permutation(nb)
+    slots, bi = [], 0
+    for start in range(bs):
+        for length in (1, t - 1, t, t + 3, 2 * t + 5):
+            pid, off = int(blocks[bi]), start
+            bi += 1
+            for _ in range(length):
+                if off == bs:
+                    pid, off = int(blocks[bi]), 0
+                    bi += 1
+                slots.append(pid * bs + off)
+                off += 1
+            if bi >= nb - 4:
+                break
+        if bi >= nb - 4:
+            break
+    slots = np.array(slots, dtype=np.int64)
+    slots_dev = slots.copy()
+    slots_dev[7] = -1
+    slots_dev[40] = nb * bs + 1  # past the pool: skipped, ends its run
+    n = len(slots)
+    k = _rand((n, hkv, d), dt, g)
+    v = _rand((n, hkv, d), dt, g)
+    kc_h, vc_h = host_bits(kc), host_bits(vc)
+    pa.write_cache(k, v, kc, vc, torch.from_numpy(slots_dev.astype(np.int32)).to(DEV))
+    torch.cuda.synchronize()
+    ref = slots_dev.copy()
+    ref[40] = -1
+    kc_o, vc_o = oracle.write_cache(host_bits(k), host_bits(v), kc_h, vc_h, ref, bs)
+    assert raw_equal(kc, kc_o) and raw_equal(vc, vc_o)
+
+
 @pytest.mark.parametrize("dt,bs", [(torch.bfloat16, 16), (torch.float32, 8), (torch.float16, 32)])
 def test_copy_blocks_matches_oracle(dt, bs):
     pa = _pa()
