@@ -51,6 +51,12 @@
  * Thread safety: the library keeps no state besides a per-device cache of the
  * compute-unit count and kernel occupancy, filled under a lock. Calls that
  * share a workspace must not overlap.
+ *
+ * Graph capture: the device calls enqueue kernels only (no allocation,
+ * memset, copy or synchronization), so a caller may record them into a HIP
+ * graph and replay it. Make one call of each kind on the device before
+ * capturing: the first call fills the per-device cache above through host
+ * queries.
  */
 #ifndef PA_H
 #define PA_H
