@@ -506,6 +506,32 @@ def main():
     kb.record()
     torch.cuda.synchronize()
     part_us = 1e3 * ka.elapsed_time(kb) / args.steps
+
+    # The cache maintenance calls of the step, each timed the same way
+    # (writing the same rows, or copying the same blocks, again changes
+    # nothing): moved bytes are read + written.
+    def back_to_back(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / args.steps
+
+    row_bytes = w.num_kv_heads * w.head_dim * q.element_size()
+    cache_ops = {"timing": f"{args.steps} back-to-back launches between two HIP events on the launch stream",
+                 "write": [], "copy": None}
+    for sl, (k, v) in zip(slots, vals["writes"]):
+        us = back_to_back(lambda: pa.write_cache(k, v, kc, vc, sl))
+        moved = 4 * sl.shape[0] * row_bytes
+        cache_ops["write"].append({"tokens": int(sl.shape[0]), "us": round(us, 2),
+                                   "moved_gbs": round(moved / (us * 1e-6) / 1e9, 1)})
+    if len(w.cow_pairs):
+        us = back_to_back(lambda: pa.copy_blocks(kc, vc, pairs))
+        moved = 4 * len(w.cow_pairs) * w.block_size * row_bytes
+        cache_ops["copy"] = {"pairs": int(len(w.cow_pairs)), "us": round(us, 2),
+                             "moved_gbs": round(moved / (us * 1e-6) / 1e9, 1)}
     kv = w.kv_bytes()
     unique = w.unique_kv_bytes()
     value = kv / (ms_step * 1e-3) / 1e9
@@ -581,6 +607,7 @@ def main():
         "unique_kv_bytes": unique,
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "wall_ms_per_step": round(1e3 * t_wall / args.steps, 5),
+        "cache_ops": cache_ops,
         "roofline": {"bound": "hbm", "kernel": "pa_decode_partitions (pa_decode_mfma_wave / pa_decode_mfma / pa_decode_valu)",
                      "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
