@@ -99,8 +99,10 @@ def test_write_cache_matches_oracle(dt, d, bs, hkv):
 
 
 def test_write_cache_wide_rows_use_smaller_chunks():
-    """float32 rows of 4096 elements (16 KB): the kernel stages 2 tokens at
-    a time; the result is still the oracle's, bit for bit."""
+    """float32 rows of 4096 elements (16 KB, 16,388 bytes staged with the
+    padding): too wide for runs of staged tokens, so the kernel goes by
+    plain chunks of one token; the result is still the oracle's, bit for
+    bit."""
     pa = _pa()
     rng = np.random.default_rng(5)
     g = torch.Generator(device=DEV).manual_seed(5)
