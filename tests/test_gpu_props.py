@@ -146,10 +146,16 @@ def test_block_sizes(bs, g):
 @pytest.mark.parametrize("dt,d", [(torch.float32, 128), (torch.float32, 256), (torch.bfloat16, 256),
                                   (torch.bfloat16, 64), (torch.float16, 64)])
 def test_block_sizes_wide_rows(bs, dt, d):
-    """Row geometries of the VALU kernel other than 256-byte rows."""
-    if dt == torch.float32 and d == 256 and bs < 16:
-        pytest.skip("float32 head_dim 256 needs blocks of at least 16 tokens")
+    """Row geometries of the VALU kernel other than 256-byte rows. float32
+    head_dim 256 takes blocks of at least 16 tokens: a smaller block is
+    rejected with PA_ERR_UNSUPPORTED before anything is launched."""
     c = make_case([5, 100, 700], 4, 4, d, bs, dt, seed=bs + d)
+    if dt == torch.float32 and d == 256 and bs < 16:
+        pa = _pa()
+        with pytest.raises(pa.PaError) as e:
+            run_gpu(c, 0.1)
+        assert e.value.status == pa._lib.PA_ERR_UNSUPPORTED
+        return
     out = run_gpu(c, 0.1)
     compare_attention(out, run_oracle(c, 0.1), f"{dt} D{d} bs {bs}")
 
