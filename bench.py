@@ -17,6 +17,7 @@ float64 CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -48,6 +49,10 @@ def parse():
     ap.add_argument("--workload", default="gqa8b",
                     choices=["tiny", "layout", "mha7b", "gqa8b", "prefix", "long"])
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--tp", type=int, default=1,
+                    help="time one GPU's shard of the workload split by KV head over this many GPUs: the same "
+                         "sequences, contexts and block tables with num_heads / N query and num_kv_heads / N "
+                         "KV heads")
     ap.add_argument("--block-size", type=int, default=None,
                     help="page the gqa8b sequences with this block size instead of 16 (block-size sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -460,6 +465,11 @@ def main():
         print("--block-size applies to the gqa8b workload only", file=sys.stderr)
         sys.exit(2)
     w = W.build(args.workload, **({"block_size": args.block_size} if args.block_size else {}))
+    if args.tp > 1:
+        if w.num_kv_heads % args.tp or w.num_heads % args.tp:
+            raise SystemExit(f"{w.name}: {w.num_kv_heads} KV heads do not split over {args.tp} GPUs")
+        w = dataclasses.replace(w, name=f"{w.name}_tp{args.tp}", num_heads=w.num_heads // args.tp,
+                                num_kv_heads=w.num_kv_heads // args.tp)
     if args.partition_size:
         w.partition_size = args.partition_size
     vals = W.make_values(w, device=dev, poison=True)
@@ -599,7 +609,9 @@ def main():
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "partition_size": resolved_partition(w), "ctx": w.ctx_recipe, "tokens": int(w.context_lens.sum()), "tail_waste": round(W.tail_waste(w), 5),
-                   "kv_bytes": kv, "seed": w.seed, "parallelism": "none (1 GPU)"},
+                   "kv_bytes": kv, "seed": w.seed,
+                   "parallelism": "none (1 GPU)" if args.tp == 1 else
+                   f"one GPU's shard of a {args.tp}-way split by KV head (no exchange needed)"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "copy_ceiling": {"gbs": round(copy_gbs, 1), "pct_of_ceiling": round(100.0 * value / copy_gbs, 2),
                          "what": "device copy of 1 GiB (bytes read + written per time), 10 launches, same run"},
