@@ -43,10 +43,11 @@ __host__ __device__ constexpr int write_lds_row(int head_dim, int elem_bytes) {
 // first entry writes the whole run, reaching up to vt - 1 entries into the
 // next chunk, whose workgroup skips them. The V rows of those tokens are
 // staged in LDS and written with the token index fastest across lanes, so a
-// run that fills a tile leaves the wave as whole tile rows. Rows too wide
-// for a window of 2^log2_win = 32 staged tokens in LDS go by plain chunks
-// instead (log2_win = log2_chunk, fewer than 16 entries: every workgroup
-// writes exactly its chunk's V rows). Slots outside [0, pool_slots) skip the
+// run that fills a tile leaves the wave as whole tile rows (the staging
+// window holds 2^log2_win = 32 tokens). Rows too wide for 32 staged tokens
+// in 64 KB of LDS go by plain chunks instead: log2_win = log2_chunk, 16
+// entries or fewer so that a chunk's rows fit in 32 KB, and every workgroup
+// writes exactly its chunk's V rows. Slots outside [0, pool_slots) skip the
 // token (and end any run).
 
 template <typename EW>
