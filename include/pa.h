@@ -48,15 +48,16 @@
  * host; the kernels clamp what they read so that a bad index can never make
  * them touch memory outside the arrays (see each call).
  *
- * Thread safety: the library keeps no state besides a per-device cache of the
- * compute-unit count and kernel occupancy, filled under a lock. Calls that
- * share a workspace must not overlap.
+ * Thread safety: the library keeps no state besides two caches filled under a
+ * lock: per device, the compute-unit count and LDS sizes; per (device, decode
+ * kernel, LDS request), the runtime's occupancy figure. Calls that share a
+ * workspace must not overlap.
  *
  * Graph capture: the device calls enqueue kernels only (no allocation,
  * memset, copy or synchronization), so a caller may record them into a HIP
- * graph and replay it. Make one call of each kind on the device before
- * capturing: the first call fills the per-device cache above through host
- * queries.
+ * graph and replay it. Make one call of each kind and shape on the device
+ * before capturing: a call whose cache entries are missing fills them through
+ * host queries of the runtime; later calls of the same shape make none.
  */
 #ifndef PA_H
 #define PA_H
@@ -68,7 +69,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 8
+#define PA_ABI_VERSION 9
 
 typedef enum pa_dtype {
     PA_F32 = 0,  /* IEEE binary32 */
@@ -84,6 +85,22 @@ typedef enum pa_status {
     PA_ERR_HIP = 4,         /* the HIP runtime reported an error */
     PA_ERR_NO_BLOCKS = 5    /* block manager (pa_blocks.h): not enough free blocks */
 } pa_status_t;
+
+/* The three decode partition kernels (see pa_decode_plan). */
+typedef enum pa_decode_kernel {
+    PA_DECODE_VALU = 0,      /* vector ALU; one item per workgroup (float32, or one query head per KV head) */
+    PA_DECODE_MFMA = 1,      /* matrix cores; one item per workgroup (partitions of more than 128 blocks) */
+    PA_DECODE_MFMA_WAVE = 2  /* matrix cores; one item per wave (partitions of at most 128 blocks) */
+} pa_decode_kernel_t;
+
+/* How pa_decode launches its partition kernel for one shape. */
+typedef struct pa_decode_plan {
+    pa_decode_kernel_t kernel;
+    int partition_size;     /* tokens per partition (partition_size = 0 resolved) */
+    int lds_bytes;          /* dynamic LDS per workgroup; the kernels hold no static LDS */
+    int ring_slots;         /* item results a workgroup buffers in that LDS before storing them */
+    int workgroups_per_cu;  /* resident workgroups per compute unit the LDS allows */
+} pa_decode_plan_t;
 
 /* ABI version of the loaded library (PA_ABI_VERSION it was built with). */
 int pa_abi_version(void);
@@ -124,6 +141,25 @@ int pa_default_partition_size(int num_seqs, int num_heads, int num_kv_heads, int
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                 int max_context_len, int block_size, int partition_size, pa_dtype_t dtype);
+
+/*
+ * Host-only planning query: fills *plan with the partition kernel, LDS request
+ * and result ring pa_decode would use for this shape on a device whose
+ * compute units hold lds_per_cu bytes of LDS, with at most lds_per_workgroup
+ * per workgroup (163840 and 163840 on MI355X), when the registers of the
+ * kernel allow max_workgroups_per_cu workgroups of 256 threads per compute
+ * unit (the matrix-core kernels always run one per compute unit; 1 is always
+ * a valid value). No device is queried: pa_decode runs this same computation
+ * with its device's values (hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+ * hipDeviceAttributeMaxSharedMemoryPerBlock and the runtime's occupancy).
+ * Returns PA_ERR_UNSUPPORTED when no kernel for the shape fits the LDS (the
+ * batch's schedule grows with num_seqs); pa_decode then returns the same
+ * status without launching. Other arguments and errors as pa_decode's shape
+ * checks; the sizes must be positive.
+ */
+pa_status_t pa_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
+                           int block_size, int partition_size, pa_dtype_t dtype, int lds_per_cu,
+                           int lds_per_workgroup, int max_workgroups_per_cu, pa_decode_plan_t* plan);
 
 /*
  * Paged decode attention.

@@ -17,11 +17,19 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 PA_OK = 0
 PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_BLOCKS = 1, 2, 3, 4, 5
+PA_DECODE_VALU, PA_DECODE_MFMA, PA_DECODE_MFMA_WAVE = 0, 1, 2
+ABI_VERSION = 9
+
+
+class DecodePlan(ctypes.Structure):
+    """pa_decode_plan_t (include/pa.h)."""
+    _fields_ = [("kernel", ctypes.c_int), ("partition_size", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("ring_slots", ctypes.c_int), ("workgroups_per_cu", ctypes.c_int)]
 
 # every symbol include/pa.h and include/pa_blocks.h declare
 EXPORTED = (
     "pa_abi_version", "pa_status_string", "pa_last_error", "pa_default_partition_size",
-    "pa_decode_workspace_size", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
+    "pa_decode_workspace_size", "pa_decode_plan", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
     "pa_prefill", "pa_write_cache", "pa_copy_blocks", "pa_write_cache_layers", "pa_copy_blocks_layers",
     "pa_append_block_tables", "pa_append_block_tables_host",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_prefill", "pa_bm_share", "pa_bm_append", "pa_bm_free",
@@ -62,6 +70,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.pa_default_partition_size.argtypes = [_i, _i, _i, _i, _i, _i]
         lib.pa_decode_workspace_size.restype = ctypes.c_size_t
         lib.pa_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+        lib.pa_decode_plan.restype = _i
+        lib.pa_decode_plan.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(DecodePlan)]
         for name in ("pa_decode", "pa_decode_partitions", "pa_decode_merge"):
             f = getattr(lib, name)
             f.restype = _i

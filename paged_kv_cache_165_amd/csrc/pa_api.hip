@@ -63,9 +63,10 @@ pa_status_t hip_fail(hipError_t e, const char* what) {
     return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-pa_status_t lds_fail(int num_seqs, int head_dim, int group) {
+pa_status_t lds_fail(int num_seqs, int head_dim, int group, size_t lds_per_cu, size_t lds_per_wg) {
     return fail(PA_ERR_UNSUPPORTED, "num_seqs %d with head_dim %d and group %d needs more LDS than one "
-                "workgroup can hold", num_seqs, head_dim, group);
+                "workgroup can hold (%zu bytes per compute unit, %zu per workgroup)", num_seqs, head_dim, group,
+                lds_per_cu, lds_per_wg);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -82,10 +83,11 @@ int log2i(int x) {
     return r;
 }
 
-// Compute-unit count of the current device, cached per device.
-pa_status_t num_cus(int* out) {
+// What the launches need to know of the current device, read once per
+// device: compute units and LDS sizes.
+pa_status_t device_info(pa::DeviceInfo* out) {
     static std::mutex mu;
-    static std::unordered_map<int, int> cache;
+    static std::unordered_map<int, pa::DeviceInfo> cache;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -95,11 +97,17 @@ pa_status_t num_cus(int* out) {
         *out = it->second;
         return PA_OK;
     }
-    int n = 0;
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0, lds_cu = 0, lds_wg = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_wg, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    cache[dev] = n;
-    *out = n;
+    if (cus < 1 || lds_cu < 1 || lds_wg < 1)
+        return fail(PA_ERR_HIP, "device %d reports %d compute units, %d bytes of LDS per compute unit, %d per "
+                    "workgroup", dev, cus, lds_cu, lds_wg);
+    pa::DeviceInfo d{dev, cus, static_cast<size_t>(lds_cu), static_cast<size_t>(lds_wg)};
+    cache[dev] = d;
+    *out = d;
     return PA_OK;
 }
 
@@ -153,23 +161,18 @@ int pmax_of(int max_context_len, int part) {
     return p < 1 ? 1 : p;
 }
 
-// Shared validation of the decode entry points; fills `p`.
-pa_status_t prepare_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                           const int32_t* block_tables, const int32_t* context_lens, float scale,
-                           int block_size, int num_seqs, int num_heads, int num_kv_heads,
-                           int head_dim, int num_blocks, int max_blocks_per_seq,
-                           int max_context_len, int partition_size, pa_dtype_t dtype,
-                           void* workspace, size_t workspace_bytes, pa::DecodeParams* p) {
-    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
-        max_blocks_per_seq <= 0 || max_context_len < 0 || block_size <= 0 || partition_size < 0)
+// Shape checks shared by the decode entry points and the planning query;
+// sets *part to the resolved partition size.
+pa_status_t check_decode_shape(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
+                               int block_size, int partition_size, pa_dtype_t dtype, int* part_out) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+        block_size <= 0 || partition_size < 0)
         return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_seqs=%d num_heads=%d num_kv_heads=%d "
-                    "head_dim=%d num_blocks=%d max_blocks_per_seq=%d max_context_len=%d block_size=%d "
-                    "partition_size=%d)", num_seqs, num_heads, num_kv_heads, head_dim, num_blocks,
-                    max_blocks_per_seq, max_context_len, block_size, partition_size);
+                    "head_dim=%d max_context_len=%d block_size=%d partition_size=%d)", num_seqs, num_heads,
+                    num_kv_heads, head_dim, max_context_len, block_size, partition_size);
     if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
     if (num_heads % num_kv_heads != 0)
         return fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
-    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
     const int group = num_heads / num_kv_heads;
     if (!pa::decode_supported(dtype, head_dim, group))
         return fail(PA_ERR_UNSUPPORTED, "no kernel for dtype=%d head_dim=%d group=%d "
@@ -186,6 +189,26 @@ pa_status_t prepare_decode(void* out, const void* q, const void* k_cache, const 
     if (part % 16 != 0 || part % block_size != 0 || part / block_size > kMaxTableSlice)
         return fail(PA_ERR_INVALID_ARG, "partition_size %d must be a multiple of 16 and of block_size %d "
                     "spanning at most %d blocks", part, block_size, kMaxTableSlice);
+    *part_out = part;
+    return PA_OK;
+}
+
+// Shared validation of the decode entry points; fills `p`.
+pa_status_t prepare_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           int block_size, int num_seqs, int num_heads, int num_kv_heads,
+                           int head_dim, int num_blocks, int max_blocks_per_seq,
+                           int max_context_len, int partition_size, pa_dtype_t dtype,
+                           void* workspace, size_t workspace_bytes, pa::DecodeParams* p) {
+    int part = 0;
+    pa_status_t st = check_decode_shape(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size,
+                                        partition_size, dtype, &part);
+    if (st != PA_OK) return st;
+    if (num_blocks <= 0 || max_blocks_per_seq <= 0)
+        return fail(PA_ERR_INVALID_ARG, "num_blocks %d and max_blocks_per_seq %d must be positive", num_blocks,
+                    max_blocks_per_seq);
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    const int group = num_heads / num_kv_heads;
     if (static_cast<long long>(max_blocks_per_seq) * block_size < max_context_len)
         return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size = %lld < max_context_len %d",
                     static_cast<long long>(max_blocks_per_seq) * block_size, max_context_len);
@@ -322,6 +345,31 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
     return ws_layout(num_seqs, num_heads, head_dim, pmax_of(max_context_len, part)).total;
 }
 
+pa_status_t pa_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
+                           int block_size, int partition_size, pa_dtype_t dtype, int lds_per_cu,
+                           int lds_per_workgroup, int max_workgroups_per_cu, pa_decode_plan_t* plan) {
+    if (!plan) return fail(PA_ERR_INVALID_ARG, "null plan");
+    if (lds_per_cu <= 0 || lds_per_workgroup <= 0 || max_workgroups_per_cu <= 0)
+        return fail(PA_ERR_INVALID_ARG, "lds_per_cu %d, lds_per_workgroup %d and max_workgroups_per_cu %d must be "
+                    "positive", lds_per_cu, lds_per_workgroup, max_workgroups_per_cu);
+    int part = 0;
+    const pa_status_t st = check_decode_shape(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                                              block_size, partition_size, dtype, &part);
+    if (st != PA_OK) return st;
+    const int group = num_heads / num_kv_heads;
+    pa::DecodePlan pl;
+    if (pa::plan_decode(dtype, head_dim, group, num_seqs, part / block_size, static_cast<size_t>(lds_per_cu),
+                        static_cast<size_t>(lds_per_workgroup), max_workgroups_per_cu, &pl) != PA_OK)
+        return lds_fail(num_seqs, head_dim, group, static_cast<size_t>(lds_per_cu),
+                        static_cast<size_t>(lds_per_workgroup));
+    plan->kernel = pl.kernel;
+    plan->partition_size = part;
+    plan->lds_bytes = static_cast<int>(pl.smem);
+    plan->ring_slots = pl.ring_slots;
+    plan->workgroups_per_cu = pl.resident;
+    return PA_OK;
+}
+
 #define PA_DECODE_ARGS                                                                              \
     out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, num_seqs, num_heads, \
         num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, partition_size,  \
@@ -338,11 +386,12 @@ pa_status_t pa_decode_partitions(void* out, const void* q, const void* k_cache,
     pa_status_t st = prepare_decode(PA_DECODE_ARGS, &p);
     if (st != PA_OK) return st;
     if (num_seqs == 0) return PA_OK;
-    int cus = 0;
-    st = num_cus(&cus);
+    pa::DeviceInfo dv;
+    st = device_info(&dv);
     if (st != PA_OK) return st;
-    hipError_t e = pa::launch_decode_partitions(p, dtype, head_dim, cus, static_cast<hipStream_t>(stream));
-    if (e == hipErrorInvalidConfiguration) return lds_fail(num_seqs, head_dim, num_heads / num_kv_heads);
+    hipError_t e = pa::launch_decode_partitions(p, dtype, head_dim, dv, static_cast<hipStream_t>(stream));
+    if (e == hipErrorInvalidConfiguration)
+        return lds_fail(num_seqs, head_dim, num_heads / num_kv_heads, dv.lds_per_cu, dv.lds_per_wg);
     if (e != hipSuccess) return hip_fail(e, "decode partition kernel launch");
     return PA_OK;
 }
@@ -373,12 +422,13 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void*
     pa_status_t st = prepare_decode(PA_DECODE_ARGS, &p);
     if (st != PA_OK) return st;
     if (num_seqs == 0) return PA_OK;
-    int cus = 0;
-    st = num_cus(&cus);
+    pa::DeviceInfo dv;
+    st = device_info(&dv);
     if (st != PA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = pa::launch_decode_partitions(p, dtype, head_dim, cus, s);
-    if (e == hipErrorInvalidConfiguration) return lds_fail(num_seqs, head_dim, num_heads / num_kv_heads);
+    hipError_t e = pa::launch_decode_partitions(p, dtype, head_dim, dv, s);
+    if (e == hipErrorInvalidConfiguration)
+        return lds_fail(num_seqs, head_dim, num_heads / num_kv_heads, dv.lds_per_cu, dv.lds_per_wg);
     if (e != hipSuccess) return hip_fail(e, "decode partition kernel launch");
     e = pa::launch_decode_merge(p, dtype, head_dim, s);
     if (e != hipSuccess) return hip_fail(e, "decode merge kernel launch");

@@ -206,9 +206,8 @@ __global__ __launch_bounds__(256) void pa_table_append_kernel(int32_t* __restric
 hipError_t launch_table_append(int32_t* tables, int max_blocks, const int32_t* lens, const int32_t* slots,
                                int num_seqs, int block_size, hipStream_t stream) {
     if (num_seqs == 0) return hipSuccess;
-    hipLaunchKernelGGL(pa_table_append_kernel, dim3(static_cast<unsigned>((num_seqs + 255) / 256)), dim3(256), 0,
-                       stream, tables, max_blocks, lens, slots, num_seqs, ilog2(block_size));
-    return hipGetLastError();
+    return launch_kernel(pa_table_append_kernel, dim3(static_cast<unsigned>((num_seqs + 255) / 256)), dim3(256), 0,
+                         stream, tables, max_blocks, lens, slots, num_seqs, ilog2(block_size));
 }
 
 // The same append with the step's lengths and slots carried in the launch
@@ -256,8 +255,7 @@ hipError_t launch_stage_append(int32_t* tables, int max_blocks, const int32_t* h
         a.log2_bs = log2_bs;
         std::memcpy(a.lens, host_lens + i0, sizeof(int32_t) * n);
         std::memcpy(a.slots, host_slots + i0, sizeof(int32_t) * n);
-        hipLaunchKernelGGL(pa_stage_append_kernel, dim3(1), dim3(kStageSeqs), 0, stream, a);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = launch_kernel(pa_stage_append_kernel, dim3(1), dim3(kStageSeqs), 0, stream, a);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -286,28 +284,23 @@ hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void*
     const long long pool_slots = static_cast<long long>(num_blocks) * block_size;
     const unsigned chunks = static_cast<unsigned>((num_tokens + (1 << log2_chunk) - 1) >> log2_chunk);
     const dim3 grid(chunks, static_cast<unsigned>(num_kv_heads), static_cast<unsigned>(num_layers));
-    if (elem_bytes == 2) {
-        hipLaunchKernelGGL(pa_write_kernel<uint16_t>, grid, dim3(256), smem, stream,
-                           static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
-                           static_cast<u32x4*>(k_cache), static_cast<uint16_t*>(v_cache), slots, num_tokens,
-                           num_kv_heads, head_dim, row16, log2_bs, log2_vt, log2_chunk, log2_win, pool_slots);
-    } else {
-        hipLaunchKernelGGL(pa_write_kernel<uint32_t>, grid, dim3(256), smem, stream,
-                           static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
-                           static_cast<u32x4*>(k_cache), static_cast<uint32_t*>(v_cache), slots, num_tokens,
-                           num_kv_heads, head_dim, row16, log2_bs, log2_vt, log2_chunk, log2_win, pool_slots);
-    }
-    return hipGetLastError();
+    if (elem_bytes == 2)
+        return launch_kernel(pa_write_kernel<uint16_t>, grid, dim3(256), smem, stream,
+                             static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
+                             static_cast<u32x4*>(k_cache), static_cast<uint16_t*>(v_cache), slots, num_tokens,
+                             num_kv_heads, head_dim, row16, log2_bs, log2_vt, log2_chunk, log2_win, pool_slots);
+    return launch_kernel(pa_write_kernel<uint32_t>, grid, dim3(256), smem, stream,
+                         static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
+                         static_cast<u32x4*>(k_cache), static_cast<uint32_t*>(v_cache), slots, num_tokens,
+                         num_kv_heads, head_dim, row16, log2_bs, log2_vt, log2_chunk, log2_win, pool_slots);
 }
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
                               int num_layers, size_t block_bytes, int num_blocks, hipStream_t stream) {
     if (num_pairs == 0 || num_layers == 0) return hipSuccess;
-    hipLaunchKernelGGL(pa_copy_kernel, dim3(static_cast<unsigned>(num_pairs), 2, static_cast<unsigned>(num_layers)),
-                       dim3(256), 0, stream,
-                       static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), pairs,
-                       block_bytes / 16, num_blocks);
-    return hipGetLastError();
+    return launch_kernel(pa_copy_kernel, dim3(static_cast<unsigned>(num_pairs), 2, static_cast<unsigned>(num_layers)),
+                         dim3(256), 0, stream, static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), pairs,
+                         block_bytes / 16, num_blocks);
 }
 
 }  // namespace pa

@@ -44,6 +44,11 @@
 // A sequence that fits one partition is written straight to `out`; longer
 // ones leave one (m, l, o) record per partition for the merge kernel.
 
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -90,8 +95,12 @@ __host__ __device__ constexpr size_t red_stride(int d) { return static_cast<size
 constexpr int kBuckets = 256;
 
 // LDS ints of the schedule: fullpre[S + 1] | plist[S] | lens[S] | bucket[kBuckets]
+// | the build's scratch: wave_tot[kWaves] | wave_cnt[kWaves][kBuckets]. All of
+// it is dynamic LDS, so that the kernels hold no static LDS and a launch's
+// LDS is exactly what the host plan computes.
 __host__ __device__ constexpr size_t sched_ints(int num_seqs) {
-    return static_cast<size_t>((num_seqs + 4) & ~3) + 2 * static_cast<size_t>((num_seqs + 3) & ~3) + kBuckets;
+    return static_cast<size_t>((num_seqs + 4) & ~3) + 2 * static_cast<size_t>((num_seqs + 3) & ~3) + kBuckets +
+           kWaves + static_cast<size_t>(kWaves) * kBuckets;
 }
 
 struct Sched {
@@ -99,6 +108,8 @@ struct Sched {
     int* plist;
     int* lens;   // context lengths, clamped to [0, max_ctx]
     int* bucket;
+    int* wave_tot;  // scratch of build_schedule
+    int* wave_cnt;  // [kWaves][kBuckets], scratch of build_schedule
     int full;    // number of full partitions
     int total;   // number of items
 };
@@ -109,6 +120,8 @@ __device__ __forceinline__ Sched sched_lds(const DecodeParams& p, int* base) {
     sc.plist = sc.fullpre + ((p.num_seqs + 4) & ~3);
     sc.lens = sc.plist + ((p.num_seqs + 3) & ~3);
     sc.bucket = sc.lens + ((p.num_seqs + 3) & ~3);
+    sc.wave_tot = sc.bucket + kBuckets;
+    sc.wave_cnt = sc.wave_tot + kWaves;
     sc.full = sc.total = 0;
     return sc;
 }
@@ -126,8 +139,8 @@ __device__ __forceinline__ int size_class(int r, int part) {
 // (ranks inside a wave come from ballots, not from atomics).
 __device__ void build_schedule(const DecodeParams& p, Sched& sc) {
     static_assert(kBuckets == kThreads, "one size class per thread");
-    __shared__ int wave_tot[kWaves];
-    __shared__ int wave_cnt[kWaves][kBuckets];
+    int* wave_tot = sc.wave_tot;
+    int (*wave_cnt)[kBuckets] = reinterpret_cast<int (*)[kBuckets]>(sc.wave_cnt);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int S = p.num_seqs;
     sc.bucket[tid] = 0;
@@ -1328,22 +1341,17 @@ __global__ __launch_bounds__(64 * kMergeWideWaves) void pa_merge_wide(DecodePara
 }
 
 // ---------------------------------------------------------------------------
-// Host-side dispatch
+// Host-side launch plan and dispatch
 // ---------------------------------------------------------------------------
 
 namespace {
 
-// LDS per compute unit (also the most one workgroup may hold); the result
-// ring gets what the resident workgroups (as many as the kernel's registers
-// allow) leave over. A workgroup's LDS (static + dynamic) is allocated in
-// whole granules, so every fit below is computed on rounded sizes: the
-// occupancy query counts exact bytes, and a grid sized from it can exceed
-// what fits, leaving workgroups to start only when others finish.
-constexpr size_t kLdsPerCu = 160 * 1024;
-constexpr size_t kLdsGranule = 1024;  // at least the hardware's allocation unit
+// A workgroup's LDS is allocated in whole granules, so every fit below is
+// computed on rounded sizes (1 KB is at least the hardware's unit).
+constexpr size_t kLdsGranule = 1024;
 constexpr int kMaxRingSlots = 32;
 
-// Workgroups per compute unit of the MFMA kernel. Its scattered 4 KB tile
+// Workgroups per compute unit of the MFMA kernels. Their scattered 4 KB tile
 // reads run faster from fewer, deeper streams: measured on MI355X, one
 // workgroup per CU is as fast as two or three on the batch-256 grouped-query
 // decode and 10 % faster on the long-context one.
@@ -1351,156 +1359,199 @@ constexpr int kMfmaWgPerCu = 1;
 
 constexpr size_t lds_alloc(size_t bytes) { return (bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule; }
 
-// Ring slots that fit next to `used` bytes of LDS (static + fixed dynamic)
-// when `resident` workgroups share a compute unit; 0 if not even one does.
-int ring_slots_for(size_t used, int d, int g, int resident) {
-    const size_t slot = static_cast<size_t>(ring_slot_floats(g, d)) * sizeof(float);
-    if (lds_alloc(used + slot) > kLdsPerCu) return 0;
-    const size_t share = kLdsPerCu / static_cast<size_t>(resident < 1 ? 1 : resident);
+size_t ring_slot_bytes(int d, int g) { return static_cast<size_t>(ring_slot_floats(g, d)) * sizeof(float); }
+
+// Ring slots that fit next to `used` bytes of LDS when `resident` workgroups
+// share a compute unit of `lds_per_cu` bytes; at least one if a single
+// workgroup of used + one slot fits in `lds_per_wg`, else 0.
+int ring_slots_for(size_t used, int d, int g, int resident, size_t lds_per_cu, size_t lds_per_wg) {
+    const size_t slot = ring_slot_bytes(d, g);
+    if (lds_alloc(used + slot) > lds_per_wg) return 0;
+    const size_t share = std::min(lds_per_wg, lds_per_cu / static_cast<size_t>(resident < 1 ? 1 : resident));
     int n = 1;
     while (n < kMaxRingSlots && lds_alloc(used + static_cast<size_t>(n + 1) * slot) <= share) ++n;
     return n;
 }
 
+// Dynamic LDS of each kernel besides its result ring.
 size_t decode_smem_valu(int num_seqs, int d, int g) {
+    // schedule | table slice | wave partials
     return (sched_ints(num_seqs) + kMaxTableSlice) * sizeof(int) +
            static_cast<size_t>(kWaves) * g * red_stride(d) * sizeof(float);
 }
 
 size_t decode_smem_mfma(int num_seqs, int d, int g) {
-    // prefix | two table slices | two query blocks | two sets of wave partials
+    // schedule | two table slices | two query blocks | one or two sets of wave partials
     const size_t qw = ((static_cast<size_t>(g) * d / 2 + 3) & ~static_cast<size_t>(3));
     return (sched_ints(num_seqs) + 2 * kMaxTableSlice) * sizeof(int) +
            2 * qw * sizeof(uint32_t) +
            (mfma_red_double(g, d) ? 2 : 1) * static_cast<size_t>(kWaves) * g * red_stride(d) * sizeof(float);
 }
 
-// Launch a persistent kernel: as many workgroups as can be resident, with
-// the result ring sized to the LDS the resident workgroups leave free. A
-// configuration whose LDS (static + dynamic) cannot fit one workgroup is
-// refused with hipErrorInvalidConfiguration before anything is launched.
-template <typename K>
-hipError_t launch_persistent(K kern, DecodeParams p, size_t fixed_smem, int d, int g, int num_cus,
-                             int max_per_cu, hipStream_t stream, int ring_multiple = 1) {
-    hipFuncAttributes attr{};
-    hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kern));
-    if (e != hipSuccess) return e;
-    const size_t static_lds = attr.sharedSizeBytes;
-    int occ = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, fixed_smem);
-    if (e != hipSuccess) return e;
-    if (occ < 1) occ = 1;
-    if (max_per_cu > 0 && occ > max_per_cu) occ = max_per_cu;
-    p.ring_slots = ring_slots_for(static_lds + fixed_smem, d, g, occ) / ring_multiple * ring_multiple;
-    if (p.ring_slots < 1) return hipErrorInvalidConfiguration;
-    const size_t smem = fixed_smem + static_cast<size_t>(p.ring_slots) * ring_slot_floats(g, d) * sizeof(float);
-    const size_t alloc = lds_alloc(static_lds + smem);
-    if (alloc > kLdsPerCu) return hipErrorInvalidConfiguration;
-    int resident = 0;  // workgroups per compute unit with the final LDS request
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident, kern, kThreads, smem);
-    if (e != hipSuccess) return e;
-    const int lds_resident = static_cast<int>(kLdsPerCu / alloc);
-    if (lds_resident < resident) resident = lds_resident;
-    if (resident < 1) return hipErrorInvalidConfiguration;
-    if (resident < occ) occ = resident;
-    const long long upper = static_cast<long long>(p.num_seqs) * p.num_kv_heads * p.pmax;
-    long long grid = static_cast<long long>(num_cus) * occ;
-    if (grid > upper) grid = upper;
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), smem, stream, p);
-    return hipGetLastError();
-}
-
-template <int DT, int D, int G>
-hipError_t launch_valu(const DecodeParams& p, int num_cus, hipStream_t stream) {
-    constexpr int step = ValuGeom<Elem<DT>::E, D>::STEP;
-    const size_t fixed = decode_smem_valu(p.num_seqs, D, G);
-    if ((1 << p.log2_bs) >= step)
-        return launch_persistent(pa_decode_valu<DT, D, G, true>, p, fixed, D, G, num_cus, 0, stream);
-    return launch_persistent(pa_decode_valu<DT, D, G, false>, p, fixed, D, G, num_cus, 0, stream);
-}
-
 size_t decode_smem_mfma_wave(int num_seqs, int d, int g) {
-    // prefix | per wave: a table slice and a query block
+    // schedule | per wave: a table slice and a query block
     return (sched_ints(num_seqs) + static_cast<size_t>(kWaves) * kWaveSlice) * sizeof(int) +
            static_cast<size_t>(kWaves) * wave_q_words(g, d) * sizeof(uint32_t);
 }
 
-template <int DT, int D, int G>
-hipError_t launch_mfma(const DecodeParams& p, int num_cus, hipStream_t stream) {
-    if ((p.part >> p.log2_bs) <= kWaveSlice) {
-        const size_t fixed = decode_smem_mfma_wave(p.num_seqs, D, G);
-        const hipError_t e =
-            (1 << p.log2_bs) >= 16
-                ? launch_persistent(pa_decode_mfma_wave<DT, D, G, true>, p, fixed, D, G, num_cus, kMfmaWgPerCu,
-                                    stream, kWaves)
-                : launch_persistent(pa_decode_mfma_wave<DT, D, G, false>, p, fixed, D, G, num_cus, kMfmaWgPerCu,
-                                    stream, kWaves);
-        // hipErrorInvalidConfiguration: the four waves' buffers and rings do
-        // not fit next to this batch's schedule (nothing was launched); one
-        // item per workgroup needs less LDS
-        if (e != hipErrorInvalidConfiguration) return e;
+// Workgroups of kThreads threads that one compute unit can hold for `kern`
+// with `smem` bytes of dynamic LDS, from the runtime's occupancy query, made
+// once per (device, kernel, smem) and then served from a cache.
+hipError_t residency(const void* kern, int dev, size_t smem, int* out) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void*, size_t>, int> cache;
+    const auto key = std::make_tuple(dev, kern, smem);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        const auto it = cache.find(key);
+        if (it != cache.end()) {
+            *out = it->second;
+            return hipSuccess;
+        }
     }
-    const size_t fixed = decode_smem_mfma(p.num_seqs, D, G);
-    if ((1 << p.log2_bs) >= 16)
-        return launch_persistent(pa_decode_mfma<DT, D, G, true>, p, fixed, D, G, num_cus, kMfmaWgPerCu, stream);
-    return launch_persistent(pa_decode_mfma<DT, D, G, false>, p, fixed, D, G, num_cus, kMfmaWgPerCu, stream);
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kThreads, smem);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    cache[key] = n;
+    *out = n;
+    return hipSuccess;
+}
+
+// Launch a persistent kernel as planned: as many workgroups as the plan and
+// the runtime's occupancy for the planned LDS allow on every compute unit.
+hipError_t run_planned(void (*kern)(DecodeParams), DecodeParams p, const DecodePlan& pl, const DeviceInfo& dv,
+                       hipStream_t stream) {
+    int occ = 0;
+    const hipError_t e = residency(reinterpret_cast<const void*>(kern), dv.id, pl.smem, &occ);
+    if (e != hipSuccess) return e;
+    const int resident = std::min(pl.resident, occ);
+    if (resident < 1) return hipErrorInvalidConfiguration;
+    p.ring_slots = pl.ring_slots;
+    const long long upper = static_cast<long long>(p.num_seqs) * p.num_kv_heads * p.pmax;
+    long long grid = static_cast<long long>(dv.cus) * resident;
+    if (grid > upper) grid = upper;
+    if (grid < 1) grid = 1;
+    return launch_kernel(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), pl.smem, stream, p);
+}
+
+template <int DT, int D, int G>
+hipError_t launch_valu(const DecodeParams& p, const DeviceInfo& dv, hipStream_t stream) {
+    constexpr int step = ValuGeom<Elem<DT>::E, D>::STEP;
+    void (*kern)(DecodeParams) =
+        (1 << p.log2_bs) >= step ? pa_decode_valu<DT, D, G, true> : pa_decode_valu<DT, D, G, false>;
+    int occ = 0;  // as many as the registers allow
+    hipError_t e = residency(reinterpret_cast<const void*>(kern), dv.id, 0, &occ);
+    if (e != hipSuccess) return e;
+    DecodePlan pl;
+    if (plan_decode(static_cast<pa_dtype_t>(DT), D, G, p.num_seqs, p.part >> p.log2_bs, dv.lds_per_cu,
+                    dv.lds_per_wg, occ, &pl) != PA_OK)
+        return hipErrorInvalidConfiguration;
+    return run_planned(kern, p, pl, dv, stream);
+}
+
+template <int DT, int D, int G>
+hipError_t launch_mfma(const DecodeParams& p, const DeviceInfo& dv, hipStream_t stream) {
+    DecodePlan pl;
+    if (plan_decode(static_cast<pa_dtype_t>(DT), D, G, p.num_seqs, p.part >> p.log2_bs, dv.lds_per_cu,
+                    dv.lds_per_wg, kMfmaWgPerCu, &pl) != PA_OK)
+        return hipErrorInvalidConfiguration;
+    const bool big = (1 << p.log2_bs) >= 16;
+    void (*kern)(DecodeParams);
+    if (pl.kernel == PA_DECODE_MFMA_WAVE)
+        kern = big ? pa_decode_mfma_wave<DT, D, G, true> : pa_decode_mfma_wave<DT, D, G, false>;
+    else
+        kern = big ? pa_decode_mfma<DT, D, G, true> : pa_decode_mfma<DT, D, G, false>;
+    return run_planned(kern, p, pl, dv, stream);
 }
 
 template <int DT, int D>
-hipError_t launch_d(const DecodeParams& p, int num_cus, hipStream_t stream) {
+hipError_t launch_d(const DecodeParams& p, const DeviceInfo& dv, hipStream_t stream) {
     if constexpr (DT == PA_F32) {
         switch (p.group) {
-            case 1: return launch_valu<DT, D, 1>(p, num_cus, stream);
-            case 2: return launch_valu<DT, D, 2>(p, num_cus, stream);
-            case 4: return launch_valu<DT, D, 4>(p, num_cus, stream);
-            case 8: return launch_valu<DT, D, 8>(p, num_cus, stream);
+            case 1: return launch_valu<DT, D, 1>(p, dv, stream);
+            case 2: return launch_valu<DT, D, 2>(p, dv, stream);
+            case 4: return launch_valu<DT, D, 4>(p, dv, stream);
+            case 8: return launch_valu<DT, D, 8>(p, dv, stream);
         }
     } else {
         switch (p.group) {
-            case 1: return launch_valu<DT, D, 1>(p, num_cus, stream);
-            case 2: return launch_mfma<DT, D, 2>(p, num_cus, stream);
-            case 4: return launch_mfma<DT, D, 4>(p, num_cus, stream);
-            case 8: return launch_mfma<DT, D, 8>(p, num_cus, stream);
-            case 16: return launch_mfma<DT, D, 16>(p, num_cus, stream);
+            case 1: return launch_valu<DT, D, 1>(p, dv, stream);
+            case 2: return launch_mfma<DT, D, 2>(p, dv, stream);
+            case 4: return launch_mfma<DT, D, 4>(p, dv, stream);
+            case 8: return launch_mfma<DT, D, 8>(p, dv, stream);
+            case 16: return launch_mfma<DT, D, 16>(p, dv, stream);
         }
     }
     return hipErrorInvalidValue;
 }
 
 template <int DT>
-hipError_t launch_dt(const DecodeParams& p, int head_dim, int num_cus, hipStream_t stream) {
+hipError_t launch_dt(const DecodeParams& p, int head_dim, const DeviceInfo& dv, hipStream_t stream) {
     switch (head_dim) {
-        case 64: return launch_d<DT, 64>(p, num_cus, stream);
-        case 128: return launch_d<DT, 128>(p, num_cus, stream);
-        case 256: return launch_d<DT, 256>(p, num_cus, stream);
+        case 64: return launch_d<DT, 64>(p, dv, stream);
+        case 128: return launch_d<DT, 128>(p, dv, stream);
+        case 256: return launch_d<DT, 256>(p, dv, stream);
     }
     return hipErrorInvalidValue;
+}
+
+template <int DT, int D>
+hipError_t launch_merge_dd(const DecodeParams& p, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(p.num_heads), static_cast<unsigned>(p.num_seqs));
+    if (p.pmax >= kMergeWideMinParts)
+        return launch_kernel(pa_merge_wide<DT, D>, grid, dim3(64 * kMergeWideWaves), 0, stream, p);
+    return launch_kernel(pa_merge<DT, D>, grid, dim3(64), 0, stream, p);
 }
 
 template <int DT>
 hipError_t launch_merge_d(const DecodeParams& p, int head_dim, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(p.num_heads), static_cast<unsigned>(p.num_seqs));
-    if (p.pmax >= kMergeWideMinParts) {
-        const dim3 block(64 * kMergeWideWaves);
-        switch (head_dim) {
-            case 64: hipLaunchKernelGGL((pa_merge_wide<DT, 64>), grid, block, 0, stream, p); break;
-            case 128: hipLaunchKernelGGL((pa_merge_wide<DT, 128>), grid, block, 0, stream, p); break;
-            case 256: hipLaunchKernelGGL((pa_merge_wide<DT, 256>), grid, block, 0, stream, p); break;
-            default: return hipErrorInvalidValue;
-        }
-        return hipGetLastError();
-    }
     switch (head_dim) {
-        case 64: hipLaunchKernelGGL((pa_merge<DT, 64>), grid, dim3(64), 0, stream, p); break;
-        case 128: hipLaunchKernelGGL((pa_merge<DT, 128>), grid, dim3(64), 0, stream, p); break;
-        case 256: hipLaunchKernelGGL((pa_merge<DT, 256>), grid, dim3(64), 0, stream, p); break;
-        default: return hipErrorInvalidValue;
+        case 64: return launch_merge_dd<DT, 64>(p, stream);
+        case 128: return launch_merge_dd<DT, 128>(p, stream);
+        case 256: return launch_merge_dd<DT, 256>(p, stream);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+pa_status_t plan_decode(pa_dtype_t dt, int head_dim, int group, int num_seqs, int part_blocks, size_t lds_per_cu,
+                        size_t lds_per_wg, int max_per_cu, DecodePlan* out) {
+    struct Candidate {
+        pa_decode_kernel_t kernel;
+        size_t fixed;
+        int cap;       // most resident workgroups per CU
+        int multiple;  // ring slots come in multiples of this (one share per wave)
+    };
+    Candidate c[2];
+    int n = 0;
+    const int regs = max_per_cu < 1 ? 1 : max_per_cu;
+    if (decode_uses_mfma(dt, group)) {
+        const int cap = std::min(kMfmaWgPerCu, regs);
+        if (part_blocks <= kWaveSlice)
+            c[n++] = {PA_DECODE_MFMA_WAVE, decode_smem_mfma_wave(num_seqs, head_dim, group), cap, kWaves};
+        c[n++] = {PA_DECODE_MFMA, decode_smem_mfma(num_seqs, head_dim, group), cap, 1};
+    } else {
+        c[n++] = {PA_DECODE_VALU, decode_smem_valu(num_seqs, head_dim, group), regs, 1};
+    }
+    for (int i = 0; i < n; ++i) {
+        const int ring = ring_slots_for(c[i].fixed, head_dim, group, c[i].cap, lds_per_cu, lds_per_wg) /
+                         c[i].multiple * c[i].multiple;
+        if (ring < 1) continue;  // (for the wave kernel: the one-item-per-workgroup kernel needs less)
+        const size_t smem = c[i].fixed + static_cast<size_t>(ring) * ring_slot_bytes(head_dim, group);
+        const size_t alloc = lds_alloc(smem);
+        if (alloc > lds_per_wg || alloc > lds_per_cu) continue;
+        const int resident = std::min(c[i].cap, static_cast<int>(lds_per_cu / alloc));
+        if (resident < 1) continue;
+        out->kernel = c[i].kernel;
+        out->smem = smem;
+        out->ring_slots = ring;
+        out->resident = resident;
+        return PA_OK;
+    }
+    return PA_ERR_UNSUPPORTED;
+}
 
 bool decode_uses_mfma(pa_dtype_t dt, int group) { return dt != PA_F32 && group >= 2; }
 
@@ -1524,12 +1575,12 @@ bool decode_supported(pa_dtype_t dt, int head_dim, int group) {
     return false;
 }
 
-hipError_t launch_decode_partitions(const DecodeParams& p, pa_dtype_t dt, int head_dim,
-                                    int num_cus, hipStream_t stream) {
+hipError_t launch_decode_partitions(const DecodeParams& p, pa_dtype_t dt, int head_dim, const DeviceInfo& dv,
+                                    hipStream_t stream) {
     switch (dt) {
-        case PA_F32: return launch_dt<PA_F32>(p, head_dim, num_cus, stream);
-        case PA_BF16: return launch_dt<PA_BF16>(p, head_dim, num_cus, stream);
-        case PA_F16: return launch_dt<PA_F16>(p, head_dim, num_cus, stream);
+        case PA_F32: return launch_dt<PA_F32>(p, head_dim, dv, stream);
+        case PA_BF16: return launch_dt<PA_BF16>(p, head_dim, dv, stream);
+        case PA_F16: return launch_dt<PA_F16>(p, head_dim, dv, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -6,6 +6,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 #include "pa.h"
 
 namespace pa {
@@ -80,9 +83,53 @@ inline int ilog2(int x) {
     return r;
 }
 
+// Launch `kern` and return the status of this launch alone. hipLaunchKernel
+// reports its own error; checking hipGetLastError() after a launch would also
+// return (and clear) an error left behind by an earlier, unrelated HIP call
+// on the thread. The arguments are converted to the kernel's parameter types
+// first and passed by address, as hipLaunchKernel expects.
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kern)(P...), dim3 grid, dim3 block, size_t smem, hipStream_t stream,
+                         A&&... a) {
+    static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+    std::tuple<P...> args(std::forward<A>(a)...);
+    return std::apply(
+        [&](auto&... x) {
+            void* ptrs[] = {static_cast<void*>(&x)...};
+            return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, smem, stream);
+        },
+        args);
+}
+
+// What a launch needs to know of the current device (read once per device).
+struct DeviceInfo {
+    int id;
+    int cus;            // compute units
+    size_t lds_per_cu;  // LDS bytes of one compute unit
+    size_t lds_per_wg;  // LDS bytes one workgroup may hold
+};
+
+// The decode partition kernel a launch runs and its LDS (see pa_decode_plan
+// in pa.h): which kernel, the dynamic LDS per workgroup (the kernels hold no
+// static LDS), the result-ring slots inside it and the workgroups per compute
+// unit.
+struct DecodePlan {
+    pa_decode_kernel_t kernel;
+    size_t smem;
+    int ring_slots;
+    int resident;
+};
+
+// Host-only: no device is queried. max_per_cu is the most workgroups per
+// compute unit the registers of the VALU kernel allow (ignored for the MFMA
+// kernels, which run one per compute unit). PA_ERR_UNSUPPORTED if no kernel
+// for the shape fits the LDS.
+pa_status_t plan_decode(pa_dtype_t dt, int head_dim, int group, int num_seqs, int part_blocks, size_t lds_per_cu,
+                        size_t lds_per_wg, int max_per_cu, DecodePlan* out);
+
 // Return hipSuccess or the launch error.
-hipError_t launch_decode_partitions(const DecodeParams& p, pa_dtype_t dt, int head_dim,
-                                    int num_cus, hipStream_t stream);
+hipError_t launch_decode_partitions(const DecodeParams& p, pa_dtype_t dt, int head_dim, const DeviceInfo& dv,
+                                    hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams& p, pa_dtype_t dt, int head_dim,
                                hipStream_t stream);
 bool decode_supported(pa_dtype_t dt, int head_dim, int group);

@@ -911,9 +911,8 @@ hipError_t launch_prefill_f32_g(const PrefillParams& p, hipStream_t stream) {
     const long long grid = qtiles * p.num_seqs * p.num_kv_heads;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((pa_prefill_f32<D, G>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                       prefill_smem_f32<D>(), stream, p);
-    return hipGetLastError();
+    return launch_kernel(pa_prefill_f32<D, G>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                         prefill_smem_f32<D>(), stream, p);
 }
 
 template <int D>
@@ -935,9 +934,8 @@ hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t stream) {
     const long long grid = qtiles * p.num_seqs * p.num_kv_heads;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((pa_prefill_mfma<DT, D, G>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                       prefill_smem<D>(), stream, p);
-    return hipGetLastError();
+    return launch_kernel(pa_prefill_mfma<DT, D, G>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                         prefill_smem<D>(), stream, p);
 }
 
 template <int DT, int D>

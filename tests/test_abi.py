@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(L.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 8
+    assert lib.pa_abi_version() == 9
 
 
 def test_status_strings_and_workspace_size():
