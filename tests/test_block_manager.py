@@ -1,7 +1,7 @@
 """The native block manager (include/pa_blocks.h) on the CPU: the state the
 tutorial's BlockManager demo ends in (tests/golden/demo_block_manager.json),
 operation-by-operation agreement with the Python pool of workloads/pool.py
-over random scripts, all-or-nothing batches, the consistency check, and
+(a separate design) over random scripts, all-or-nothing batches, the consistency check, and
 error cases. Host code only: no GPU is touched."""
 
 import json
@@ -91,28 +91,18 @@ def test_agrees_with_python_pool_on_random_scripts(seed):
         elif op < 9:
             k = int(rng.integers(1, len(live) + 1))
             batch = [int(x) for x in rng.choice(live, size=k, replace=False)]
-            saved = (list(pool.refs), {s: list(t) for s, t in pool.tables.items()}, dict(pool.used),
-                     list(pool.free))
-            want_slots, want_pairs = [], []
+            before = (pool.refs, pool.tables, pool.used, pool.free)
             try:
-                for s in batch:
-                    slot, cow = pool.append_token(s)
-                    want_slots.append(slot)
-                    if cow is not None:
-                        want_pairs.append(list(cow))
+                want_slots, want_pairs = pool.append_batch(batch)
             except PoolExhausted:
-                # the Python pool is not all-or-nothing: undo, then expect the
-                # native batch to fail without changes
-                pool.refs, pool.used = saved[0], saved[2]
-                pool.tables = saved[1]
-                pool.free.clear()
-                pool.free.extend(saved[3])
+                # both batches are all or nothing
+                assert (pool.refs, pool.tables, pool.used, pool.free) == before
                 with pytest.raises(BlocksExhausted):
                     bm.append(batch)
                 continue
             slots, pairs = bm.append(batch)
             assert slots.tolist() == want_slots
-            assert pairs.tolist() == want_pairs
+            assert pairs.tolist() == [list(p) for p in want_pairs]
         else:
             s = int(rng.choice(live))
             pool.free_seq(s)

@@ -56,9 +56,29 @@ def test_pool_release_and_exhaustion():
 def test_consistency_check_catches_leak():
     pool = HostBlockPool(4, 2)
     pool.prefill("a", 3)
-    pool.refs[0] += 1  # a lost decrement
+    pool._holders[0] += 1  # a lost decrement
     with pytest.raises(AssertionError):
         pool.check_consistency()
+
+
+def test_pool_batch_is_all_or_nothing_and_copies_for_all_but_the_last_sharer():
+    pool = HostBlockPool(6, 4)
+    pool.prefill("p", 6)            # blocks 0, 1 (block 1 half full)
+    pool.share("a", "p", 6)
+    pool.share("b", "p", 6)
+    pool.free_seq("p")              # the two samples keep the blocks
+    slots, pairs = pool.append_batch(["a", "b"])
+    assert pairs == [(1, 2)]                  # the first sharer copies block 1 into block 2
+    assert slots == [2 * 4 + 2, 1 * 4 + 2]    # the last one writes in place
+    pool.prefill("c", 12)           # 3 of the 3 free blocks left
+    before = (pool.refs, pool.tables, pool.used, pool.free)
+    pool.append_batch(["a"])        # still room in block 2
+    with pytest.raises(PoolExhausted):
+        pool.append_batch(["b", "c"])   # c needs a new block: none left
+    assert (pool.refs, pool.used["b"], pool.used["c"]) == (before[0], before[2]["b"], before[2]["c"])
+    with pytest.raises(ValueError):
+        pool.append_batch(["a", "a"])
+    pool.check_consistency()
 
 
 def test_layout_example_workload():

@@ -120,12 +120,12 @@ class Workload:
 def _finish(name, pool: HostBlockPool, seqs, prefill_slots, cow_pairs, writes, *, num_heads,
             num_kv_heads, head_dim, dtype, scale, seed, trap, partition_size=0, ctx_recipe=""):
     pool.check_consistency()
-    lens = np.array([pool.used[s] for s in seqs], dtype=np.int32)
+    lens = np.array([pool.tokens(s) for s in seqs], dtype=np.int32)
     bs = pool.block_size
     width = max(1, max(-(-int(L) // bs) for L in lens))
     tables = np.full((len(seqs), width), trap, dtype=np.int32)
     for i, s in enumerate(seqs):
-        t = pool.tables[s]
+        t = pool.blocks_of(s)
         assert len(t) == -(-int(lens[i]) // bs)
         tables[i, :len(t)] = t
     if trap in set(np.asarray(tables[tables != trap]).tolist()):
@@ -137,7 +137,7 @@ def _finish(name, pool: HostBlockPool, seqs, prefill_slots, cow_pairs, writes, *
         prefill_slots=np.array(sorted(prefill_slots), dtype=np.int64),
         cow_pairs=np.array(cow_pairs, dtype=np.int32).reshape(-1, 2),
         writes=writes, partition_size=partition_size, ctx_recipe=ctx_recipe,
-        refcount_max=max(pool.refs) if pool.refs else 0,
+        refcount_max=max(pool.refs) if pool.num_blocks else 0,
     )
 
 
