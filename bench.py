@@ -72,7 +72,8 @@ def parse():
                          "tokens) and 192 copy-on-write block copies for this many layers: one layered launch "
                          "against one launch per layer")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target duration of the CPU oracle sample")
+                    help="target duration of the all-core CPU oracle sample (the one-thread samples take half "
+                         "and a quarter of it)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="counter-derived HBM bytes per partition-kernel launch, if measured")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -145,37 +146,136 @@ def summarize_counters(fetch_csv, write_csv, out_json, workload, calib_mb, parti
     print(json.dumps(data[workload], indent=1))
 
 
-def cpu_baseline(w, q_h, kc_h, vc_h, seconds: float):
-    """Time the oracle on the batch's sequences, in order and cycling, until
-    about `seconds` of CPU work has been done; single BLAS thread."""
-    import numpy as np
-    import oracle
+def host_cores() -> int:
+    """CPU cores this process may run on (the GPU machine's share of its host)."""
     try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
-    except Exception:  # pragma: no cover - threadpoolctl is installed on this image
-        limiter = None
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - Linux has sched_getaffinity
+        return os.cpu_count() or 1
+
+
+def time_oracle(w, q_h, kc_h, vc_h, seconds: float, threads: int) -> dict:
+    """Time the oracle, unmodified, on the batch's sequences in order and
+    cycling, until about `seconds` of CPU work has been done, with `threads`
+    BLAS threads."""
+    import oracle
+    from threadpoolctl import threadpool_limits
     dt = {"f32": oracle.F32, "bf16": oracle.BF16}[w.dtype]
     done, t_used, kv = 0, 0.0, 0
     e = 4 if w.dtype == "f32" else 2
     t0 = time.perf_counter()
-    while t_used < seconds:
-        i = done % w.num_seqs
-        ts = time.perf_counter()
-        oracle.paged_decode(q_h[i:i + 1], kc_h, vc_h, w.block_tables[i:i + 1], w.context_lens[i:i + 1],
-                            w.scale, w.block_size, dt)
-        t_used += time.perf_counter() - ts
-        kv += 2 * int(w.context_lens[i]) * w.num_kv_heads * w.head_dim * e
-        done += 1
+    with threadpool_limits(limits=threads):
+        while t_used < seconds:
+            i = done % w.num_seqs
+            ts = time.perf_counter()
+            oracle.paged_decode(q_h[i:i + 1], kc_h, vc_h, w.block_tables[i:i + 1], w.context_lens[i:i + 1],
+                                w.scale, w.block_size, dt)
+            t_used += time.perf_counter() - ts
+            kv += 2 * int(w.context_lens[i]) * w.num_kv_heads * w.head_dim * e
+            done += 1
     wall = time.perf_counter() - t0
-    if limiter is not None:
-        limiter.restore_original_limits()
+    return {"gbs": round(kv / t_used / 1e9, 4), "seqs_per_s": round(done / t_used, 3), "threads": threads,
+            "decodes": done, "kv_mb": round(kv / 1e6, 1), "seconds": round(wall, 1)}
+
+
+def cpu_baseline(w, q_h, kc_h, vc_h, seconds: float) -> dict:
+    """The float64 oracle on the host's cores: BLAS threads = the cores this
+    process may use (the reported value), then one thread on the same batch
+    and on the 4-sequence fp32 batch (``tiny``)."""
+    import workloads as W
+    cores = host_cores()
+    allc = time_oracle(w, q_h, kc_h, vc_h, seconds, cores)
+    one = time_oracle(w, q_h, kc_h, vc_h, seconds / 2, 1)
+    t = W.build("tiny")
+    tv = W.make_values(t, device="cpu", poison=False)
+    tiny = time_oracle(t, tv["q"].numpy(), tv["k_cache"].numpy(), tv["v_cache"].numpy(), seconds / 4, 1)
     return {
-        "value": round(kv / t_used / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "seqs_per_s": round(done / t_used, 3),
-        "sample": f"{done} sequence decodes cycling over the {w.num_seqs} sequences of {w.name} "
-                  f"({kv / 1e6:.1f} MB of K+V), float64 numpy oracle, 1 BLAS thread, {wall:.1f} s",
+        "value": allc["gbs"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "seqs_per_s": allc["seqs_per_s"],
+        "sample": f"{allc['decodes']} sequence decodes cycling over the {w.num_seqs} sequences of {w.name} "
+                  f"({allc['kv_mb']} MB of K+V), float64 numpy oracle, {cores} BLAS threads "
+                  f"(= the host cores this process may use), {allc['seconds']} s",
+        "single_thread": {w.name: one, "tiny": tiny},
     }
+
+
+def run_env() -> dict:
+    """GPU, compiler target and software versions of the run."""
+    import platform
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    return {"gpu": torch.cuda.get_device_name(0), "gfx": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hbm_gib": round(props.total_memory / 2 ** 30, 1),
+            "hip": torch.version.hip, "torch": torch.__version__, "python": platform.python_version(),
+            "host_cores": host_cores()}
+
+
+def percentiles(xs) -> dict:
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
+
+
+def per_call_us(fn, calls: int, warmup: int = 10) -> dict:
+    """Time `calls` calls of `fn` one by one, each between two HIP events on
+    the launch stream, after `warmup` untimed calls: median, p10, p90 (us)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return percentiles([1e3 * a.elapsed_time(b) for a, b in evs])
+
+
+def pattern_ceiling(w, kc, vc, dev) -> dict:
+    """The decode's access pattern without its arithmetic: the K and V tiles
+    of every block of every sequence's table (per KV head), read by the
+    bandwidth probe (pa_probe_read_tiles). The best rate over its launch
+    shapes bounds what the decode can reach on this device."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_165_amd as pa
+    hkv, b = w.num_kv_heads, w.block_size
+    parts = []
+    for s in range(w.num_seqs):
+        nb = -(-int(w.context_lens[s]) // b)
+        blocks = w.block_tables[s, :nb].astype(np.int64)
+        parts.append((blocks[None, :] * hkv + np.arange(hkv)[:, None]).ravel())
+    tiles_h = np.concatenate(parts).astype(np.int32)
+    tiles = torch.from_numpy(tiles_h).to(dev)
+    tile_bytes = b * w.head_dim * kc.element_size()
+    nbytes = 2 * len(tiles_h) * tile_bytes
+    sink = torch.empty(16 * 256 * 1024, dtype=torch.uint8, device=dev)
+    best, runs = None, []
+    for u in (1, 2, 4):
+        for wg in (256, 512, 1024):
+            fn = lambda: pa.probe_read_tiles(kc, vc, tiles, u, wg, sink)
+            for _ in range(3):
+                fn()
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(10):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            us = 1e3 * a.elapsed_time(e) / 10
+            gbs = nbytes / (us * 1e-6) / 1e9
+            runs.append({"tiles_in_flight": u, "workgroups": wg, "us": round(us, 2), "gbs": round(gbs, 1)})
+            if best is None or gbs > best["gbs"]:
+                best = runs[-1]
+    return {"gbs": best["gbs"], "us": best["us"], "bytes": nbytes, "tiles": int(len(tiles_h)),
+            "tile_bytes": tile_bytes, "best": {"tiles_in_flight": best["tiles_in_flight"],
+                                               "workgroups": best["workgroups"]},
+            "runs": runs,
+            "what": "K and V tiles of every block in every table row (per KV head), read with the decode's "
+                    "nontemporal 16-byte loads and no arithmetic (pa_probe_read_tiles), best of 9 launch shapes, "
+                    "10 back-to-back launches each; whole tiles, so the last block's empty slots are read too"}
 
 
 def engine_bench(args, dev):
@@ -318,15 +418,13 @@ def cache_layers_bench(args, dev):
 
 def prefill_cpu_baseline(w, q_h, kc_h, vc_h, seconds: float):
     """Time the oracle's paged prefill on the last rows of the workload's
-    sequences, cycling, until about `seconds` of CPU work has been done; one
-    BLAS thread."""
+    sequences, cycling, until about `seconds` of CPU work has been done; BLAS
+    threads = the host cores this process may use."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
-    except Exception:  # pragma: no cover
-        limiter = None
+    from threadpoolctl import threadpool_limits
+    cores = host_cores()
+    limiter = threadpool_limits(limits=cores)
     qs = w.query_start
     rows_per_call = 8
     done, t_used, flops = 0, 0.0, 0
@@ -342,12 +440,11 @@ def prefill_cpu_baseline(w, q_h, kc_h, vc_h, seconds: float):
         flops += 4 * w.head_dim * w.num_heads * sum(L - m + i + 1 for i in range(m))
         done += 1
     wall = time.perf_counter() - t0
-    if limiter is not None:
-        limiter.restore_original_limits()
+    limiter.restore_original_limits()
     return {
-        "value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+        "value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
         "sample": f"{done} calls of the last {rows_per_call} new rows of one sequence, cycling over the "
-                  f"{w.num_seqs} sequences of {w.name}, float64 numpy oracle, 1 BLAS thread, {wall:.1f} s",
+                  f"{w.num_seqs} sequences of {w.name}, float64 numpy oracle, {cores} BLAS threads, {wall:.1f} s",
     }
 
 
@@ -548,6 +645,23 @@ def main():
     achieved = kv / (part_us * 1e-6) / 1e9
     progress(f"step {ms_step * 1e3:.1f} us, partition kernel {part_us:.1f} us per launch")
 
+    # Per-call timings (median, p10, p90 of single calls between two events):
+    # pa_decode (partition kernel + merge) and the partition kernel alone.
+    calls = max(50, args.steps)
+    per_call = {"calls": calls, "warmup": 10,
+                "decode_us": per_call_us(lambda: pa.decode(*dargs), calls),
+                "partition_us": per_call_us(lambda: pa.decode_partitions(*dargs), calls),
+                "timing": "each call between two HIP events on the launch stream (an event pair adds a few us "
+                          "of queue time around the kernel)"}
+    progress(f"per call: decode {per_call['decode_us']}, partition kernel {per_call['partition_us']}")
+    progress("pattern ceiling (bandwidth probe over the same tiles)")
+    ceiling = pattern_ceiling(w, kc, vc, dev)
+    ceiling["decode_kernel_pct_of_ceiling"] = round(100.0 * (kv / (part_us * 1e-6) / 1e9) / ceiling["gbs"], 2)
+    ceiling["decode_kernel_pct_of_ceiling_same_bytes"] = round(
+        100.0 * (ceiling["bytes"] / (part_us * 1e-6) / 1e9) / ceiling["gbs"], 2)
+    progress(f"pattern ceiling {ceiling['gbs']} GB/s ({ceiling['best']}); the partition kernel reaches "
+             f"{ceiling['decode_kernel_pct_of_ceiling']} % of it")
+
     # On-box ceiling next to the peak: a plain device copy of 1 GiB (bytes
     # read plus written, per time), after the timed region.
     cbuf = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
@@ -628,7 +742,12 @@ def main():
                      "kernel_timing": f"{args.steps} back-to-back launches between two HIP events on the launch stream",
                      "bytes_per_launch": kv},
         "cpu_baseline": cpu,
+        "pattern_ceiling": ceiling,
+        "per_call": per_call,
+        "env": run_env(),
     }
+    if w.refcount_max > 1:
+        result["prefix_sharing"] = w.sharing_savings()
     print(json.dumps(result), flush=True)
 
 

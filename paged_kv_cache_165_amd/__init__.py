@@ -33,7 +33,7 @@ __all__ = [
     "PaError", "library", "default_partition_size", "workspace_size", "alloc_workspace",
     "v_tile", "v_cache_shape", "alloc_cache",
     "decode", "decode_partitions", "decode_merge", "append_block_tables", "append_block_tables_host", "prefill", "write_cache", "copy_blocks",
-    "alloc_cache_layers", "write_cache_layers", "copy_blocks_layers",
+    "alloc_cache_layers", "write_cache_layers", "copy_blocks_layers", "decode_plan", "probe_read_tiles",
 ]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16, torch.float16: _lib.PA_F16}
@@ -340,3 +340,33 @@ def copy_blocks_layers(k_cache, v_cache, src_dst_pairs):
     _check(library().pa_copy_blocks_layers(k_cache.data_ptr(), v_cache.data_ptr(), src_dst_pairs.data_ptr(),
                                            src_dst_pairs.shape[0], nl, hkv, bs, d, nb, _DTYPES[k_cache.dtype],
                                            _stream(k_cache)))
+
+
+def decode_plan(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,
+                block_size: int, partition_size: int, dtype: torch.dtype, lds_per_cu: int = 163840,
+                lds_per_workgroup: int = 163840, max_workgroups_per_cu: int = 1) -> dict:
+    """The partition kernel, LDS request and result ring ``decode`` would use
+    for this shape (``pa_decode_plan``, host only)."""
+    plan = _lib.DecodePlan()
+    _check(library().pa_decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size,
+                                    partition_size, _DTYPES[dtype], lds_per_cu, lds_per_workgroup,
+                                    max_workgroups_per_cu, ctypes.byref(plan)))
+    names = {_lib.PA_DECODE_VALU: "valu", _lib.PA_DECODE_MFMA: "mfma", _lib.PA_DECODE_MFMA_WAVE: "mfma_wave"}
+    return {"kernel": names[plan.kernel], "partition_size": plan.partition_size, "lds_bytes": plan.lds_bytes,
+            "ring_slots": plan.ring_slots, "workgroups_per_cu": plan.workgroups_per_cu}
+
+
+def probe_read_tiles(k_cache, v_cache, tiles, tiles_in_flight: int, workgroups: int, sink):
+    """Bandwidth probe (``pa_probe_read_tiles``, include/pa_probe.h): read the
+    K and V tiles listed in ``tiles`` (int32 indices of (block, KV head)
+    tiles) with the decode's loads and no arithmetic. ``sink`` must hold
+    16 * 256 * workgroups bytes."""
+    nb, hkv, bs, d = _check_caches(k_cache, v_cache)
+    _dev_tensor(tiles, "tiles", dtype=torch.int32, ndim=1)
+    _dev_tensor(sink, "sink")
+    if sink.numel() * sink.element_size() < 16 * 256 * workgroups:
+        raise ValueError("sink too small")
+    tile_bytes = bs * d * k_cache.element_size()
+    _check(library().pa_probe_read_tiles(k_cache.data_ptr(), v_cache.data_ptr(), tiles.data_ptr(), tiles.shape[0],
+                                         nb * hkv, tile_bytes, int(tiles_in_flight), int(workgroups),
+                                         sink.data_ptr(), _stream(k_cache)))

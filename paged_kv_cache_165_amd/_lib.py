@@ -1,5 +1,5 @@
-"""ctypes loader for libpa.so, the C-ABI library declared in include/pa.h and
-include/pa_blocks.h.
+"""ctypes loader for libpa.so, the C-ABI library declared in include/pa.h,
+include/pa_blocks.h and include/pa_probe.h.
 
 No compute happens here: this module only loads the shared library and
 declares the argument types of its exported functions. There is no fallback:
@@ -26,7 +26,7 @@ class DecodePlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("partition_size", ctypes.c_int), ("lds_bytes", ctypes.c_int),
                 ("ring_slots", ctypes.c_int), ("workgroups_per_cu", ctypes.c_int)]
 
-# every symbol include/pa.h and include/pa_blocks.h declare
+# every symbol include/pa.h, include/pa_blocks.h and include/pa_probe.h declare
 EXPORTED = (
     "pa_abi_version", "pa_status_string", "pa_last_error", "pa_default_partition_size",
     "pa_decode_workspace_size", "pa_decode_plan", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
@@ -34,7 +34,7 @@ EXPORTED = (
     "pa_append_block_tables", "pa_append_block_tables_host",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_prefill", "pa_bm_share", "pa_bm_append", "pa_bm_free",
     "pa_bm_block_tables", "pa_bm_num_free", "pa_bm_blocks_in_use", "pa_bm_refcount", "pa_bm_seq_tokens",
-    "pa_bm_blocks_without_sharing", "pa_bm_check",
+    "pa_bm_blocks_without_sharing", "pa_bm_check", "pa_probe_read_tiles",
 )
 
 _lock = threading.Lock()
@@ -117,5 +117,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.pa_bm_blocks_without_sharing.argtypes = [_vp]
         lib.pa_bm_check.restype = _i
         lib.pa_bm_check.argtypes = [_vp]
+        lib.pa_probe_read_tiles.restype = _i
+        lib.pa_probe_read_tiles.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
         _lib = lib
         return lib

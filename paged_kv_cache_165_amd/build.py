@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
-SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_cache.hip", "pa_blocks.hip", "pa_prefill.hip"]
+SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_cache.hip", "pa_blocks.hip", "pa_prefill.hip", "pa_probe.hip"]
 ARCH = "gfx950"
 
 

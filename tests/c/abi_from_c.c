@@ -11,6 +11,7 @@
 
 #include "pa.h"
 #include "pa_blocks.h"
+#include "pa_probe.h"
 
 #define CHECK(cond)                                                     \
     do {                                                                \
@@ -34,6 +35,15 @@ int main(void) {
     /* a null pointer is rejected on the host, before anything is launched */
     CHECK(pa_write_cache(NULL, NULL, NULL, NULL, NULL, 4, 8, 128, 16, 64, PA_BF16, NULL) == PA_ERR_INVALID_ARG);
     CHECK(strstr(pa_last_error(), "null") != NULL);
+    CHECK(pa_probe_read_tiles(NULL, NULL, NULL, 4, 64, 4096, 2, 256, NULL, NULL) == PA_ERR_INVALID_ARG);
+
+    /* the host-only launch plan of the GQA batch-256 shape: one item per wave */
+    {
+        pa_decode_plan_t plan;
+        CHECK(pa_decode_plan(256, 32, 8, 128, 8192, 16, 0, PA_BF16, 163840, 163840, 1, &plan) == PA_OK);
+        CHECK(plan.kernel == PA_DECODE_MFMA_WAVE && plan.partition_size == 2048);
+        CHECK(plan.lds_bytes > 0 && plan.lds_bytes <= 163840 && plan.ring_slots >= 4);
+    }
 
     /* 8 blocks of 4 tokens; sequence 0 holds 10 tokens (blocks 0, 1, 2, the
      * last with 2 of 4 slots used), sequence 1 shares all 10 */

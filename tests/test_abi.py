@@ -9,7 +9,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h", "pa_probe.h")]
 
 
 def _lib():
@@ -277,3 +277,22 @@ def test_status_constants_match_header():
                  "PA_ERR_NO_BLOCKS"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == getattr(L, name), name
+
+
+def test_probe_rejects_before_launch():
+    lib, L = _lib()
+    p = ctypes.c_void_p(16)  # aligned, never dereferenced: every case fails on the host
+    odd = ctypes.c_void_p(18)
+    cases = [
+        ((p, p, p, -1, 64, 4096, 2, 256, p), L.PA_ERR_INVALID_ARG),
+        ((p, p, p, 4, 0, 4096, 2, 256, p), L.PA_ERR_INVALID_ARG),
+        ((p, p, p, 4, 64, 4096, 2, 0, p), L.PA_ERR_INVALID_ARG),
+        ((p, p, p, 4, 64, 3000, 2, 256, p), L.PA_ERR_UNSUPPORTED),
+        ((p, p, p, 4, 64, 16384, 2, 256, p), L.PA_ERR_UNSUPPORTED),
+        ((p, p, p, 4, 64, 4096, 3, 256, p), L.PA_ERR_UNSUPPORTED),
+        ((None, p, p, 4, 64, 4096, 2, 256, p), L.PA_ERR_INVALID_ARG),
+        ((odd, p, p, 4, 64, 4096, 2, 256, p), L.PA_ERR_INVALID_ARG),
+    ]
+    for args, status in cases:
+        assert lib.pa_probe_read_tiles(*args, None) == status, args
+    assert lib.pa_probe_read_tiles(None, None, None, 0, 64, 4096, 2, 256, None, None) == 0  # empty list: no-op

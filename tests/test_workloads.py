@@ -160,3 +160,17 @@ def test_prefix_sharing_workload():
     for s in range(256):
         L = int(w.context_lens[s])
         assert 1024 + 1 + 1 <= L <= 1024 + 15 + 1 + 512
+
+
+def test_prefix_sharing_savings_follow_the_tutorial_formula():
+    """aiqz.cc tutorial, section 前缀共享机制: M_saved = N_p x B_block x bytes x (R - 1).
+    The prefix batch shares each prompt's 64 full blocks among its 4 samples
+    (the partly filled 65th is copied by three of them), so N_p = 64 x 64,
+    R = 4, and a block of 16 tokens of 8 KV heads x 128 bf16 values is 32 KB
+    of K plus 32 KB of V."""
+    w = W.build("prefix")
+    m = w.sharing_savings()
+    assert m["shared_blocks_by_refcount"] == {"4": 64 * 64}
+    assert m["block_bytes"] == 2 * 16 * 8 * 128 * 2
+    assert m["m_saved_bytes"] == 64 * 64 * 65536 * 3 == m["m_saved_direct_bytes"]
+    assert W.build("gqa8b").sharing_savings()["m_saved_bytes"] == 0

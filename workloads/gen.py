@@ -99,6 +99,35 @@ class Workload:
                 per_block[pid] = max(per_block.get(pid, 0), min(b, L - t))
         return int(2 * sum(per_block.values()) * self.num_kv_heads * self.head_dim * e)
 
+    def sharing_savings(self) -> dict:
+        """K+V memory that prefix sharing saves on this batch (one layer).
+        The aiqz.cc tutorial (section 前缀共享机制) gives M_saved = N_p x B_block
+        x bytes x (R - 1) for N_p blocks shared by R sequences; here it is
+        summed over the reference counts the tables show, and checked against
+        the direct count: blocks the tables would take without sharing minus
+        the distinct blocks they list."""
+        e = 4 if self.dtype == F32 else 2
+        b = self.block_size
+        block_bytes = 2 * b * self.num_kv_heads * self.head_dim * e  # K and V of one block
+        counts = {}
+        listed = 0
+        for s in range(self.num_seqs):
+            n = -(-int(self.context_lens[s]) // b)
+            listed += n
+            for pid in self.block_tables[s, :n]:
+                counts[int(pid)] = counts.get(int(pid), 0) + 1
+        by_r = {}
+        for r in counts.values():
+            if r > 1:
+                by_r[r] = by_r.get(r, 0) + 1
+        formula = sum(n_p * block_bytes * (r - 1) for r, n_p in by_r.items())
+        direct = (listed - len(counts)) * block_bytes
+        return {"shared_blocks_by_refcount": {str(r): n for r, n in sorted(by_r.items())},
+                "block_bytes": block_bytes, "m_saved_bytes": formula, "m_saved_direct_bytes": direct,
+                "blocks_listed": listed, "blocks_distinct": len(counts),
+                "what": "M_saved = N_p x B_block x bytes x (R - 1) summed over the refcounts R of the shared blocks "
+                        "(aiqz.cc tutorial, 前缀共享机制), one layer of K and V; direct = (listed - distinct) blocks"}
+
     def summary(self) -> dict:
         c = self.context_lens.astype(np.int64)
         return {
