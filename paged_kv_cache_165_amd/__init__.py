@@ -23,6 +23,7 @@ Layouts (see include/pa.h):
 from __future__ import annotations
 
 import ctypes
+import os
 
 import numpy as np
 import torch
@@ -34,6 +35,7 @@ __all__ = [
     "v_tile", "v_cache_shape", "alloc_cache",
     "decode", "decode_partitions", "decode_merge", "append_block_tables", "append_block_tables_host", "prefill", "write_cache", "copy_blocks",
     "alloc_cache_layers", "write_cache_layers", "copy_blocks_layers", "decode_plan", "probe_read_tiles",
+    "debug_enabled", "check_slot_mapping", "check_copy_pairs", "check_decode_inputs",
 ]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16, torch.float16: _lib.PA_F16}
@@ -67,6 +69,76 @@ def _dev_tensor(t: torch.Tensor, name: str, dtype=None, ndim=None) -> torch.Tens
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+# ---------------------------------------------------------------------------
+# Debug precondition checks (PA_DEBUG=1)
+# ---------------------------------------------------------------------------
+#
+# The kernels clamp what they read, so a bad index gives wrong values, never a
+# fault; they cannot tell a caller that broke a precondition. With the
+# environment variable PA_DEBUG=1 the binding copies the index arrays of each
+# call to the host (a synchronizing copy: keep it off timed paths) and checks
+# them first, the debug consistency check the cf-1.com blog describes (4.3).
+# The checks are plain functions of host arrays and can be called directly.
+
+def debug_enabled() -> bool:
+    return os.environ.get("PA_DEBUG", "") == "1"
+
+
+def _host_ints(a) -> np.ndarray:
+    if isinstance(a, torch.Tensor):
+        a = a.detach().to("cpu")
+        return a.numpy()
+    return np.asarray(a)
+
+
+def check_slot_mapping(slot_mapping, num_blocks: int, block_size: int) -> None:
+    """Every slot is -1 (skip) or in [0, num_blocks * block_size), and no two
+    tokens name the same slot (pa_write_cache leaves either value there)."""
+    s = _host_ints(slot_mapping).astype(np.int64).ravel()
+    bad = s[(s < -1) | (s >= num_blocks * block_size)]
+    if bad.size:
+        raise ValueError(f"slot_mapping holds {bad.size} slot(s) outside {{-1}} and [0, {num_blocks * block_size}): "
+                         f"{bad[:4].tolist()}")
+    live = s[s >= 0]
+    u, c = np.unique(live, return_counts=True)
+    if (c > 1).any():
+        raise ValueError(f"slot_mapping names slot(s) {u[c > 1][:4].tolist()} more than once")
+
+
+def check_copy_pairs(src_dst_pairs, num_blocks: int) -> None:
+    """Every id is in [0, num_blocks), every dst is distinct and no dst is
+    also a src (pairs act as if applied at once)."""
+    p = _host_ints(src_dst_pairs).astype(np.int64).reshape(-1, 2)
+    bad = p[(p < 0) | (p >= num_blocks)]
+    if bad.size:
+        raise ValueError(f"src_dst_pairs holds block id(s) outside [0, {num_blocks}): {bad[:4].tolist()}")
+    u, c = np.unique(p[:, 1], return_counts=True)
+    if (c > 1).any():
+        raise ValueError(f"src_dst_pairs copies into block(s) {u[c > 1][:4].tolist()} more than once")
+    both = np.intersect1d(p[:, 0], p[:, 1])
+    if both.size:
+        raise ValueError(f"block(s) {both[:4].tolist()} are both a copy source and a copy destination")
+
+
+def check_decode_inputs(block_tables, context_lens, num_blocks: int, block_size: int, max_context_len: int) -> None:
+    """Every context length is in [0, max_context_len] and every table entry
+    a sequence reads (the first ceil(L / B)) is a block of the pool."""
+    t = _host_ints(block_tables).astype(np.int64)
+    lens = _host_ints(context_lens).astype(np.int64).ravel()
+    bad = np.nonzero((lens < 0) | (lens > max_context_len))[0]
+    if bad.size:
+        raise ValueError(f"context_lens of sequence(s) {bad[:4].tolist()} outside [0, {max_context_len}]")
+    need = -(-lens // block_size)
+    if t.ndim != 2 or (need > t.shape[1]).any():
+        raise ValueError("a context needs more table entries than a row holds")
+    cols = np.arange(t.shape[1])[None, :]
+    read = cols < need[:, None]
+    badt = read & ((t < 0) | (t >= num_blocks))
+    if badt.any():
+        s, j = np.argwhere(badt)[0]
+        raise ValueError(f"block_tables[{s}][{j}] = {t[s, j]} is outside [0, {num_blocks}) and is read")
 
 
 def _stream(t: torch.Tensor) -> ctypes.c_void_p:
@@ -144,6 +216,8 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
         raise ValueError("one block table row and one context length per sequence")
     if max_context_len is None:
         max_context_len = int(context_lens.max().item()) if s else 0  # device -> host read
+    if debug_enabled():
+        check_decode_inputs(block_tables, context_lens, nb, bs, int(max_context_len))
     if workspace is None:
         workspace = alloc_workspace(s, hq, hkv, d, max_context_len, bs, partition_size, q.dtype, device=q.device)
     else:
@@ -217,6 +291,8 @@ def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, s
         max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if s else 0
     if max_context_len is None:
         max_context_len = int(context_lens.max().item()) if s else 0
+    if debug_enabled():
+        check_decode_inputs(block_tables, context_lens, nb, bs, int(max_context_len))
     _check(library().pa_prefill(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                 block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(),
                                 float(scale), bs, s, n, hq, hkv, d, nb, block_tables.shape[1],
@@ -233,6 +309,8 @@ def write_cache(k, v, k_cache, v_cache, slot_mapping):
     n = slot_mapping.shape[0]
     if tuple(k.shape) != (n, hkv, d) or tuple(v.shape) != (n, hkv, d):
         raise ValueError("k and v must be [num_tokens, num_kv_heads, head_dim]")
+    if debug_enabled():
+        check_slot_mapping(slot_mapping, nb, bs)
     _check(library().pa_write_cache(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                     slot_mapping.data_ptr(), n, hkv, d, bs, nb, _DTYPES[k_cache.dtype],
                                     _stream(k_cache)))
@@ -244,6 +322,8 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs):
     _dev_tensor(src_dst_pairs, "src_dst_pairs", dtype=torch.int32, ndim=2)
     if src_dst_pairs.shape[1] != 2:
         raise ValueError("src_dst_pairs must be [num_pairs, 2]")
+    if debug_enabled():
+        check_copy_pairs(src_dst_pairs, nb)
     _check(library().pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src_dst_pairs.data_ptr(),
                                     src_dst_pairs.shape[0], hkv, bs, d, nb, _DTYPES[k_cache.dtype],
                                     _stream(k_cache)))
@@ -326,6 +406,8 @@ def write_cache_layers(k, v, k_cache, v_cache, slot_mapping):
     n = slot_mapping.shape[0]
     if tuple(k.shape) != (nl, n, hkv, d) or tuple(v.shape) != (nl, n, hkv, d):
         raise ValueError("k and v must be [num_layers, num_tokens, num_kv_heads, head_dim]")
+    if debug_enabled():
+        check_slot_mapping(slot_mapping, nb, bs)
     _check(library().pa_write_cache_layers(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                            slot_mapping.data_ptr(), n, nl, hkv, d, bs, nb, _DTYPES[k_cache.dtype],
                                            _stream(k_cache)))
@@ -337,6 +419,8 @@ def copy_blocks_layers(k_cache, v_cache, src_dst_pairs):
     _dev_tensor(src_dst_pairs, "src_dst_pairs", dtype=torch.int32, ndim=2)
     if src_dst_pairs.shape[1] != 2:
         raise ValueError("src_dst_pairs must be [num_pairs, 2]")
+    if debug_enabled():
+        check_copy_pairs(src_dst_pairs, nb)
     _check(library().pa_copy_blocks_layers(k_cache.data_ptr(), v_cache.data_ptr(), src_dst_pairs.data_ptr(),
                                            src_dst_pairs.shape[0], nl, hkv, bs, d, nb, _DTYPES[k_cache.dtype],
                                            _stream(k_cache)))

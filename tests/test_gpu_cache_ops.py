@@ -200,3 +200,29 @@ def test_copy_blocks_matches_oracle(dt, bs):
     torch.cuda.synchronize()
     kc_o, vc_o = oracle.copy_blocks(kc_h, vc_h, pairs)
     assert raw_equal(kc, kc_o) and raw_equal(vc, vc_o)
+
+
+def test_debug_mode_rejects_broken_preconditions_before_the_call(monkeypatch):
+    """With PA_DEBUG=1 the binding checks the index arrays on the host first:
+    duplicate slots, repeated copy destinations and a destination that is
+    also a source are rejected and the caches stay untouched."""
+    pa = _pa()
+    monkeypatch.setenv("PA_DEBUG", "1")
+    nb, hkv, bs, d = 8, 2, 16, 64
+    kc, vc = pa.alloc_cache(nb, hkv, bs, d, torch.bfloat16, device=DEV)
+    kc.zero_()
+    vc.zero_()
+    g = torch.Generator(device=DEV).manual_seed(3)
+    k = _rand((2, hkv, d), torch.bfloat16, g)
+    v = _rand((2, hkv, d), torch.bfloat16, g)
+    with pytest.raises(ValueError, match="more than once"):
+        pa.write_cache(k, v, kc, vc, torch.tensor([5, 5], dtype=torch.int32, device=DEV))
+    with pytest.raises(ValueError, match="more than once"):
+        pa.copy_blocks(kc, vc, torch.tensor([[1, 2], [3, 2]], dtype=torch.int32, device=DEV))
+    with pytest.raises(ValueError, match="both a copy source"):
+        pa.copy_blocks(kc, vc, torch.tensor([[1, 2], [2, 3]], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert int(kc.view(torch.int16).abs().sum()) == 0 and int(vc.view(torch.int16).abs().sum()) == 0
+    pa.write_cache(k, v, kc, vc, torch.tensor([5, 6], dtype=torch.int32, device=DEV))  # valid: goes through
+    torch.cuda.synchronize()
+    assert torch.equal(kc[0, :, 5].view(torch.int16), k[0].view(torch.int16))
