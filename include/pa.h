@@ -231,6 +231,29 @@ pa_status_t pa_decode_merge(void* out, const void* q, const void* k_cache, const
                             void* stream);
 
 /*
+ * pa_decode for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * result and errors as pa_decode without the workspace: the split-K records
+ * go to a scratch array the library holds in device memory (one copy per GPU
+ * it runs on, PA_NOALLOC_SCRATCH_BYTES bytes, kept until the process ends).
+ * The call allocates nothing: no hipMalloc or hipFree, no allocating library
+ * routine. A shape whose records (pa_decode_workspace_size for the same
+ * arguments) exceed the scratch is refused with PA_ERR_UNSUPPORTED before
+ * anything is launched. The scratch needs no contents between calls (every
+ * record the merge reads is written by the same call), but every call on one
+ * GPU uses the same scratch: calls that overlap on one GPU (on different
+ * streams, or from several threads) race and give undefined results. The
+ * first call on a device looks up the scratch's device address once
+ * (hipGetSymbolAddress); make it before capturing a graph.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+pa_status_t pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens, float scale,
+                              int block_size, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                              int num_blocks, int max_blocks_per_seq, int max_context_len, int partition_size,
+                              pa_dtype_t dtype, void* stream);
+
+/*
  * Paged prefill attention (several new tokens per sequence).
  *
  * Sequence s holds L = context_lens[s] tokens in its blocks; the last

@@ -35,7 +35,7 @@ __all__ = [
     "v_tile", "v_cache_shape", "alloc_cache",
     "decode", "decode_partitions", "decode_merge", "append_block_tables", "append_block_tables_host", "prefill", "write_cache", "copy_blocks",
     "alloc_cache_layers", "write_cache_layers", "copy_blocks_layers", "decode_plan", "probe_read_tiles",
-    "debug_enabled", "check_slot_mapping", "check_copy_pairs", "check_decode_inputs",
+    "debug_enabled", "check_slot_mapping", "check_copy_pairs", "check_decode_inputs", "decode_noalloc",
 ]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16, torch.float16: _lib.PA_F16}
@@ -239,6 +239,36 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_cont
     args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                         max_context_len, partition_size, workspace)
     _check(library().pa_decode(*args))
+    return out
+
+
+def decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len: int,
+                   partition_size: int = 0):
+    """``decode`` without a workspace and without any allocation
+    (``pa_decode_noalloc``): the split-K records go to the library's static
+    device scratch of ``_lib.NOALLOC_SCRATCH_BYTES`` bytes per GPU. Calls that
+    overlap on one GPU race. ``max_context_len`` is required (reading it from
+    the device would synchronize)."""
+    _dev_tensor(q, "q", ndim=3)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _dev_tensor(out, "out", dtype=q.dtype, ndim=3)
+    if k_cache.dtype != q.dtype:
+        raise ValueError(f"k_cache must be {q.dtype}, got {k_cache.dtype}")
+    nb, hkv, bs, d2 = _check_caches(k_cache, v_cache)
+    _dev_tensor(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev_tensor(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    s, hq, d = q.shape
+    if tuple(out.shape) != (s, hq, d) or d2 != d:
+        raise ValueError("out must have the shape of q, the caches its head_dim")
+    if block_tables.shape[0] != s or context_lens.shape[0] != s:
+        raise ValueError("one block table row and one context length per sequence")
+    if debug_enabled():
+        check_decode_inputs(block_tables, context_lens, nb, bs, int(max_context_len))
+    _check(library().pa_decode_noalloc(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                       block_tables.data_ptr(), context_lens.data_ptr(), float(scale), bs, s, hq,
+                                       hkv, d, nb, block_tables.shape[1], int(max_context_len), int(partition_size),
+                                       _DTYPES[q.dtype], _stream(q)))
     return out
 
 

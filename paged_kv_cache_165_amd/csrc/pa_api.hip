@@ -39,6 +39,14 @@ using pa::kMaxTableSlice;
 
 thread_local std::string g_last_error;
 
+// Scratch of pa_decode_noalloc: the split-K records live here instead of in a
+// caller's workspace. Each GPU the library runs on holds its own copy until
+// the process ends. Host code must not use the array's name as an address:
+// it is a host-side stand-in; the device address comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+constexpr size_t kNoAllocScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 }  // namespace
 
 namespace pa {
@@ -108,6 +116,29 @@ pa_status_t device_info(pa::DeviceInfo* out) {
     pa::DeviceInfo d{dev, cus, static_cast<size_t>(lds_cu), static_cast<size_t>(lds_wg)};
     cache[dev] = d;
     *out = d;
+    return PA_OK;
+}
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device with that device current and kept.
+pa_status_t noalloc_scratch(void** out) {
+    static std::mutex mu;
+    static std::unordered_map<int, void*> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) {
+        *out = it->second;
+        return PA_OK;
+    }
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    cache[dev] = ptr;
+    *out = ptr;
     return PA_OK;
 }
 
@@ -433,6 +464,32 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void*
     e = pa::launch_decode_merge(p, dtype, head_dim, s);
     if (e != hipSuccess) return hip_fail(e, "decode merge kernel launch");
     return PA_OK;
+}
+
+pa_status_t pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens, float scale,
+                              int block_size, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                              int num_blocks, int max_blocks_per_seq, int max_context_len, int partition_size,
+                              pa_dtype_t dtype, void* stream) {
+    // the same shape checks and record sizing as pa_decode (no device query)
+    int part = 0;
+    pa_status_t st = check_decode_shape(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size,
+                                        partition_size, dtype, &part);
+    if (st != PA_OK) return st;
+    const size_t need = ws_layout(num_seqs, num_heads, head_dim, pmax_of(max_context_len, part)).total;
+    if (need > kNoAllocScratchBytes)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_noalloc: %d sequences x %d heads x %d partitions of %d tokens "
+                    "need %zu bytes of split-K records, more than the %zu bytes of its static scratch (use "
+                    "pa_decode with a workspace, or longer partitions)", num_seqs, num_heads,
+                    pmax_of(max_context_len, part), part, need, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if (need > 0 && num_seqs > 0) {
+        st = noalloc_scratch(&ws);
+        if (st != PA_OK) return st;
+    }
+    return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, num_seqs, num_heads,
+                     num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, part, dtype, ws,
+                     ws ? kNoAllocScratchBytes : 0, stream);
 }
 
 pa_status_t pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -1,0 +1,91 @@
+"""pa_decode_noalloc (include/pa.h) through the C ABI against pa_decode with a
+caller's workspace: two calls in a row on one GPU, the second with a smaller
+batch, each bit for bit equal to pa_decode on the same inputs (same kernels,
+same partitions, deterministic reductions), and a shape whose records exceed
+the static scratch refused before anything runs."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _lib():
+    from paged_kv_cache_165_amd import _lib as L
+    return L.load(), L
+
+
+def _args(w, out, q, kc, vc, tables, lens, max_ctx, part):
+    return (out.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), tables.data_ptr(), lens.data_ptr(),
+            ctypes.c_float(w.scale), w.block_size, q.shape[0], w.num_heads, w.num_kv_heads, w.head_dim,
+            w.num_blocks, tables.shape[1], max_ctx, part, 1)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def test_noalloc_matches_decode_with_workspace_on_two_calls():
+    lib, L = _lib()
+    import paged_kv_cache_165_amd as pa
+    w = W.build("gqa8b")
+    v = W.make_values(w, device=DEV, poison=True)
+    q, kc, vc = v["q"], v["k_cache"], v["v_cache"]
+    (k_new, v_new), = v["writes"]  # every sequence's last token: the one slot left NaN
+    pa.write_cache(k_new, v_new, kc, vc, torch.from_numpy(w.writes[0].slots).to(DEV))
+    tables = torch.from_numpy(w.block_tables).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    # call 1: the whole batch (records of 256 x 32 heads x 4 partitions)
+    # call 2: its first 48 sequences, shorter contexts, a shorter partition
+    lens2_h = np.minimum(w.context_lens[:48], 3000).astype(np.int32)
+    cases = [(q, tables, lens, w.max_context_len, 0),
+             (q[:48].contiguous(), tables[:48].contiguous(), torch.from_numpy(lens2_h).to(DEV),
+              int(lens2_h.max()), 512)]
+    for i, (qq, tt, ll, mctx, part) in enumerate(cases):
+        part_r = part or pa.default_partition_size(qq.shape[0], w.num_heads, w.num_kv_heads, mctx, w.block_size,
+                                                   torch.bfloat16)
+        need = pa.workspace_size(qq.shape[0], w.num_heads, w.num_kv_heads, w.head_dim, mctx, w.block_size, part_r,
+                                 torch.bfloat16)
+        assert 0 < need <= L.NOALLOC_SCRATCH_BYTES, (i, need)
+        ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        ref = torch.full_like(qq, float("nan"))
+        got = torch.full_like(qq, float("nan"))
+        a_ref = _args(w, ref, qq, kc, vc, tt, ll, mctx, part)
+        assert lib.pa_decode(*a_ref, ctypes.c_void_p(ws.data_ptr()), need, _stream()) == 0, lib.pa_last_error()
+        a_got = _args(w, got, qq, kc, vc, tt, ll, mctx, part)
+        assert lib.pa_decode_noalloc(*a_got, _stream()) == 0, lib.pa_last_error()
+        torch.cuda.synchronize()
+        assert torch.isfinite(got.float()).all(), i
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"call {i} differs from pa_decode"
+
+
+def test_noalloc_refuses_records_beyond_its_scratch():
+    """64 sequences x 32 heads x 256 partitions of 512 tokens need 272 MB of
+    records: refused on the host. (Every buffer is real and every context
+    empty, so nothing could be read out of bounds even if a launch happened.)"""
+    lib, L = _lib()
+    import paged_kv_cache_165_amd as pa
+    s, hq, hkv, d, bs, max_ctx = 64, 32, 8, 128, 16, 131072
+    kc, vc = pa.alloc_cache(4, hkv, bs, d, torch.bfloat16, device=DEV)
+    q = torch.zeros(s, hq, d, dtype=torch.bfloat16, device=DEV)
+    out = torch.empty_like(q)
+    tables = torch.zeros(s, max_ctx // bs, dtype=torch.int32, device=DEV)
+    lens = torch.zeros(s, dtype=torch.int32, device=DEV)
+    assert pa.workspace_size(s, hq, hkv, d, max_ctx, bs, 512, torch.bfloat16) > L.NOALLOC_SCRATCH_BYTES
+    st = lib.pa_decode_noalloc(out.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), tables.data_ptr(),
+                               lens.data_ptr(), ctypes.c_float(0.1), bs, s, hq, hkv, d, 4, tables.shape[1], max_ctx,
+                               512, 1, _stream())
+    assert st == L.PA_ERR_UNSUPPORTED
+    assert b"static scratch" in lib.pa_last_error()
