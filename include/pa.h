@@ -90,7 +90,10 @@ typedef enum pa_status {
 typedef enum pa_decode_kernel {
     PA_DECODE_VALU = 0,      /* vector ALU; one item per workgroup (float32, or one query head per KV head) */
     PA_DECODE_MFMA = 1,      /* matrix cores; one item per workgroup (partitions of more than 128 blocks) */
-    PA_DECODE_MFMA_WAVE = 2  /* matrix cores; one item per wave (partitions of at most 128 blocks) */
+    PA_DECODE_MFMA_WAVE = 2,  /* matrix cores; one item per wave (partitions of at most 128 blocks,
+                                 blocks of fewer than 16 tokens) */
+    PA_DECODE_MFMA_STREAM = 3 /* matrix cores; the batch's tiles split evenly over the waves (partitions of
+                                 at most 128 blocks, blocks of 16 tokens or more) */
 } pa_decode_kernel_t;
 
 /* How pa_decode launches its partition kernel for one shape. */

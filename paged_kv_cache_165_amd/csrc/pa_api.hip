@@ -171,13 +171,27 @@ int resolve_partition(int partition_size, int num_seqs, int num_heads, int num_k
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Workspace: the per-partition records m, l and o, needed only when some
-// sequence can span several partitions.
+// sequence can span several partitions. The stream kernel keeps no
+// per-partition records (a wave merges the partitions of its stretch of a
+// pair itself): one (first wave, later waves) pair per (sequence, KV head),
+// and a tail and a head record, of every query head of a group, per wave of
+// its grid.
 struct WsLayout {
-    size_t m_off, l_off, o_off, total;
+    size_t m_off, l_off, o_off, meta_off, xm_off, xl_off, xo_off, total;
 };
 
-WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int pmax) {
+WsLayout ws_layout(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int pmax, bool stream) {
     WsLayout w{};
+    if (stream) {
+        const size_t pairs = static_cast<size_t>(num_seqs) * num_kv_heads;
+        const size_t xrecs = 2 * static_cast<size_t>(pa::kMaxStreamWaves) * (num_heads / num_kv_heads);
+        w.meta_off = 0;
+        w.xm_off = align256(pairs * 2 * sizeof(int));
+        w.xl_off = w.xm_off + align256(xrecs * sizeof(float));
+        w.xo_off = w.xl_off + align256(xrecs * sizeof(float));
+        w.total = w.xo_off + align256(xrecs * head_dim * sizeof(float));
+        return w;
+    }
     if (pmax <= 1) return w;  // single-partition sequences never write records
     const size_t recs = static_cast<size_t>(num_seqs) * num_heads * pmax;
     w.m_off = 0;
@@ -251,7 +265,8 @@ pa_status_t prepare_decode(void* out, const void* q, const void* k_cache, const 
         if (out == q) return fail(PA_ERR_INVALID_ARG, "out aliases q");
     }
     const int pmax = pmax_of(max_context_len, part);
-    const WsLayout ws = ws_layout(num_seqs, num_heads, head_dim, pmax);
+    const bool stream = pa::decode_stream(dtype, group, block_size, part, num_seqs, num_kv_heads, max_context_len);
+    const WsLayout ws = ws_layout(num_seqs, num_heads, num_kv_heads, head_dim, pmax, stream);
     if (ws.total > 0 && num_seqs > 0) {
         if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes required", ws.total);
         if (workspace_bytes < ws.total)
@@ -265,9 +280,14 @@ pa_status_t prepare_decode(void* out, const void* q, const void* k_cache, const 
     p->v_cache = v_cache;
     p->block_tables = block_tables;
     p->context_lens = context_lens;
-    p->ws_m = ws.total ? reinterpret_cast<float*>(wsb + ws.m_off) : nullptr;
-    p->ws_l = ws.total ? reinterpret_cast<float*>(wsb + ws.l_off) : nullptr;
-    p->ws_o = ws.total ? reinterpret_cast<float*>(wsb + ws.o_off) : nullptr;
+    p->ws_m = ws.total && !stream ? reinterpret_cast<float*>(wsb + ws.m_off) : nullptr;
+    p->ws_l = ws.total && !stream ? reinterpret_cast<float*>(wsb + ws.l_off) : nullptr;
+    p->ws_o = ws.total && !stream ? reinterpret_cast<float*>(wsb + ws.o_off) : nullptr;
+    p->ws_meta = stream && ws.total ? reinterpret_cast<int*>(wsb + ws.meta_off) : nullptr;
+    p->ws_xm = stream && ws.total ? reinterpret_cast<float*>(wsb + ws.xm_off) : nullptr;
+    p->ws_xl = stream && ws.total ? reinterpret_cast<float*>(wsb + ws.xl_off) : nullptr;
+    p->ws_xo = stream && ws.total ? reinterpret_cast<float*>(wsb + ws.xo_off) : nullptr;
+    p->stream = stream ? 1 : 0;
     p->scale_log2 = scale * 1.4426950408889634f;
     p->num_seqs = num_seqs;
     p->num_heads = num_heads;
@@ -373,7 +393,9 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
         return 0;
     const int part =
         resolve_partition(partition_size, num_seqs, num_heads, num_kv_heads, max_context_len, block_size, dtype);
-    return ws_layout(num_seqs, num_heads, head_dim, pmax_of(max_context_len, part)).total;
+    const bool stream = pa::decode_stream(dtype, num_heads / num_kv_heads, block_size, part, num_seqs, num_kv_heads,
+                                          max_context_len);
+    return ws_layout(num_seqs, num_heads, num_kv_heads, head_dim, pmax_of(max_context_len, part), stream).total;
 }
 
 pa_status_t pa_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
@@ -388,8 +410,10 @@ pa_status_t pa_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int he
                                               block_size, partition_size, dtype, &part);
     if (st != PA_OK) return st;
     const int group = num_heads / num_kv_heads;
+    const bool stream =
+        pa::decode_stream(dtype, group, block_size, part, num_seqs, num_kv_heads, max_context_len);
     pa::DecodePlan pl;
-    if (pa::plan_decode(dtype, head_dim, group, num_seqs, part / block_size, static_cast<size_t>(lds_per_cu),
+    if (pa::plan_decode(dtype, head_dim, group, num_seqs, part / block_size, stream, static_cast<size_t>(lds_per_cu),
                         static_cast<size_t>(lds_per_workgroup), max_workgroups_per_cu, &pl) != PA_OK)
         return lds_fail(num_seqs, head_dim, group, static_cast<size_t>(lds_per_cu),
                         static_cast<size_t>(lds_per_workgroup));
@@ -476,7 +500,10 @@ pa_status_t pa_decode_noalloc(void* out, const void* q, const void* k_cache, con
     pa_status_t st = check_decode_shape(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size,
                                         partition_size, dtype, &part);
     if (st != PA_OK) return st;
-    const size_t need = ws_layout(num_seqs, num_heads, head_dim, pmax_of(max_context_len, part)).total;
+    const bool split = pa::decode_stream(dtype, num_heads / num_kv_heads, block_size, part, num_seqs, num_kv_heads,
+                                         max_context_len);
+    const size_t need =
+        ws_layout(num_seqs, num_heads, num_kv_heads, head_dim, pmax_of(max_context_len, part), split).total;
     if (need > kNoAllocScratchBytes)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode_noalloc: %d sequences x %d heads x %d partitions of %d tokens "
                     "need %zu bytes of split-K records, more than the %zu bytes of its static scratch (use "

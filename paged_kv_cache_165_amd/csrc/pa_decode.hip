@@ -1243,6 +1243,550 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma_wave(DecodeParams p) 
     }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA kernel, even tile streams
+// ---------------------------------------------------------------------------
+//
+// The per-tile products, softmax and two-deep load schedule of the wave-item
+// kernel, with the work split evenly instead of dealt item by item. The
+// batch's (sequence, KV head) pairs, in order, form one stream of 16-token
+// tiles; every tile costs kStreamTileCost units and every pair
+// kStreamPairCost more (its switch). Wave w of W takes the tiles whose cost
+// position falls in [ceil(w C / W), ceil((w + 1) C / W)), C the total: one
+// contiguous run per wave, equal to within a tile, with no queue, counter or
+// barrier between waves.
+//
+// Within a run, each partition of a pair (partition_size tokens) is reduced
+// on its own (running max, sum and weighted V rows), and the partitions of
+// one pair that follow each other in the run are merged by the log-sum-exp
+// rule as they end, in registers: split-K records exist only where the work
+// is split between waves. A run therefore holds one segment per pair it
+// touches: a pair it holds whole is written to `out` directly; a pair split
+// between waves w0 < ... < w1 leaves the tail record of w0 (its first part)
+// and the head records of w0 + 1 .. w1 (a run starts inside at most one pair
+// and ends inside at most one), which the merge kernel combines. The wave
+// holding a pair's first tile also stores the pair's (w0, w1 - w0). Results
+// wait in an LDS ring and are stored when it is full or the run ends: a
+// store between the streaming loads holds back the loads issued after it
+// (measured on MI355X: storing each result as soon as it is known, by the
+// reducing wave or by a fifth wave of the workgroup, cost 25-35 % more time
+// on the long-context batch). Empty sequences count as one tile without
+// loads and give zero rows.
+
+constexpr int kStreamTileCost = 4;
+constexpr int kStreamPairCost = 3;
+
+// Result-ring slot of the stream kernel (floats): o[G][D] | m[G] | l[G] |
+// s, kv, kind, n (as ints, padded to 16 bytes).
+__host__ __device__ constexpr int stream_slot_floats(int g, int d) { return ((g * d + 2 * g + 4) + 3) & ~3; }
+
+// Kinds of a segment's result.
+enum : int { kSegDirect = 0, kSegTail = 1, kSegHead = 2 };
+
+// LDS ints of the stream schedule: lens[S] | cs[S + 1] | wave_tot[kWaves]
+__host__ __device__ constexpr size_t stream_sched_ints(int num_seqs) {
+    return static_cast<size_t>((num_seqs + 3) & ~3) + static_cast<size_t>((num_seqs + 4) & ~3) + kWaves;
+}
+
+// Tiles of a sequence of L tokens in the stream (an empty one counts one).
+__device__ __forceinline__ int stream_ntiles(int L) { return L > 0 ? (L + 15) >> 4 : 1; }
+
+// lens[s] = clamped context length, cs[s] = cost of the pairs of sequences
+// before s (cs[S] = C). Every thread of the workgroup takes part.
+__device__ void build_stream_schedule(const DecodeParams& p, int* lens, int* cs, int* wave_tot) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int S = p.num_seqs;
+    if (tid == 0) cs[0] = 0;
+    int carry = 0;
+    for (int base = 0; base < S; base += kThreads) {
+        const int i = base + tid;
+        int x = 0;
+        if (i < S) {
+            const int L = clamp_ctx(p.context_lens[i], p);
+            lens[i] = L;
+            x = p.num_kv_heads * (kStreamTileCost * stream_ntiles(L) + kStreamPairCost);
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wave_tot[wave] = x;
+        __syncthreads();
+        int add = carry;
+        for (int w = 0; w < wave; ++w) add += wave_tot[w];
+        if (i < S) cs[i + 1] = x + add;
+        carry += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+        __syncthreads();
+    }
+}
+
+// A run's position: pair (s, kv), tile t of the pair; s == num_seqs: none.
+struct StreamCursor {
+    int s, kv, t;
+};
+
+// One piece: a maximal stretch of a wave's run inside one partition of one
+// pair, tokens [t0, t1). seg_start: the piece opens the run's segment of its
+// pair (the run's first piece, or the pair's first tile); pair_start: that
+// segment begins at the pair's first tile; seg_end: the piece closes the
+// segment (the pair's last tile, or the end of the run); wspan: for a piece
+// at the pair's first tile, the number of later waves the pair reaches.
+struct Piece {
+    int s, kv, t0, t1, b0, nblk;
+    int seg_start, pair_start, seg_end, wspan;
+};
+
+struct StreamRun {
+    long long lo, hi;  // cost positions [lo, hi) of this wave's run
+    long long total;   // C
+    int w, weff;       // this wave, waves with a run
+};
+
+__device__ __forceinline__ long long stream_pos(const DecodeParams& p, const int* lens, const int* cs,
+                                                const StreamCursor& c) {
+    const int pc = kStreamTileCost * stream_ntiles(lens[c.s]) + kStreamPairCost;
+    return static_cast<long long>(cs[c.s]) + static_cast<long long>(c.kv) * pc + kStreamPairCost +
+           static_cast<long long>(kStreamTileCost) * c.t;
+}
+
+// The first tile whose position is at least x (x < C).
+__device__ __forceinline__ StreamCursor stream_seek(const DecodeParams& p, const int* lens, const int* cs,
+                                                    long long x) {
+    int lo = 0, hi = p.num_seqs;  // cs[lo] <= x < cs[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cs[mid] <= x) lo = mid; else hi = mid;
+    }
+    StreamCursor c;
+    c.s = lo;
+    const int n = stream_ntiles(lens[lo]);
+    const int pc = kStreamTileCost * n + kStreamPairCost;
+    const long long r = x - cs[lo];
+    c.kv = static_cast<int>(r / pc);
+    const int o = static_cast<int>(r - static_cast<long long>(c.kv) * pc);
+    c.t = o <= kStreamPairCost ? 0 : (o - kStreamPairCost + kStreamTileCost - 1) / kStreamTileCost;
+    if (c.t >= n) {
+        c.t = 0;
+        if (++c.kv == p.num_kv_heads) {
+            c.kv = 0;
+            ++c.s;
+        }
+    }
+    return c;
+}
+
+// The piece at cursor c (which this wave owns; `first`: the run's first
+// piece), and the cursor of the next one (s = num_seqs when the run ends).
+__device__ __forceinline__ Piece stream_piece(const DecodeParams& p, const int* lens, const int* cs,
+                                              const StreamRun& run, const StreamCursor& c, bool first,
+                                              StreamCursor& next) {
+    const int L = lens[c.s];
+    const int n = stream_ntiles(L);
+    const int pc = kStreamTileCost * n + kStreamPairCost;
+    const long long base = static_cast<long long>(cs[c.s]) + static_cast<long long>(c.kv) * pc;
+    const int ptiles = p.part >> 4;
+    const int pidx = c.t / ptiles;
+    const int last_owned = static_cast<int>((run.hi - 1 - base - kStreamPairCost) / kStreamTileCost);
+    const int te = min(min(n, (pidx + 1) * ptiles), last_owned + 1);
+    Piece x;
+    x.s = c.s;
+    x.kv = c.kv;
+    x.t0 = c.t * 16;
+    x.t1 = min(L, te * 16);
+    x.b0 = x.t0 >> p.log2_bs;
+    x.nblk = x.t1 > x.t0 ? ((x.t1 - 1) >> p.log2_bs) - x.b0 + 1 : 0;
+    x.seg_start = first || c.t == 0;
+    x.seg_end = te >= n || te > last_owned;
+    x.pair_start = c.t == 0;  // (meaningful on the segment's first piece)
+    x.wspan = 0;
+    if (c.t == 0) {
+        const long long last = base + kStreamPairCost + static_cast<long long>(kStreamTileCost) * (n - 1);
+        x.wspan = static_cast<int>(last * run.weff / run.total) - run.w;
+    }
+    next = c;
+    next.t = te;
+    if (next.t >= n) {
+        next.t = 0;
+        if (++next.kv == p.num_kv_heads) {
+            next.kv = 0;
+            ++next.s;
+        }
+    }
+    if (next.s < p.num_seqs && stream_pos(p, lens, cs, next) >= run.hi) next.s = p.num_seqs;
+    return x;
+}
+
+// Store one ring slot: a head or tail record of wave `w`, or a pair's rows of
+// `out`; a segment that began at its pair's first tile also stores the pair's
+// (first wave, later waves). Every lane first reads its 16-byte chunks of the
+// rows from LDS, then stores them.
+template <int DT, int D, int G>
+__device__ __forceinline__ void stream_write_slot(const DecodeParams& p, const float* sl, int w, int lane) {
+    using EL = Elem<DT>;
+    constexpr int E = 2;
+    constexpr int OC = G * D / 4;          // 16-byte chunks of the rows
+    constexpr int OCL = (OC + 63) / 64;    // per lane
+    const int* meta = reinterpret_cast<const int*>(sl + G * D + 2 * G);
+    const int s = meta[0], kv = meta[1], kind = meta[2], span = meta[3];
+    f32x4_t ch[OCL];
+#pragma unroll
+    for (int c = 0; c < OCL; ++c) ch[c] = *reinterpret_cast<const f32x4_t*>(sl + 4 * min(lane + 64 * c, OC - 1));
+    const float mv = sl[G * D + (lane < G ? lane : 0)];
+    const float lv = sl[G * D + G + (lane < G ? lane : 0)];
+    if (kind == kSegDirect) {
+        const size_t row0 = static_cast<size_t>(s) * p.num_heads + kv * G;  // first query head row
+#pragma unroll
+        for (int c = 0; c < OCL; ++c) {
+            if (lane + 64 * c < OC) {
+                u32x2 v;
+                v.x = static_cast<uint32_t>(EL::round(ch[c][0])) | (static_cast<uint32_t>(EL::round(ch[c][1])) << 16);
+                v.y = static_cast<uint32_t>(EL::round(ch[c][2])) | (static_cast<uint32_t>(EL::round(ch[c][3])) << 16);
+                *reinterpret_cast<u32x2*>(static_cast<char*>(p.out) + (row0 * D + 4 * (lane + 64 * c)) * E) = v;
+            }
+        }
+    } else {
+        const size_t x0 = (static_cast<size_t>(kind == kSegTail ? 0 : kMaxStreamWaves) + w) * G;
+#pragma unroll
+        for (int c = 0; c < OCL; ++c)
+            if (lane + 64 * c < OC) *reinterpret_cast<f32x4_t*>(p.ws_xo + x0 * D + 4 * (lane + 64 * c)) = ch[c];
+        if (lane < G) {
+            p.ws_xm[x0 + lane] = mv;
+            p.ws_xl[x0 + lane] = lv;
+        }
+    }
+    if (kind != kSegHead && lane == 0)
+        *reinterpret_cast<int2*>(p.ws_meta + 2 * (static_cast<size_t>(s) * p.num_kv_heads + kv)) = make_int2(w, span);
+}
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
+    static_assert(DT == PA_BF16 || DT == PA_F16, "MFMA path is for 16-bit elements");
+    static_assert(G == 2 || G == 4 || G == 8 || G == 16, "group size");
+    constexpr int E = 2;
+    constexpr int NK = D / 32;
+    constexpr int NV = D / 16;
+    constexpr int QW = G * D / 2;
+    constexpr int QWP = wave_q_words(G, D);
+    constexpr int QPL = (QW + 63) / 64;
+    constexpr int TPL = kWaveSlice / 64;
+    constexpr float kLazy = 8.f;
+    constexpr int SL = stream_slot_floats(G, D);
+
+    // LDS: schedule | tbl[kWaves][kWaveSlice] | qs[kWaves][QWP] | ring[kWaves][wring]
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int* lens = reinterpret_cast<int*>(smem);
+    int* cs = lens + ((p.num_seqs + 3) & ~3);
+    int* wave_tot = cs + ((p.num_seqs + 4) & ~3);
+    int* tbl_all = reinterpret_cast<int*>(smem) + stream_sched_ints(p.num_seqs);
+    uint32_t* qs_all = reinterpret_cast<uint32_t*>(tbl_all + kWaves * kWaveSlice);
+    float* ring_all = reinterpret_cast<float*>(qs_all + kWaves * QWP);
+    const int wring = p.ring_slots / kWaves;
+    int* tbl = tbl_all + wave * kWaveSlice;
+    uint32_t* qs = qs_all + wave * QWP;
+    float* ring = ring_all + wave * wring * SL;
+    int nring = 0;
+
+    const int r16 = lane & 15;
+    const int j = lane >> 4;
+    const int bs = 1 << p.log2_bs;
+    const int hkv = p.num_kv_heads;
+    const size_t blk_el = static_cast<size_t>(bs) * D;
+    const char* kbase = static_cast<const char*>(p.k_cache);
+    const char* vbase = static_cast<const char*>(p.v_cache);
+    const uint32_t* qwords = static_cast<const uint32_t*>(p.q);
+
+    if (p.num_seqs == 0) return;
+    build_stream_schedule(p, lens, cs, wave_tot);  // the last barrier of the kernel
+    StreamRun run;
+    run.total = cs[p.num_seqs];
+    // every run spans at least 8 cost units, so that each owns a tile
+    const long long wmax = static_cast<long long>(gridDim.x) * kWaves;
+    run.weff = static_cast<int>(min(wmax, max(1ll, run.total / 8)));
+    run.w = blockIdx.x * kWaves + wave;
+    if (run.w >= run.weff) return;
+    run.lo = (static_cast<long long>(run.w) * run.total + run.weff - 1) / run.weff;
+    run.hi = (static_cast<long long>(run.w + 1) * run.total + run.weff - 1) / run.weff;
+
+    struct Buf {
+        u32x4 k[NK];
+        u32x2 v[NV];
+    };
+    auto ntiles_of = [](const Piece& x) { return x.t1 > x.t0 ? (x.t1 - x.t0 + 15) >> 4 : 0; };
+    auto last4_of = [](const Piece& x) { return x.t1 > x.t0 ? ((x.t1 - 1) >> 2) << 2 : 0; };
+    auto q_word0 = [&](const Piece& x) {
+        return (static_cast<size_t>(x.s) * p.num_heads + x.kv * G) * (D / 2);
+    };
+    auto clamp_pid = [&](int pid) { return pid < 0 ? 0 : (pid >= p.num_blocks ? p.num_blocks - 1 : pid); };
+
+    // K/V loads of one 16-token tile: the tile lies in one block (blocks of
+    // 16 tokens or more) and one 16-token V tile, so the bases are scalar
+    auto load_with = [&](const Piece& x, int tile, int pk, Buf& b) {
+        const int tt0 = x.t0 + 16 * tile;
+        const int krow = min(tt0 + r16, x.t1 - 1);
+        const int vtok = min(tt0 + 4 * j, last4_of(x));
+        const int pid = __builtin_amdgcn_readfirstlane(pk);
+        const size_t tile_el = (static_cast<size_t>(pid) * hkv + x.kv) * blk_el;
+        const char* kt = kbase + tile_el * E;
+        const char* vtp = vbase + (tile_el + static_cast<size_t>((tt0 & (bs - 1)) >> 4) * D * 16) * E;
+        const uint32_t ko = static_cast<uint32_t>(((krow & (bs - 1)) * D + 8 * j) * E);
+        const uint32_t vo = static_cast<uint32_t>(((vtok & 15) + 16 * r16) * E);
+#pragma unroll
+        for (int c = 0; c < NK; ++c) b.k[c] = nt_load<u32x4>(kt, ko + 64 * c);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) b.v[v] = nt_load<u32x2>(vtp, vo + 512 * v);
+    };
+    auto tile_block = [&](const Piece& x, const int* tb, int tile) {
+        return tb[(min(x.t0 + 16 * tile, x.t1 - 1) >> p.log2_bs) - x.b0];
+    };
+    auto stage_slice = [&](const Piece& x, int* tb) {
+        const int* trow = p.block_tables + static_cast<size_t>(x.s) * p.max_blocks + x.b0;
+#pragma unroll
+        for (int i = 0; i < TPL; ++i)
+            if (lane + 64 * i < x.nblk) tb[lane + 64 * i] = clamp_pid(trow[lane + 64 * i]);
+    };
+
+    // prologue: the first piece's table slice and query block, its first tile
+    const StreamCursor at = stream_seek(p, lens, cs, run.lo);
+    if (at.s >= p.num_seqs) return;  // (a run of 8 or more units always holds a tile)
+    StreamCursor after;
+    Piece cur = stream_piece(p, lens, cs, run, at, true, after);
+    bool has_next = after.s < p.num_seqs;
+    Piece nxt = cur;
+    if (has_next) {
+        const StreamCursor c2 = after;
+        nxt = stream_piece(p, lens, cs, run, c2, false, after);
+    }
+    stage_slice(cur, tbl);
+    for (int w = lane; w < QW; w += 64) qs[w] = qwords[q_word0(cur) + w];
+    Buf A, B;
+    {
+        int pk = 0;
+        if (ntiles_of(cur) > 0) pk = tile_block(cur, tbl, 0);
+        load_with(cur, 0, pk, A);
+    }
+
+    // the segment's running result: the merged partitions so far (max in
+    // log2 units, this lane's share of the sum, unnormalised V rows)
+    f32x4_t seg_o[NV];
+    float seg_m = -INFINITY, seg_l = 0.f;
+    int seg_kind = kSegDirect, seg_span = 0;
+
+    while (true) {
+        const bool next_tile = has_next && ntiles_of(nxt) > 0;
+        // raw loads of the next piece's metadata, consumed at the end
+        const int* trow = p.block_tables + static_cast<size_t>(nxt.s) * p.max_blocks + nxt.b0;
+        const int* safe = p.context_lens;
+        const int pk_raw = *(next_tile ? trow : safe);
+        int tbl_raw[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i)
+            tbl_raw[i] = *(has_next && lane + 64 * i < nxt.nblk ? trow + lane + 64 * i : safe);
+        uint32_t q_raw[QPL];
+#pragma unroll
+        for (int i = 0; i < QPL; ++i) q_raw[i] = qwords[q_word0(nxt) + min(lane + 64 * i, QW - 1)];
+
+        if (cur.seg_start) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) seg_o[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            seg_m = -INFINITY;
+            seg_l = 0.f;
+            seg_kind = !cur.pair_start ? kSegHead : kSegDirect;
+            seg_span = cur.wspan;
+        }
+        u32x4 qf[NK];
+        {
+            const uint32_t* qrow = qs + (r16 % G) * (D / 2);
+#pragma unroll
+            for (int c = 0; c < NK; ++c) qf[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c + 4 * j);
+        }
+        f32x4_t acc[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        float m_run = -INFINITY, lsum = 0.f;
+        const int t1 = cur.t1;
+        const int ntiles = ntiles_of(cur);
+
+        auto compute_tile = [&](int tile, const Buf& b) {
+            const int tt0 = cur.t0 + 16 * tile;
+            f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NK; ++c) st = mfma_qk<DT>(b.k[c], qf[c], st);
+            float x[4];
+            bool valid[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                valid[r] = tt0 + 4 * j + r < t1;
+                x[r] = valid[r] ? st[r] * p.scale_log2 : -INFINITY;
+            }
+            float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const bool need = tmax > m_run + kLazy;
+            if (__any(need)) {
+                const float mn = need ? tmax : m_run;
+                const float alpha = fast_exp2(m_run - mn);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) acc[v] *= alpha;
+                lsum *= alpha;
+                m_run = mn;
+            }
+            float pr[4];
+            u32x2 pb;
+            pb.x = pack2<DT>(fast_exp2(x[0] - m_run), fast_exp2(x[1] - m_run), pr[0], pr[1]);
+            pb.y = pack2<DT>(fast_exp2(x[2] - m_run), fast_exp2(x[3] - m_run), pr[2], pr[3]);
+            lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            const uint32_t mask0 = (valid[0] ? 0xffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
+            const uint32_t mask1 = (valid[2] ? 0xffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                u32x2 a = b.v[v];
+                a.x &= mask0;
+                a.y &= mask1;
+                acc[v] = mfma_pv<DT>(a, pb, acc[v]);
+            }
+        };
+        auto load_tile = [&](int tile, Buf& b) { load_with(cur, tile, tile_block(cur, tbl, tile), b); };
+        auto load_next = [&](Buf& b) {
+            int pk = pk_raw;
+            asm volatile("" : "+v"(pk));
+            if (next_tile) load_with(nxt, 0, clamp_pid(pk), b);
+            else load_with(cur, 0, 0, b);
+        };
+
+        // the piece's tiles, two deep
+        int t = 0;
+        if (ntiles > 0) {
+            for (int i = 0; i < ((ntiles - 1) >> 1); ++i) {
+                load_tile(t + 1, B);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_tile(t, A);
+                __builtin_amdgcn_sched_barrier(0);
+                load_tile(t + 2, A);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_tile(t + 1, B);
+                t += 2;
+            }
+            if (ntiles & 1) {
+                compute_tile(t, A);
+            } else {
+                load_tile(t + 1, B);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_tile(t, A);
+                compute_tile(t + 1, B);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_next(A);
+        asm volatile("" ::"v"(pk_raw));
+
+        // the partition (piece) joins the segment by the log-sum-exp rule:
+        // both sides are rescaled to the larger max (m_run is the same on
+        // the four lanes of a column, and sums stay per lane)
+        {
+            const float mn = fmaxf(seg_m, m_run);
+            const float mu = mn == -INFINITY ? 0.f : mn;
+            const float a = fast_exp2(seg_m - mu), b = fast_exp2(m_run - mu);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) seg_o[v] = seg_o[v] * a + acc[v] * b;
+            seg_l = seg_l * a + lsum * b;
+            seg_m = mn;
+        }
+
+        if (cur.seg_end) {
+            // seg_o[v][r] = O^T[d = 16v + 4j + r][head column r16]; the sum
+            // over the column's four lanes
+            float l = seg_l;
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            // a segment that began at the pair's first tile and stops short of
+            // its last is the pair's tail record
+            const bool pair_done = cur.t1 >= lens[cur.s];
+            const int kind = seg_kind == kSegHead ? kSegHead : (pair_done ? kSegDirect : kSegTail);
+            float* slot = ring + nring * SL;
+            if (r16 < G) {
+                const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    *reinterpret_cast<f32x4_t*>(slot + r16 * D + 16 * v + 4 * j) = seg_o[v] * inv;
+                if (j == 0) {
+                    slot[G * D + r16] = seg_m;
+                    slot[G * D + G + r16] = l;
+                }
+            }
+            if (lane == 0) {
+                int* meta = reinterpret_cast<int*>(slot + G * D + 2 * G);
+                meta[0] = cur.s;
+                meta[1] = cur.kv;
+                meta[2] = kind;
+                meta[3] = seg_span;
+            }
+            ++nring;
+        }
+        // the next piece's table slice and query block (unconditional stores:
+        // every path consumes the raw loads)
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) tbl[lane + 64 * i] = clamp_pid(tbl_raw[i]);
+#pragma unroll
+        for (int i = 0; i < QPL; ++i) qs[min(lane + 64 * i, QW - 1)] = q_raw[i];
+        if (nring == wring || !has_next) {
+            for (int i = 0; i < nring; ++i) stream_write_slot<DT, D, G>(p, ring + i * SL, run.w, lane);
+            nring = 0;
+        }
+        if (!has_next) break;
+        cur = nxt;
+        has_next = after.s < p.num_seqs;
+        if (has_next) {
+            const StreamCursor c2 = after;
+            nxt = stream_piece(p, lens, cs, run, c2, false, after);
+        }
+    }
+}
+
+// Merge of the stream kernel's split pairs, one (sequence, query head) per
+// wave: the tail record of the pair's first wave w0 and the head records of
+// w0 + 1 .. w0 + n, by the log-sum-exp rule. Pairs one wave held whole were
+// written directly (n = 0) and are skipped.
+template <int DT, int D>
+__global__ __launch_bounds__(64) void pa_merge_stream(DecodeParams p) {
+    using EL = Elem<DT>;
+    constexpr int PER = D / 64;
+    const int hq = blockIdx.x;
+    const int s = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int G = p.group;
+    const int kv = hq / G;
+    const int h = hq - kv * G;
+    const int* meta = p.ws_meta + 2 * (static_cast<size_t>(s) * p.num_kv_heads + kv);
+    const int w0 = meta[0], n = meta[1];
+    if (n <= 0) return;
+    // record i: i = 0 the tail of w0, i >= 1 the head of w0 + i
+    auto rec = [&](int i) -> size_t {
+        return (static_cast<size_t>(i == 0 ? 0 : kMaxStreamWaves) + w0 + i) * G + h;
+    };
+    float M = -INFINITY;
+    for (int i = lane; i <= n; i += 64) M = fmaxf(M, p.ws_xm[rec(i)]);
+    M = wave_max(M);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+    float W = 0.f;
+    for (int i = 0; i <= n; ++i) {
+        const size_t r = rec(i);
+        const float w = p.ws_xl[r] * fast_exp2(p.ws_xm[r] - Mu);
+        W += w;
+        const float* o = p.ws_xo + r * D;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, o[lane + 64 * k], acc[k]);
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+        EL::store(p.out, (static_cast<size_t>(s) * p.num_heads + hq) * D + lane + 64 * k, acc[k] * inv);
+}
+
 // Log-sum-exp merge of the partition records of one (sequence, query head).
 template <int DT, int D>
 __global__ __launch_bounds__(64) void pa_merge(DecodeParams p) {
@@ -1359,13 +1903,14 @@ constexpr int kMfmaWgPerCu = 1;
 
 constexpr size_t lds_alloc(size_t bytes) { return (bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule; }
 
-size_t ring_slot_bytes(int d, int g) { return static_cast<size_t>(ring_slot_floats(g, d)) * sizeof(float); }
+size_t ring_slot_bytes(int d, int g, bool stream) {
+    return static_cast<size_t>(stream ? stream_slot_floats(g, d) : ring_slot_floats(g, d)) * sizeof(float);
+}
 
 // Ring slots that fit next to `used` bytes of LDS when `resident` workgroups
 // share a compute unit of `lds_per_cu` bytes; at least one if a single
 // workgroup of used + one slot fits in `lds_per_wg`, else 0.
-int ring_slots_for(size_t used, int d, int g, int resident, size_t lds_per_cu, size_t lds_per_wg) {
-    const size_t slot = ring_slot_bytes(d, g);
+int ring_slots_for(size_t used, size_t slot, int resident, size_t lds_per_cu, size_t lds_per_wg) {
     if (lds_alloc(used + slot) > lds_per_wg) return 0;
     const size_t share = std::min(lds_per_wg, lds_per_cu / static_cast<size_t>(resident < 1 ? 1 : resident));
     int n = 1;
@@ -1388,6 +1933,12 @@ size_t decode_smem_mfma(int num_seqs, int d, int g) {
            (mfma_red_double(g, d) ? 2 : 1) * static_cast<size_t>(kWaves) * g * red_stride(d) * sizeof(float);
 }
 
+size_t decode_smem_stream(int num_seqs, int d, int g) {
+    // schedule | per wave: a table slice and a query block
+    return (stream_sched_ints(num_seqs) + static_cast<size_t>(kWaves) * kWaveSlice) * sizeof(int) +
+           static_cast<size_t>(kWaves) * wave_q_words(g, d) * sizeof(uint32_t);
+}
+
 size_t decode_smem_mfma_wave(int num_seqs, int d, int g) {
     // schedule | per wave: a table slice and a query block
     return (sched_ints(num_seqs) + static_cast<size_t>(kWaves) * kWaveSlice) * sizeof(int) +
@@ -1397,10 +1948,10 @@ size_t decode_smem_mfma_wave(int num_seqs, int d, int g) {
 // Workgroups of kThreads threads that one compute unit can hold for `kern`
 // with `smem` bytes of dynamic LDS, from the runtime's occupancy query, made
 // once per (device, kernel, smem) and then served from a cache.
-hipError_t residency(const void* kern, int dev, size_t smem, int* out) {
+hipError_t residency(const void* kern, int dev, size_t smem, int threads, int* out) {
     static std::mutex mu;
-    static std::map<std::tuple<int, const void*, size_t>, int> cache;
-    const auto key = std::make_tuple(dev, kern, smem);
+    static std::map<std::tuple<int, const void*, size_t, int>, int> cache;
+    const auto key = std::make_tuple(dev, kern, smem, threads);
     {
         std::lock_guard<std::mutex> lock(mu);
         const auto it = cache.find(key);
@@ -1410,7 +1961,7 @@ hipError_t residency(const void* kern, int dev, size_t smem, int* out) {
         }
     }
     int n = 0;
-    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kThreads, smem);
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, smem);
     if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> lock(mu);
     cache[key] = n;
@@ -1422,17 +1973,20 @@ hipError_t residency(const void* kern, int dev, size_t smem, int* out) {
 // the runtime's occupancy for the planned LDS allow on every compute unit.
 hipError_t run_planned(void (*kern)(DecodeParams), DecodeParams p, const DecodePlan& pl, const DeviceInfo& dv,
                        hipStream_t stream) {
+    const int threads = kThreads;
     int occ = 0;
-    const hipError_t e = residency(reinterpret_cast<const void*>(kern), dv.id, pl.smem, &occ);
+    const hipError_t e = residency(reinterpret_cast<const void*>(kern), dv.id, pl.smem, threads, &occ);
     if (e != hipSuccess) return e;
     const int resident = std::min(pl.resident, occ);
     if (resident < 1) return hipErrorInvalidConfiguration;
     p.ring_slots = pl.ring_slots;
-    const long long upper = static_cast<long long>(p.num_seqs) * p.num_kv_heads * p.pmax;
+    const long long upper = pl.kernel == PA_DECODE_MFMA_STREAM
+                                ? kMaxStreamWaves / kWaves
+                                : static_cast<long long>(p.num_seqs) * p.num_kv_heads * p.pmax;
     long long grid = static_cast<long long>(dv.cus) * resident;
     if (grid > upper) grid = upper;
     if (grid < 1) grid = 1;
-    return launch_kernel(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), pl.smem, stream, p);
+    return launch_kernel(kern, dim3(static_cast<unsigned>(grid)), dim3(threads), pl.smem, stream, p);
 }
 
 template <int DT, int D, int G>
@@ -1441,10 +1995,10 @@ hipError_t launch_valu(const DecodeParams& p, const DeviceInfo& dv, hipStream_t 
     void (*kern)(DecodeParams) =
         (1 << p.log2_bs) >= step ? pa_decode_valu<DT, D, G, true> : pa_decode_valu<DT, D, G, false>;
     int occ = 0;  // as many as the registers allow
-    hipError_t e = residency(reinterpret_cast<const void*>(kern), dv.id, 0, &occ);
+    hipError_t e = residency(reinterpret_cast<const void*>(kern), dv.id, 0, kThreads, &occ);
     if (e != hipSuccess) return e;
     DecodePlan pl;
-    if (plan_decode(static_cast<pa_dtype_t>(DT), D, G, p.num_seqs, p.part >> p.log2_bs, dv.lds_per_cu,
+    if (plan_decode(static_cast<pa_dtype_t>(DT), D, G, p.num_seqs, p.part >> p.log2_bs, false, dv.lds_per_cu,
                     dv.lds_per_wg, occ, &pl) != PA_OK)
         return hipErrorInvalidConfiguration;
     return run_planned(kern, p, pl, dv, stream);
@@ -1453,12 +2007,14 @@ hipError_t launch_valu(const DecodeParams& p, const DeviceInfo& dv, hipStream_t 
 template <int DT, int D, int G>
 hipError_t launch_mfma(const DecodeParams& p, const DeviceInfo& dv, hipStream_t stream) {
     DecodePlan pl;
-    if (plan_decode(static_cast<pa_dtype_t>(DT), D, G, p.num_seqs, p.part >> p.log2_bs, dv.lds_per_cu,
-                    dv.lds_per_wg, kMfmaWgPerCu, &pl) != PA_OK)
+    if (plan_decode(static_cast<pa_dtype_t>(DT), D, G, p.num_seqs, p.part >> p.log2_bs, p.stream != 0,
+                    dv.lds_per_cu, dv.lds_per_wg, kMfmaWgPerCu, &pl) != PA_OK)
         return hipErrorInvalidConfiguration;
     const bool big = (1 << p.log2_bs) >= 16;
     void (*kern)(DecodeParams);
-    if (pl.kernel == PA_DECODE_MFMA_WAVE)
+    if (pl.kernel == PA_DECODE_MFMA_STREAM)
+        kern = pa_decode_stream<DT, D, G>;
+    else if (pl.kernel == PA_DECODE_MFMA_WAVE)
         kern = big ? pa_decode_mfma_wave<DT, D, G, true> : pa_decode_mfma_wave<DT, D, G, false>;
     else
         kern = big ? pa_decode_mfma<DT, D, G, true> : pa_decode_mfma<DT, D, G, false>;
@@ -1499,6 +2055,7 @@ hipError_t launch_dt(const DecodeParams& p, int head_dim, const DeviceInfo& dv, 
 template <int DT, int D>
 hipError_t launch_merge_dd(const DecodeParams& p, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.num_heads), static_cast<unsigned>(p.num_seqs));
+    if (p.stream) return launch_kernel(pa_merge_stream<DT, D>, grid, dim3(64), 0, stream, p);
     if (p.pmax >= kMergeWideMinParts)
         return launch_kernel(pa_merge_wide<DT, D>, grid, dim3(64 * kMergeWideWaves), 0, stream, p);
     return launch_kernel(pa_merge<DT, D>, grid, dim3(64), 0, stream, p);
@@ -1516,8 +2073,8 @@ hipError_t launch_merge_d(const DecodeParams& p, int head_dim, hipStream_t strea
 
 }  // namespace
 
-pa_status_t plan_decode(pa_dtype_t dt, int head_dim, int group, int num_seqs, int part_blocks, size_t lds_per_cu,
-                        size_t lds_per_wg, int max_per_cu, DecodePlan* out) {
+pa_status_t plan_decode(pa_dtype_t dt, int head_dim, int group, int num_seqs, int part_blocks, bool stream,
+                        size_t lds_per_cu, size_t lds_per_wg, int max_per_cu, DecodePlan* out) {
     struct Candidate {
         pa_decode_kernel_t kernel;
         size_t fixed;
@@ -1527,7 +2084,11 @@ pa_status_t plan_decode(pa_dtype_t dt, int head_dim, int group, int num_seqs, in
     Candidate c[2];
     int n = 0;
     const int regs = max_per_cu < 1 ? 1 : max_per_cu;
-    if (decode_uses_mfma(dt, group)) {
+    if (stream) {
+        // the stream split's records differ: no other kernel can stand in
+        c[n++] = {PA_DECODE_MFMA_STREAM, decode_smem_stream(num_seqs, head_dim, group),
+                  std::min(kMfmaWgPerCu, regs), kWaves};
+    } else if (decode_uses_mfma(dt, group)) {
         const int cap = std::min(kMfmaWgPerCu, regs);
         if (part_blocks <= kWaveSlice)
             c[n++] = {PA_DECODE_MFMA_WAVE, decode_smem_mfma_wave(num_seqs, head_dim, group), cap, kWaves};
@@ -1536,10 +2097,11 @@ pa_status_t plan_decode(pa_dtype_t dt, int head_dim, int group, int num_seqs, in
         c[n++] = {PA_DECODE_VALU, decode_smem_valu(num_seqs, head_dim, group), regs, 1};
     }
     for (int i = 0; i < n; ++i) {
-        const int ring = ring_slots_for(c[i].fixed, head_dim, group, c[i].cap, lds_per_cu, lds_per_wg) /
+        const size_t slot = ring_slot_bytes(head_dim, group, c[i].kernel == PA_DECODE_MFMA_STREAM);
+        const int ring = ring_slots_for(c[i].fixed, slot, c[i].cap, lds_per_cu, lds_per_wg) /
                          c[i].multiple * c[i].multiple;
         if (ring < 1) continue;  // (for the wave kernel: the one-item-per-workgroup kernel needs less)
-        const size_t smem = c[i].fixed + static_cast<size_t>(ring) * ring_slot_bytes(head_dim, group);
+        const size_t smem = c[i].fixed + static_cast<size_t>(ring) * slot;
         const size_t alloc = lds_alloc(smem);
         if (alloc > lds_per_wg || alloc > lds_per_cu) continue;
         const int resident = std::min(c[i].cap, static_cast<int>(lds_per_cu / alloc));
@@ -1557,6 +2119,14 @@ bool decode_uses_mfma(pa_dtype_t dt, int group) { return dt != PA_F32 && group >
 
 bool decode_wave_items(pa_dtype_t dt, int group, int part_blocks) {
     return decode_uses_mfma(dt, group) && part_blocks <= kWaveSlice;
+}
+
+bool decode_stream(pa_dtype_t dt, int group, int block_size, int part, int num_seqs, int num_kv_heads, int max_ctx) {
+    if (!decode_uses_mfma(dt, group) || block_size < 16 || part / block_size > kWaveSlice) return false;
+    // cost positions are int32 in the kernel
+    const long long tiles = max_ctx > 0 ? (static_cast<long long>(max_ctx) + 15) / 16 : 1;
+    const long long cost = static_cast<long long>(num_seqs) * num_kv_heads * (kStreamTileCost * tiles + kStreamPairCost);
+    return cost < (1ll << 31) - 1;
 }
 
 int decode_min_block_size(pa_dtype_t dt, int head_dim, int group) {
@@ -1587,7 +2157,8 @@ hipError_t launch_decode_partitions(const DecodeParams& p, pa_dtype_t dt, int he
 
 hipError_t launch_decode_merge(const DecodeParams& p, pa_dtype_t dt, int head_dim,
                                hipStream_t stream) {
-    if (p.pmax <= 1) return hipSuccess;  // every sequence was written directly
+    // without the stream split, single-partition batches were written directly
+    if (p.pmax <= 1 && !p.stream) return hipSuccess;
     switch (dt) {
         case PA_F32: return launch_merge_d<PA_F32>(p, head_dim, stream);
         case PA_BF16: return launch_merge_d<PA_BF16>(p, head_dim, stream);

@@ -63,6 +63,10 @@ template <> struct Elem<PA_F16> {
             f[2 * i + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v[i] >> 16)));
         }
     }
+    // Round to nearest, ties to even (the conversion's own rounding).
+    __device__ __forceinline__ static uint16_t round(float x) {
+        return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+    }
     __device__ __forceinline__ static void store(void* base, size_t i, float x) {
         static_cast<_Float16*>(base)[i] = static_cast<_Float16>(x);
     }

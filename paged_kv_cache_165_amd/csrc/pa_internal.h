@@ -19,9 +19,12 @@ pa_status_t fail(pa_status_t st, const char* fmt, ...) __attribute__((format(pri
 // Table entries (blocks) one decode partition may span: an item stages that
 // slice of its block table in LDS.
 constexpr int kMaxTableSlice = 512;
-// Partitions of at most this many blocks run on the MFMA kernel that gives
-// each wave whole items (bfloat16 / float16 with grouped query heads).
+// Partitions of at most this many blocks run on the MFMA kernels that give
+// each wave items of its own (bfloat16 / float16 with grouped query heads).
 constexpr int kWaveSlice = 128;
+// Waves of the stream kernel's grid at most (256 compute units x 4 waves on
+// MI355X); its workspace holds one extra record per wave.
+constexpr int kMaxStreamWaves = 1024;
 
 // Everything one decode launch needs. Pointers are device pointers.
 struct DecodeParams {
@@ -34,6 +37,11 @@ struct DecodeParams {
     float* ws_m;        // [S][Hq][pmax]  running max per partition (log2 units)
     float* ws_l;        // [S][Hq][pmax]  softmax denominator per partition
     float* ws_o;        // [S][Hq][pmax][D] normalised partial output
+    int* ws_meta;       // stream kernel: [S][Hkv] (first wave, later waves) of each pair
+    float* ws_xm;       // stream kernel: [2][kMaxStreamWaves][G] records of pairs split between
+    float* ws_xl;       //   waves (a wave's tail, then its head): max, sum,
+    float* ws_xo;       //   and [2][kMaxStreamWaves][G][D] normalised output
+    int stream;         // 1: the records are the stream kernel's
     float scale_log2;   // scale * log2(e): logits are kept in base-2 units
     int num_seqs;
     int num_heads;
@@ -124,8 +132,8 @@ struct DecodePlan {
 // compute unit the registers of the VALU kernel allow (ignored for the MFMA
 // kernels, which run one per compute unit). PA_ERR_UNSUPPORTED if no kernel
 // for the shape fits the LDS.
-pa_status_t plan_decode(pa_dtype_t dt, int head_dim, int group, int num_seqs, int part_blocks, size_t lds_per_cu,
-                        size_t lds_per_wg, int max_per_cu, DecodePlan* out);
+pa_status_t plan_decode(pa_dtype_t dt, int head_dim, int group, int num_seqs, int part_blocks, bool stream,
+                        size_t lds_per_cu, size_t lds_per_wg, int max_per_cu, DecodePlan* out);
 
 // Return hipSuccess or the launch error.
 hipError_t launch_decode_partitions(const DecodeParams& p, pa_dtype_t dt, int head_dim, const DeviceInfo& dv,
@@ -133,6 +141,9 @@ hipError_t launch_decode_partitions(const DecodeParams& p, pa_dtype_t dt, int he
 hipError_t launch_decode_merge(const DecodeParams& p, pa_dtype_t dt, int head_dim,
                                hipStream_t stream);
 bool decode_supported(pa_dtype_t dt, int head_dim, int group);
+// Whether a shape runs the stream kernel, which splits the batch's tiles
+// evenly over the grid's waves (its workspace layout differs).
+bool decode_stream(pa_dtype_t dt, int group, int block_size, int part, int num_seqs, int num_kv_heads, int max_ctx);
 bool decode_uses_mfma(pa_dtype_t dt, int group);
 // Whether a partition of `part_blocks` blocks runs one item per wave.
 bool decode_wave_items(pa_dtype_t dt, int group, int part_blocks);

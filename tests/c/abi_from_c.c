@@ -37,11 +37,11 @@ int main(void) {
     CHECK(strstr(pa_last_error(), "null") != NULL);
     CHECK(pa_probe_read_tiles(NULL, NULL, NULL, 4, 64, 4096, 2, 256, NULL, NULL) == PA_ERR_INVALID_ARG);
 
-    /* the host-only launch plan of the GQA batch-256 shape: one item per wave */
+    /* the host-only launch plan of the GQA batch-256 shape: the stream split */
     {
         pa_decode_plan_t plan;
         CHECK(pa_decode_plan(256, 32, 8, 128, 8192, 16, 0, PA_BF16, 163840, 163840, 1, &plan) == PA_OK);
-        CHECK(plan.kernel == PA_DECODE_MFMA_WAVE && plan.partition_size == 2048);
+        CHECK(plan.kernel == PA_DECODE_MFMA_STREAM && plan.partition_size == 2048);
         CHECK(plan.lds_bytes > 0 && plan.lds_bytes <= 163840 && plan.ring_slots >= 4);
     }
 

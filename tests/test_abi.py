@@ -76,10 +76,20 @@ def test_status_strings_and_workspace_size():
     recs = 4 * 8 * 3
     a = lambda x: (x + 255) // 256 * 256
     expect = a(recs * 4) * 2 + a(recs * 128 * 4)
-    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 512, BF16) == expect
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 512, F32) == expect
     # the default resolves as pa_default_partition_size does: 4 x 2 pairs, 1100 tokens -> 512
-    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 0, BF16) == expect
     assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 0, F32) == expect
+    # grouped 16-bit heads with blocks of 16 or more run the stream split: no
+    # per-partition records, one (first wave, later waves) int pair per
+    # (sequence, KV head), and a tail and a head record of every query head
+    # of a group for each of the grid's 1024 waves, whatever the partition
+    xrecs = 2 * 1024 * 4
+    stream = a(4 * 2 * 8) + 2 * a(xrecs * 4) + a(xrecs * 128 * 4)
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 512, BF16) == stream
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 0, BF16) == stream
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 500, 16, 512, BF16) == stream
+    # blocks of 8 keep the one-item-per-wave kernel and its records
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 8, 512, BF16) == expect
     assert lib.pa_decode_workspace_size(-1, 8, 8, 128, 1100, 16, 0, BF16) == 0
     assert lib.pa_decode_workspace_size(4, 8, 8, 128, 1100, 16, 0, 9) == 0
 

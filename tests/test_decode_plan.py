@@ -20,7 +20,7 @@ import pytest
 LDS = 163840  # MI355X: bytes of LDS per compute unit, and per workgroup
 GRANULE = 1024
 F32, BF16, F16 = 0, 1, 2
-VALU, MFMA, WAVE = 0, 1, 2
+VALU, MFMA, WAVE, STREAM = 0, 1, 2, 3
 WAVES = 4
 WAVE_SLICE = 128   # table entries per wave of the one-item-per-wave kernel
 TABLE_SLICE = 512  # table entries of a workgroup item
@@ -45,9 +45,14 @@ def _sched_ints(s):
     return ((s + 4) & ~3) + 2 * ((s + 3) & ~3) + 256 + WAVES + WAVES * 256
 
 
-def _slot_bytes(g, d):
+def _slot_bytes(g, d, stream=False):
     # o[G][D] | m[G] | l[G] | four ints of metadata, padded to 16 bytes
     return ((g * d + 2 * g + 4 + 3) & ~3) * 4
+
+
+def _stream_sched_ints(s):
+    # lens[S] | cs[S + 1] (each padded to 4 ints) | per-wave scan totals
+    return ((s + 3) & ~3) + ((s + 4) & ~3) + WAVES
 
 
 def _fixed_bytes(kernel, s, d, g):
@@ -55,20 +60,27 @@ def _fixed_bytes(kernel, s, d, g):
     if kernel == VALU:
         return (_sched_ints(s) + TABLE_SLICE) * 4 + partials
     qw = (g * d // 2 + 3) & ~3           # 32-bit words of an item's query block
+    if kernel == STREAM:
+        return (_stream_sched_ints(s) + WAVES * WAVE_SLICE) * 4 + WAVES * qw * 4
     if kernel == MFMA:
         return (_sched_ints(s) + 2 * TABLE_SLICE) * 4 + 2 * qw * 4 + (2 if g * d <= 1024 else 1) * partials
     return (_sched_ints(s) + WAVES * WAVE_SLICE) * 4 + WAVES * qw * 4
 
 
-def _expected(dt, d, g, s, part_blocks, max_wg):
+def _expected(dt, d, g, s, part_blocks, max_wg, block_size=16, kv_heads=2, max_ctx=8192):
     """Kernel, LDS bytes, ring slots and residency the plan must give, or
     None when nothing fits."""
     mfma = dt != F32 and g >= 2
-    cands = ([WAVE] if mfma and part_blocks <= WAVE_SLICE else []) + ([MFMA] if mfma else [VALU])
+    stream = (mfma and block_size >= 16 and part_blocks <= WAVE_SLICE and
+              s * kv_heads * (4 * max(1, -(-max_ctx // 16)) + 3) < 2 ** 31 - 1)
+    if stream:   # the stream split's records differ: no other kernel stands in
+        cands = [STREAM]
+    else:
+        cands = ([WAVE] if mfma and part_blocks <= WAVE_SLICE else []) + ([MFMA] if mfma else [VALU])
     for k in cands:
         cap = min(1, max_wg) if k != VALU else max_wg
-        mult = WAVES if k == WAVE else 1
-        fixed, slot = _fixed_bytes(k, s, d, g), _slot_bytes(g, d)
+        mult = WAVES if k in (WAVE, STREAM) else 1
+        fixed, slot = _fixed_bytes(k, s, d, g), _slot_bytes(g, d, k == STREAM)
         if _alloc(fixed + slot) > LDS:
             continue
         share = LDS // cap
@@ -118,7 +130,7 @@ def test_every_accepted_plan_fits_and_the_rest_is_refused(dt, d, g):
                 assert _alloc(plan.lds_bytes) <= LDS
                 assert plan.workgroups_per_cu >= 1
                 assert plan.workgroups_per_cu * _alloc(plan.lds_bytes) <= LDS
-                if plan.kernel == WAVE:
+                if plan.kernel in (WAVE, STREAM):
                     assert plan.ring_slots % WAVES == 0
                 if plan.kernel != VALU:
                     assert plan.workgroups_per_cu == 1
@@ -126,12 +138,27 @@ def test_every_accepted_plan_fits_and_the_rest_is_refused(dt, d, g):
         assert refused > 0  # the largest batches of the largest shape do not fit
 
 
+def test_block_size_and_cost_bound_choose_the_kernel():
+    lib, L = _lib()
+    plan = L.DecodePlan()
+    for bs, part, kernel in [(16, 2048, STREAM), (32, 4096, STREAM), (8, 1024, WAVE), (4, 512, WAVE),
+                             (16, 4096, MFMA)]:  # 256 blocks: more than a wave's table slice
+        assert lib.pa_decode_plan(64, 32, 8, 128, 8192, bs, part, BF16, LDS, LDS, 1, ctypes.byref(plan)) == 0
+        assert plan.kernel == kernel, (bs, part)
+    # stream cost positions are int32: a batch whose cost could pass 2^31 keeps the wave kernel
+    assert lib.pa_decode_plan(8192, 64, 8, 128, 2 ** 20, 16, 2048, BF16, LDS, LDS, 1, ctypes.byref(plan)) == 0
+    assert plan.kernel == WAVE
+
+
 def test_plan_follows_the_default_partition_and_the_device_lds():
     lib, L = _lib()
     plan = L.DecodePlan()
-    # the GQA batch-256 shape: 2048-token partitions, one item per wave
+    # the GQA batch-256 shape: 2048-token partitions, the stream split
     assert lib.pa_decode_plan(256, 32, 8, 128, 8192, 16, 0, BF16, LDS, LDS, 1, ctypes.byref(plan)) == 0
-    assert plan.kernel == WAVE and plan.partition_size == 2048
+    assert plan.kernel == STREAM and plan.partition_size == 2048
+    # blocks of 8 tokens: one item per wave
+    assert lib.pa_decode_plan(256, 32, 8, 128, 8192, 8, 0, BF16, LDS, LDS, 1, ctypes.byref(plan)) == 0
+    assert plan.kernel == WAVE
     # a smaller LDS holds fewer ring slots, and a too small one refuses
     assert lib.pa_decode_plan(256, 32, 8, 128, 8192, 16, 0, BF16, 65536, 65536, 1, ctypes.byref(plan)) == 0
     small = plan.ring_slots

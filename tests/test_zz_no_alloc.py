@@ -72,12 +72,14 @@ def test_noalloc_matches_decode_with_workspace_on_two_calls():
 
 
 def test_noalloc_refuses_records_beyond_its_scratch():
-    """64 sequences x 32 heads x 256 partitions of 512 tokens need 272 MB of
-    records: refused on the host. (Every buffer is real and every context
-    empty, so nothing could be read out of bounds even if a launch happened.)"""
+    """64 sequences x 32 heads x 256 partitions of 512 tokens in blocks of 8
+    (the one-item-per-wave kernel, which keeps a record per partition) need
+    272 MB of records: refused on the host. (Every buffer is real and every
+    context empty, so nothing could be read out of bounds even if a launch
+    happened.)"""
     lib, L = _lib()
     import paged_kv_cache_165_amd as pa
-    s, hq, hkv, d, bs, max_ctx = 64, 32, 8, 128, 16, 131072
+    s, hq, hkv, d, bs, max_ctx = 64, 32, 8, 128, 8, 131072
     kc, vc = pa.alloc_cache(4, hkv, bs, d, torch.bfloat16, device=DEV)
     q = torch.zeros(s, hq, d, dtype=torch.bfloat16, device=DEV)
     out = torch.empty_like(q)
