@@ -27,7 +27,9 @@ METRIC = "paged decode attention: KV GB/s read (% of HBM peak), seqs/sec"
 HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_165_amd", "csrc", "pa_decode.hip")
-PARTITION_KERNELS = ("pa_decode_mfma", "pa_decode_valu")
+PARTITION_KERNELS = ("pa_decode_stream", "pa_decode_mfma", "pa_decode_valu")
+PLAN_KERNELS = {"valu": "pa_decode_valu", "mfma": "pa_decode_mfma", "mfma_wave": "pa_decode_mfma_wave",
+                "mfma_stream": "pa_decode_stream"}
 CALIBRATION_KERNEL = "neg_kernel"  # torch's elementwise negate: reads N bytes, writes N bytes
 
 
@@ -641,6 +643,11 @@ def main():
                              "moved_gbs": round(moved / (us * 1e-6) / 1e9, 1)}
     kv = w.kv_bytes()
     unique = w.unique_kv_bytes()
+    props = torch.cuda.get_device_properties(dev)
+    lds = getattr(props, "shared_memory_per_multiprocessor", 0) or 163840
+    plan = pa.decode_plan(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_context_len, w.block_size,
+                          w.partition_size, torch.float32 if w.dtype == "f32" else torch.bfloat16,
+                          lds_per_cu=lds, lds_per_workgroup=lds)
     value = kv / (ms_step * 1e-3) / 1e9
     achieved = kv / (part_us * 1e-6) / 1e9
     progress(f"step {ms_step * 1e3:.1f} us, partition kernel {part_us:.1f} us per launch")
@@ -734,7 +741,8 @@ def main():
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "wall_ms_per_step": round(1e3 * t_wall / args.steps, 5),
         "cache_ops": cache_ops,
-        "roofline": {"bound": "hbm", "kernel": "pa_decode_partitions (pa_decode_mfma_wave / pa_decode_mfma / pa_decode_valu)",
+        "roofline": {"bound": "hbm", "kernel": f"pa_decode_partitions ({PLAN_KERNELS[plan['kernel']]})",
+                     "plan": plan,
                      "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_us_mean": round(part_us, 2),

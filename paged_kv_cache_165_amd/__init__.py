@@ -465,7 +465,8 @@ def decode_plan(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
     _check(library().pa_decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size,
                                     partition_size, _DTYPES[dtype], lds_per_cu, lds_per_workgroup,
                                     max_workgroups_per_cu, ctypes.byref(plan)))
-    names = {_lib.PA_DECODE_VALU: "valu", _lib.PA_DECODE_MFMA: "mfma", _lib.PA_DECODE_MFMA_WAVE: "mfma_wave"}
+    names = {_lib.PA_DECODE_VALU: "valu", _lib.PA_DECODE_MFMA: "mfma", _lib.PA_DECODE_MFMA_WAVE: "mfma_wave",
+             _lib.PA_DECODE_MFMA_STREAM: "mfma_stream"}
     return {"kernel": names[plan.kernel], "partition_size": plan.partition_size, "lds_bytes": plan.lds_bytes,
             "ring_slots": plan.ring_slots, "workgroups_per_cu": plan.workgroups_per_cu}
 

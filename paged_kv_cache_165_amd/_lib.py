@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 PA_OK = 0
 PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_BLOCKS = 1, 2, 3, 4, 5
-PA_DECODE_VALU, PA_DECODE_MFMA, PA_DECODE_MFMA_WAVE = 0, 1, 2
+PA_DECODE_VALU, PA_DECODE_MFMA, PA_DECODE_MFMA_WAVE, PA_DECODE_MFMA_STREAM = 0, 1, 2, 3
 ABI_VERSION = 9
 NOALLOC_SCRATCH_BYTES = 32 << 20  # PA_NOALLOC_SCRATCH_BYTES
 

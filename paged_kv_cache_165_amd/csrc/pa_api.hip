@@ -173,9 +173,8 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // Workspace: the per-partition records m, l and o, needed only when some
 // sequence can span several partitions. The stream kernel keeps no
 // per-partition records (a wave merges the partitions of its stretch of a
-// pair itself): one (first wave, later waves) pair per (sequence, KV head),
-// and a tail and a head record, of every query head of a group, per wave of
-// its grid.
+// pair itself): per wave of its grid, a tail and a head record of every
+// query head of a group, and which pair the tail record belongs to.
 struct WsLayout {
     size_t m_off, l_off, o_off, meta_off, xm_off, xl_off, xo_off, total;
 };
@@ -183,10 +182,9 @@ struct WsLayout {
 WsLayout ws_layout(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int pmax, bool stream) {
     WsLayout w{};
     if (stream) {
-        const size_t pairs = static_cast<size_t>(num_seqs) * num_kv_heads;
         const size_t xrecs = 2 * static_cast<size_t>(pa::kMaxStreamWaves) * (num_heads / num_kv_heads);
         w.meta_off = 0;
-        w.xm_off = align256(pairs * 2 * sizeof(int));
+        w.xm_off = align256(static_cast<size_t>(pa::kMaxStreamWaves) * 4 * sizeof(int));
         w.xl_off = w.xm_off + align256(xrecs * sizeof(float));
         w.xo_off = w.xl_off + align256(xrecs * sizeof(float));
         w.total = w.xo_off + align256(xrecs * head_dim * sizeof(float));

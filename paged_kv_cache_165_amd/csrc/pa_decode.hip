@@ -1264,8 +1264,10 @@ __global__ __launch_bounds__(kThreads) void pa_decode_mfma_wave(DecodeParams p) 
 // touches: a pair it holds whole is written to `out` directly; a pair split
 // between waves w0 < ... < w1 leaves the tail record of w0 (its first part)
 // and the head records of w0 + 1 .. w1 (a run starts inside at most one pair
-// and ends inside at most one), which the merge kernel combines. The wave
-// holding a pair's first tile also stores the pair's (w0, w1 - w0). Results
+// and ends inside at most one), which the merge kernel combines. Every wave
+// also states which pair its tail record belongs to and how many later waves
+// continue it (none if it has no tail record), so that the merge runs one
+// workgroup per wave. Results
 // wait in an LDS ring and are stored when it is full or the run ends: a
 // store between the streaming loads holds back the loads issued after it
 // (measured on MI355X: storing each result as soon as it is known, by the
@@ -1455,8 +1457,17 @@ __device__ __forceinline__ void stream_write_slot(const DecodeParams& p, const f
             p.ws_xl[x0 + lane] = lv;
         }
     }
-    if (kind != kSegHead && lane == 0)
-        *reinterpret_cast<int2*>(p.ws_meta + 2 * (static_cast<size_t>(s) * p.num_kv_heads + kv)) = make_int2(w, span);
+    if (kind == kSegTail && lane == 0)
+        *reinterpret_cast<int4*>(p.ws_meta + 4 * static_cast<size_t>(w)) = make_int4(s, kv, span, 0);
+}
+
+// The merge's list has kMaxStreamWaves entries: wave w of a grid of W waves
+// clears entries w + W, w + 2W, ... (no wave of this launch has them) and,
+// unless it holds a tail record (which writes entry w), entry w too.
+__device__ __forceinline__ void stream_list_end(const DecodeParams& p, int w, bool own, int lane) {
+    const int W = gridDim.x * kWaves;
+    for (int x = w + W * (lane + (own ? 0 : 1)); x < kMaxStreamWaves; x += W * 64)
+        *reinterpret_cast<int4*>(p.ws_meta + 4 * static_cast<size_t>(x)) = make_int4(0, 0, 0, 0);
 }
 
 template <int DT, int D, int G>
@@ -1505,7 +1516,10 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
     const long long wmax = static_cast<long long>(gridDim.x) * kWaves;
     run.weff = static_cast<int>(min(wmax, max(1ll, run.total / 8)));
     run.w = blockIdx.x * kWaves + wave;
-    if (run.w >= run.weff) return;
+    if (run.w >= run.weff) {
+        stream_list_end(p, run.w, true, lane);
+        return;
+    }
     run.lo = (static_cast<long long>(run.w) * run.total + run.weff - 1) / run.weff;
     run.hi = (static_cast<long long>(run.w + 1) * run.total + run.weff - 1) / run.weff;
 
@@ -1549,7 +1563,10 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
 
     // prologue: the first piece's table slice and query block, its first tile
     const StreamCursor at = stream_seek(p, lens, cs, run.lo);
-    if (at.s >= p.num_seqs) return;  // (a run of 8 or more units always holds a tile)
+    if (at.s >= p.num_seqs) {  // (a run of 8 or more units always holds a tile)
+        stream_list_end(p, run.w, true, lane);
+        return;
+    }
     StreamCursor after;
     Piece cur = stream_piece(p, lens, cs, run, at, true, after);
     bool has_next = after.s < p.num_seqs;
@@ -1654,7 +1671,6 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
             if (next_tile) load_with(nxt, 0, clamp_pid(pk), b);
             else load_with(cur, 0, 0, b);
         };
-
         // the piece's tiles, two deep
         int t = 0;
         if (ntiles > 0) {
@@ -1704,6 +1720,7 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
             // its last is the pair's tail record
             const bool pair_done = cur.t1 >= lens[cur.s];
             const int kind = seg_kind == kSegHead ? kSegHead : (pair_done ? kSegDirect : kSegTail);
+            if (!has_next) stream_list_end(p, run.w, kind != kSegTail, lane);
             float* slot = ring + nring * SL;
             if (r16 < G) {
                 const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -1744,23 +1761,20 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
     }
 }
 
-// Merge of the stream kernel's split pairs, one (sequence, query head) per
-// wave: the tail record of the pair's first wave w0 and the head records of
-// w0 + 1 .. w0 + n, by the log-sum-exp rule. Pairs one wave held whole were
-// written directly (n = 0) and are skipped.
-template <int DT, int D>
-__global__ __launch_bounds__(64) void pa_merge_stream(DecodeParams p) {
+// Merge of the stream kernel's split pairs: workgroup (w, h), one wave,
+// takes query head h of the pair whose tail record wave w holds, if any,
+// and combines that record with the head records of the n waves that
+// continue the pair by the log-sum-exp rule. All loads of a chunk of CH
+// records (CH the smallest of 2, 4, 8, 16, 32 that holds them, chunks of 32
+// beyond) are issued together: lane i reads record i's max and sum, every
+// lane its head_dim elements of each record; the records are then added in
+// record order. Pairs one wave held whole were written directly.
+template <int DT, int D, int CH>
+__device__ __forceinline__ void merge_stream_pair(const DecodeParams& p, int w0, int h, int n, size_t row,
+                                                  int lane) {
     using EL = Elem<DT>;
     constexpr int PER = D / 64;
-    const int hq = blockIdx.x;
-    const int s = blockIdx.y;
-    const int lane = threadIdx.x;
     const int G = p.group;
-    const int kv = hq / G;
-    const int h = hq - kv * G;
-    const int* meta = p.ws_meta + 2 * (static_cast<size_t>(s) * p.num_kv_heads + kv);
-    const int w0 = meta[0], n = meta[1];
-    if (n <= 0) return;
     // record i: i = 0 the tail of w0, i >= 1 the head of w0 + i
     auto rec = [&](int i) -> size_t {
         return (static_cast<size_t>(i == 0 ? 0 : kMaxStreamWaves) + w0 + i) * G + h;
@@ -1771,20 +1785,51 @@ __global__ __launch_bounds__(64) void pa_merge_stream(DecodeParams p) {
     const float Mu = M == -INFINITY ? 0.f : M;
     float acc[PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-    float W = 0.f;
-    for (int i = 0; i <= n; ++i) {
-        const size_t r = rec(i);
-        const float w = p.ws_xl[r] * fast_exp2(p.ws_xm[r] - Mu);
-        W += w;
-        const float* o = p.ws_xo + r * D;
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    float wsum = 0.f;  // this lane's records' weights
+    for (int base = 0; base <= n; base += CH) {
+        const int cnt = min(CH, n + 1 - base);
+        float o[CH][PER];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, o[lane + 64 * k], acc[k]);
+        for (int k2 = 0; k2 < CH; ++k2) {
+            const float* src = p.ws_xo + rec(base + min(k2, cnt - 1)) * D;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) o[k2][e] = src[lane + 64 * e];
+        }
+        float wi = 0.f;
+        if (lane < cnt) {
+            const size_t r = rec(base + lane);
+            wi = p.ws_xl[r] * fast_exp2(p.ws_xm[r] - Mu);
+        }
+        wsum += wi;
+#pragma unroll
+        for (int k2 = 0; k2 < CH; ++k2) {
+            const float wk = k2 < cnt ? __shfl(wi, k2) : 0.f;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] = fmaf(wk, o[k2][e], acc[e]);
+        }
     }
+    const float W = group_sum<64>(wsum);
     const float inv = W > 0.f ? 1.f / W : 0.f;
 #pragma unroll
-    for (int k = 0; k < PER; ++k)
-        EL::store(p.out, (static_cast<size_t>(s) * p.num_heads + hq) * D + lane + 64 * k, acc[k] * inv);
+    for (int e = 0; e < PER; ++e) EL::store(p.out, row * D + lane + 64 * e, acc[e] * inv);
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(64) void pa_merge_stream(DecodeParams p) {
+    const int w0 = blockIdx.x;
+    const int h = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int4 t = *reinterpret_cast<const int4*>(p.ws_meta + 4 * static_cast<size_t>(w0));
+    const int s = t.x, kv = t.y, n = t.z;
+    const int G = p.group;
+    if (n <= 0 || h >= G) return;
+    const size_t row = static_cast<size_t>(s) * p.num_heads + kv * G + h;
+    if (n < 2) merge_stream_pair<DT, D, 2>(p, w0, h, n, row, lane);
+    else if (n < 4) merge_stream_pair<DT, D, 4>(p, w0, h, n, row, lane);
+    else if (n < 8) merge_stream_pair<DT, D, 8>(p, w0, h, n, row, lane);
+    else if (n < 16) merge_stream_pair<DT, D, 16>(p, w0, h, n, row, lane);
+    else merge_stream_pair<DT, D, 32>(p, w0, h, n, row, lane);
 }
 
 // Log-sum-exp merge of the partition records of one (sequence, query head).
@@ -2055,7 +2100,9 @@ hipError_t launch_dt(const DecodeParams& p, int head_dim, const DeviceInfo& dv, 
 template <int DT, int D>
 hipError_t launch_merge_dd(const DecodeParams& p, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.num_heads), static_cast<unsigned>(p.num_seqs));
-    if (p.stream) return launch_kernel(pa_merge_stream<DT, D>, grid, dim3(64), 0, stream, p);
+    if (p.stream)
+        return launch_kernel(pa_merge_stream<DT, D>, dim3(kMaxStreamWaves, static_cast<unsigned>(p.group)), dim3(64),
+                             0, stream, p);
     if (p.pmax >= kMergeWideMinParts)
         return launch_kernel(pa_merge_wide<DT, D>, grid, dim3(64 * kMergeWideWaves), 0, stream, p);
     return launch_kernel(pa_merge<DT, D>, grid, dim3(64), 0, stream, p);

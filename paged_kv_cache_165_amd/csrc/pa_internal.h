@@ -37,7 +37,8 @@ struct DecodeParams {
     float* ws_m;        // [S][Hq][pmax]  running max per partition (log2 units)
     float* ws_l;        // [S][Hq][pmax]  softmax denominator per partition
     float* ws_o;        // [S][Hq][pmax][D] normalised partial output
-    int* ws_meta;       // stream kernel: [S][Hkv] (first wave, later waves) of each pair
+    int* ws_meta;       // stream kernel: [kMaxStreamWaves][4] (sequence, KV head, later waves, 0) of the
+                        //   pair each wave's tail record belongs to (later waves = 0: no tail record)
     float* ws_xm;       // stream kernel: [2][kMaxStreamWaves][G] records of pairs split between
     float* ws_xl;       //   waves (a wave's tail, then its head): max, sum,
     float* ws_xo;       //   and [2][kMaxStreamWaves][G][D] normalised output

@@ -80,11 +80,11 @@ def test_status_strings_and_workspace_size():
     # the default resolves as pa_default_partition_size does: 4 x 2 pairs, 1100 tokens -> 512
     assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 0, F32) == expect
     # grouped 16-bit heads with blocks of 16 or more run the stream split: no
-    # per-partition records, one (first wave, later waves) int pair per
-    # (sequence, KV head), and a tail and a head record of every query head
-    # of a group for each of the grid's 1024 waves, whatever the partition
+    # per-partition records; per wave of the grid's 1024, a tail and a head
+    # record of every query head of a group and four ints naming the pair
+    # of the tail record, whatever the batch and the partition
     xrecs = 2 * 1024 * 4
-    stream = a(4 * 2 * 8) + 2 * a(xrecs * 4) + a(xrecs * 128 * 4)
+    stream = a(1024 * 16) + 2 * a(xrecs * 4) + a(xrecs * 128 * 4)
     assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 512, BF16) == stream
     assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 0, BF16) == stream
     assert lib.pa_decode_workspace_size(4, 8, 2, 128, 500, 16, 512, BF16) == stream
