@@ -249,15 +249,19 @@ def pattern_ceiling(w, kc, vc, dev) -> dict:
         nb = -(-int(w.context_lens[s]) // b)
         blocks = w.block_tables[s, :nb].astype(np.int64)
         parts.append((blocks[None, :] * hkv + np.arange(hkv)[:, None]).ravel())
-    tiles_h = np.concatenate(parts).astype(np.int32)
+    tiles_h = np.concatenate(parts)
+    # (block, head) slices over 8 KB go to the probe as 8 KB tiles
+    slice_bytes = b * w.head_dim * kc.element_size()
+    tile_bytes = min(slice_bytes, 8192)
+    sub = slice_bytes // tile_bytes
+    tiles_h = (tiles_h[:, None] * sub + np.arange(sub)[None, :]).ravel().astype(np.int32)
     tiles = torch.from_numpy(tiles_h).to(dev)
-    tile_bytes = b * w.head_dim * kc.element_size()
     nbytes = 2 * len(tiles_h) * tile_bytes
     sink = torch.empty(16 * 256 * 1024, dtype=torch.uint8, device=dev)
     best, runs = None, []
     for u in (1, 2, 4):
         for wg in (256, 512, 1024):
-            fn = lambda: pa.probe_read_tiles(kc, vc, tiles, u, wg, sink)
+            fn = lambda: pa.probe_read_tiles(kc, vc, tiles, u, wg, sink, tile_bytes)
             for _ in range(3):
                 fn()
             a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -471,17 +471,22 @@ def decode_plan(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
             "ring_slots": plan.ring_slots, "workgroups_per_cu": plan.workgroups_per_cu}
 
 
-def probe_read_tiles(k_cache, v_cache, tiles, tiles_in_flight: int, workgroups: int, sink):
+def probe_read_tiles(k_cache, v_cache, tiles, tiles_in_flight: int, workgroups: int, sink, tile_bytes=None):
     """Bandwidth probe (``pa_probe_read_tiles``, include/pa_probe.h): read the
-    K and V tiles listed in ``tiles`` (int32 indices of (block, KV head)
-    tiles) with the decode's loads and no arithmetic. ``sink`` must hold
-    16 * 256 * workgroups bytes."""
+    K and V tiles listed in ``tiles`` with the decode's loads and no
+    arithmetic. A tile is ``tile_bytes`` of the cache (default: the whole
+    (block, KV head) slice, block * head_dim elements) and ``tiles`` holds
+    int32 tile indices. ``sink`` must hold 16 * 256 * workgroups bytes."""
     nb, hkv, bs, d = _check_caches(k_cache, v_cache)
     _dev_tensor(tiles, "tiles", dtype=torch.int32, ndim=1)
     _dev_tensor(sink, "sink")
     if sink.numel() * sink.element_size() < 16 * 256 * workgroups:
         raise ValueError("sink too small")
-    tile_bytes = bs * d * k_cache.element_size()
+    slice_bytes = bs * d * k_cache.element_size()
+    tile_bytes = slice_bytes if tile_bytes is None else int(tile_bytes)
+    if tile_bytes <= 0 or slice_bytes % tile_bytes != 0:
+        raise ValueError(f"tile_bytes {tile_bytes} must divide the (block, head) slice of {slice_bytes} bytes")
     _check(library().pa_probe_read_tiles(k_cache.data_ptr(), v_cache.data_ptr(), tiles.data_ptr(), tiles.shape[0],
-                                         nb * hkv, tile_bytes, int(tiles_in_flight), int(workgroups),
+                                         nb * hkv * (slice_bytes // tile_bytes), tile_bytes, int(tiles_in_flight),
+                                         int(workgroups),
                                          sink.data_ptr(), _stream(k_cache)))

@@ -1761,8 +1761,8 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
     }
 }
 
-// Merge of the stream kernel's split pairs: workgroup (w, h), one wave,
-// takes query head h of the pair whose tail record wave w holds, if any,
+// Merge of the stream kernel's split pairs: one wave per (w, h) takes query
+// head h of the pair whose tail record wave w holds, if any,
 // and combines that record with the head records of the n waves that
 // continue the pair by the log-sum-exp rule. All loads of a chunk of CH
 // records (CH the smallest of 2, 4, 8, 16, 32 that holds them, chunks of 32
@@ -1816,14 +1816,17 @@ __device__ __forceinline__ void merge_stream_pair(const DecodeParams& p, int w0,
 }
 
 template <int DT, int D>
-__global__ __launch_bounds__(64) void pa_merge_stream(DecodeParams p) {
-    const int w0 = blockIdx.x;
-    const int h = blockIdx.y;
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void pa_merge_stream(DecodeParams p) {
+    // four (wave, head) tasks per workgroup: task i is head i % G of the
+    // tail record of wave i / G (most have none: few workgroups to dispatch)
+    const int G = p.group;
+    const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int w0 = task / G;
+    const int h = task - w0 * G;
+    const int lane = threadIdx.x & 63;
     const int4 t = *reinterpret_cast<const int4*>(p.ws_meta + 4 * static_cast<size_t>(w0));
     const int s = t.x, kv = t.y, n = t.z;
-    const int G = p.group;
-    if (n <= 0 || h >= G) return;
+    if (n <= 0) return;
     const size_t row = static_cast<size_t>(s) * p.num_heads + kv * G + h;
     if (n < 2) merge_stream_pair<DT, D, 2>(p, w0, h, n, row, lane);
     else if (n < 4) merge_stream_pair<DT, D, 4>(p, w0, h, n, row, lane);
@@ -2100,9 +2103,9 @@ hipError_t launch_dt(const DecodeParams& p, int head_dim, const DeviceInfo& dv, 
 template <int DT, int D>
 hipError_t launch_merge_dd(const DecodeParams& p, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.num_heads), static_cast<unsigned>(p.num_seqs));
-    if (p.stream)
-        return launch_kernel(pa_merge_stream<DT, D>, dim3(kMaxStreamWaves, static_cast<unsigned>(p.group)), dim3(64),
-                             0, stream, p);
+    if (p.stream)  // (kMaxStreamWaves is a multiple of 4)
+        return launch_kernel(pa_merge_stream<DT, D>, dim3(kMaxStreamWaves / 4 * static_cast<unsigned>(p.group)),
+                             dim3(256), 0, stream, p);
     if (p.pmax >= kMergeWideMinParts)
         return launch_kernel(pa_merge_wide<DT, D>, grid, dim3(64 * kMergeWideWaves), 0, stream, p);
     return launch_kernel(pa_merge<DT, D>, grid, dim3(64), 0, stream, p);
