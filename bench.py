@@ -39,6 +39,25 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+WARMUP_MIN_S = 0.25  # warm-up runs at least this long, whatever --warmup says
+
+
+def warm_up(step, count: int) -> int:
+    """Run `step` `count` times, then on until WARMUP_MIN_S has passed (the
+    GPU's clocks settle under sustained load: right after set-up the same
+    launches run up to 15 % slower). Returns the steps run."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while n < count or time.perf_counter() - t0 < WARMUP_MIN_S:
+        step()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def progress(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -486,9 +505,7 @@ def prefill_bench(args, dev):
         pa.write_cache(kn, vn, kc, vc, slots)
         pa.prefill(*pargs)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmed = warm_up(step, args.warmup)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(args.steps):
@@ -517,6 +534,7 @@ def prefill_bench(args, dev):
     print(json.dumps({
         "metric": "paged prefill attention: causal TFLOP/s",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "warmup_run": {"steps": warmed, "min_seconds": WARMUP_MIN_S},
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {**w.summary(), "new_tokens": w.num_tokens, "attended_pairs": w.attended_pairs(),
@@ -594,11 +612,9 @@ def main():
         pa.decode_partitions(*dargs)
         pa.decode_merge(*dargs)
 
-    progress(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    progress(f"timing {args.steps} steps")
+    progress(f"warmup {args.warmup} steps, at least {WARMUP_MIN_S} s")
+    warmed = warm_up(step, args.warmup)
+    progress(f"timing {args.steps} steps (after {warmed} warm-up steps)")
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -725,6 +741,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": {"steps": warmed, "min_seconds": WARMUP_MIN_S},
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
