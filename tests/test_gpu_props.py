@@ -236,3 +236,29 @@ def test_largest_batch():
     c = make_case(lens.tolist(), 8, 2, 64, 16, torch.bfloat16, seed=15)
     out = run_gpu(c, 0.125)
     compare_attention(out, run_oracle(c, 0.125), "8192 seqs")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_one_pair_split_over_every_wave(dt):
+    """One (sequence, KV head) pair of 65,536 tokens: the stream split gives
+    every wave of the grid a stretch of it, so the merge combines one tail
+    record with about a thousand head records (its chunked loads, 32 at a
+    time)."""
+    pa = _pa()
+    plan = pa.decode_plan(1, 4, 1, 128, 65536, 16, 0, dt)
+    assert plan["kernel"] == "mfma_stream"
+    c = make_case([65536], 4, 1, 128, 16, dt, seed=16)
+    compare_attention(run_gpu(c, 0.088), run_oracle(c, 0.088), "one pair, every wave")
+
+
+def test_stream_mixes_tiny_and_long_pairs():
+    """Hundreds of one- to three-token sequences around a few long ones:
+    waves that hold many whole pairs write them directly, the long pairs are
+    split between waves, and empty sequences sit between them."""
+    rng = np.random.default_rng(17)
+    lens = rng.integers(0, 4, size=900)
+    lens[[5, 450, 899]] = [30000, 17, 45000]
+    c = make_case(lens.tolist(), 32, 8, 128, 16, torch.bfloat16, seed=17)
+    pa = _pa()
+    assert pa.decode_plan(900, 32, 8, 128, 45000, 16, 0, torch.bfloat16)["kernel"] == "mfma_stream"
+    compare_attention(run_gpu(c, 0.088), run_oracle(c, 0.088), "tiny and long")
