@@ -86,7 +86,7 @@ typedef enum pa_status {
     PA_ERR_NO_BLOCKS = 5    /* block manager (pa_blocks.h): not enough free blocks */
 } pa_status_t;
 
-/* The three decode partition kernels (see pa_decode_plan). */
+/* The decode partition kernels (see pa_decode_plan). */
 typedef enum pa_decode_kernel {
     PA_DECODE_VALU = 0,      /* vector ALU; one item per workgroup (float32, or one query head per KV head) */
     PA_DECODE_MFMA = 1,      /* matrix cores; one item per workgroup (partitions of more than 128 blocks) */
@@ -134,10 +134,14 @@ int pa_default_partition_size(int num_seqs, int num_heads, int num_kv_heads, int
                               pa_dtype_t dtype);
 
 /*
- * Bytes of device workspace pa_decode needs: one (max, sum, output row)
- * record in float32 per sequence, query head and partition, or 0 when no
- * sequence can span more than one partition (max_context_len <=
- * partition_size). Returns 0 for invalid arguments too. partition_size = 0
+ * Bytes of device workspace pa_decode needs. For the item kernels: one
+ * (max, sum, output row) record in float32 per sequence, query head and
+ * partition, or 0 when no sequence can span more than one partition
+ * (max_context_len <= partition_size). For the stream split (see
+ * pa_decode): per wave of its grid (at most 1024), a tail and a head record
+ * of every query head of a group and four ints naming the pair of the tail
+ * record, whatever the batch (about 4.3 MB at 4 query heads per KV head and
+ * head_dim 128). Returns 0 for invalid arguments too. partition_size = 0
  * selects pa_default_partition_size(num_seqs, num_heads, num_kv_heads,
  * max_context_len, block_size, dtype). The workspace is caller-owned device
  * memory with no required contents; calls that share one must not overlap.
@@ -197,10 +201,17 @@ pa_status_t pa_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int he
  * clamped to max_context_len tokens. Table entries outside [0, num_blocks)
  * are clamped into that range (wrong values, no fault). q/out must not alias.
  *
- * Work is split into items of (sequence, KV head, partition) that a
- * persistent grid processes largest first; an item's result does not depend
- * on which workgroup (or, for partitions of at most 128 blocks with 16-bit
- * elements and grouped query heads, which wave) ran it.
+ * Work: with 16-bit elements, grouped query heads, blocks of 16 or more
+ * tokens and partitions of at most 128 blocks (pa_decode_plan names the
+ * kernel), the batch's 16-key tiles form one stream that a persistent grid
+ * divides evenly among its waves; a wave merges the partitions of its
+ * stretch of a (sequence, KV head) pair itself, and only pairs split between
+ * waves leave records for the merge. The division depends on the batch and
+ * on the device's compute-unit count: results repeat bit for bit on one
+ * device and differ in rounding only between devices. Otherwise the work is
+ * split into items of (sequence, KV head, partition) that a persistent grid
+ * processes largest first; an item's result does not depend on which
+ * workgroup (or wave) ran it.
  */
 pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens, float scale,
@@ -215,8 +226,10 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void*
  * pa_decode_merge on the same stream. The merge combines per-partition
  * records (m_p, l_p, o_p) of a sequence as M = max m_p, w_p = l_p e^(m_p - M),
  * out = sum w_p o_p / sum w_p, and does nothing for single-partition
- * sequences. Calling pa_decode_merge without a preceding
- * pa_decode_partitions on the same workspace leaves `out` undefined.
+ * sequences (with the stream split: the records of the pairs split between
+ * waves, and nothing for pairs one wave held whole). Calling
+ * pa_decode_merge without a preceding pa_decode_partitions on the same
+ * workspace leaves `out` undefined.
  */
 pa_status_t pa_decode_partitions(void* out, const void* q, const void* k_cache,
                                  const void* v_cache, const int32_t* block_tables,
