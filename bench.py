@@ -168,7 +168,7 @@ def summarize_counters(fetch_csv, write_csv, out_json, workload, calib_mb, parti
 
 
 def host_cores() -> int:
-    """CPU cores this process may run on (the GPU machine's share of its host)."""
+    """CPU cores this process may run on (its share of the host)."""
     try:
         return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover - Linux has sched_getaffinity
@@ -689,7 +689,7 @@ def main():
     progress(f"pattern ceiling {ceiling['gbs']} GB/s ({ceiling['best']}); the partition kernel reaches "
              f"{ceiling['decode_kernel_pct_of_ceiling']} % of it")
 
-    # On-box ceiling next to the peak: a plain device copy of 1 GiB (bytes
+    # A measured ceiling next to the peak: a plain device copy of 1 GiB (bytes
     # read plus written, per time), after the timed region.
     cbuf = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
     cdst = torch.empty_like(cbuf)

@@ -80,7 +80,7 @@ typedef enum pa_dtype {
 typedef enum pa_status {
     PA_OK = 0,
     PA_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size, misalignment */
-    PA_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for */
+    PA_ERR_UNSUPPORTED = 2, /* valid request the library has no kernel for */
     PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than pa_decode_workspace_size */
     PA_ERR_HIP = 4,         /* the HIP runtime reported an error */
     PA_ERR_NO_BLOCKS = 5    /* block manager (pa_blocks.h): not enough free blocks */
