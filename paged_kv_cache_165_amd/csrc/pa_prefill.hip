@@ -22,7 +22,8 @@
 // global_load_lds (no register holds staged data): the next tile's loads fly
 // while the current tile is reduced. Each load instruction covers keys of one
 // aligned 16-key group, so with blocks of 16 or more tokens its block id is
-// wave-uniform. K rows are stored in a permuted order (below) with their
+// wave-uniform (read from the wave's own lanes of the table entries, loaded a
+// tile ahead). K rows are stored in a permuted order (below) with their
 // 16-byte chunks XOR-swizzled; V keeps the cache's own 16-key tiles [D][16],
 // the two halves of a row swizzled; both keep the MFMA operand reads on
 // distinct banks.
@@ -215,6 +216,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr float kFloor = -1e30f;    // running-max start: exp2(x - kFloor) never meets -inf - -inf
 
     // LDS: two tile buffers [K | V], then two table slices of block ids
+    // (used with blocks of fewer than 16 tokens)
     extern __shared__ __align__(16) unsigned char lds[];
     int* tbl = reinterpret_cast<int*>(lds + 2 * SH::BUF_BYTES);
 
@@ -244,6 +246,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     const int s = pair / p.num_kv_heads;
     const int kv = pair - s * p.num_kv_heads;
+
+    // Block ids of the first two key tiles, loaded before the sequence's
+    // length is known: entries past its last block are loaded but never used
+    // (every load of a tile reads the block of a key at most the last one).
+    int traw0 = 0, traw1 = 0;
+    {
+        const int ntb = KT >= (1 << p.log2_bs) ? KT >> p.log2_bs : 1;
+        const int* trow = p.block_tables + static_cast<size_t>(s) * p.max_blocks;
+        const int hi = p.max_blocks - 1;
+        if (lane < ntb && hi >= 0) {
+            traw0 = trow[min(lane, hi)];
+            traw1 = trow[min((KT >> p.log2_bs) + lane, hi)];
+        }
+    }
 
     int L = p.context_lens[s];
     L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
@@ -321,11 +337,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int ntb = KT >= bs ? KT >> lb : 1;  // block ids one tile spans
         const bool big = bs >= 16;                 // every aligned 16 keys share a block
         auto clamp_pid = [&](int pid) { return pid < 0 ? 0 : (pid >= p.num_blocks ? p.num_blocks - 1 : pid); };
-        // block id of table entry (kt * KT >> lb) + tid, for threads < ntb; the
-        // entries past the context's last block are never read
+        // raw block id of table entry (kt * KT >> lb) + lane, in lanes < ntb of
+        // every wave (clamped where it is used); entries past the context's
+        // last block are never read
         auto lookup = [&](int kt) {
-            const int e = min(((kt * KT) >> lb) + tid, last_blk);
-            return trow[tid < ntb ? e : 0];
+            const int e = min(((kt * KT) >> lb) + lane, last_blk);
+            return trow[lane < ntb ? e : 0];
         };
         auto head_el = [&](int pid) { return (static_cast<size_t>(pid) * hkv + kv) * blk_el; };
         // byte address of (block pid, this KV head) for a wave-uniform pid:
@@ -361,7 +378,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
         // Issue the loads of tile kt into buffer `buf`; keys past the context
         // are read at the last key's position (their values are masked).
-        auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+        auto issue = [&](int kt, int buf, int traw) __attribute__((always_inline)) {
             unsigned char* bk = lds + buf * SH::BUF_BYTES;
             unsigned char* bv = bk + SH::K_BYTES;
             const int* tb = tbl + (kt & 1) * SH::TBL;
@@ -375,7 +392,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 // (in bounds; masked: scores to -inf, V to zero).
                 constexpr int KPW = KT / kWaves;
                 const int g0 = t0 + KPW * wave;
-                const int pid = __builtin_amdgcn_readfirstlane(tb[(min(g0, lastk) >> lb) - blk0]);
+                const int pid = clamp_pid(__builtin_amdgcn_readlane(traw, (min(g0, lastk) >> lb) - blk0));
                 const char* blk = kbase_kv + head_bytes(pid);
                 const uint32_t k0 = static_cast<uint32_t>((g0 & (bs - 1)) * (D * E));
 #pragma unroll
@@ -557,15 +574,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // ALU computes the exponentials; the operands of step g + 1 are read
         // from LDS one step ahead.
         const int nsteps = (nkeys + 31) / 32;
-        if (tid < SH::TBL) tbl[tid] = clamp_pid(lookup(0));
+        // With blocks of 16 or more tokens each wave reads its block id from
+        // its own lanes of the raw entries (no LDS round trip after the
+        // barrier); smaller blocks go through the table slice in LDS.
+        if (!big) {
+            if (tid < SH::TBL) tbl[tid] = clamp_pid(traw0);
+            __syncthreads();
+        }
+        issue(0, 0, traw0);
+        int treg = traw1;
+        if (!big && tid < SH::TBL) tbl[SH::TBL + tid] = clamp_pid(treg);
         __syncthreads();
-        issue(0, 0);
-        // (a raw table entry: it is clamped only where it is stored, so that
-        // nothing waits for its load before the tile's own loads are issued)
-        int treg = lookup(min(1, nkt - 1));
-        if (tid < SH::TBL) tbl[SH::TBL + tid] = clamp_pid(treg);
-        __syncthreads();
-        if (1 < nkt) issue(1, 1);
+        if (1 < nkt) issue(1, 1, treg);
         treg = lookup(min(2, nkt - 1));
 
         f32x4_t st_a[2][NC], st_b[2][NC];
@@ -589,9 +609,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 // buffer of tile t1 - 1 (its last operands are in registers)
                 // for tile t1 + 1
                 const int t1 = g1 / SPT;
-                if (tid < SH::TBL) tbl[((t1 + 1) & 1) * SH::TBL + tid] = clamp_pid(treg);
+                if (!big && tid < SH::TBL) tbl[((t1 + 1) & 1) * SH::TBL + tid] = clamp_pid(treg);
                 __syncthreads();
-                if (t1 + 1 < nkt) issue(t1 + 1, (t1 + 1) & 1);
+                if (t1 + 1 < nkt) issue(t1 + 1, (t1 + 1) & 1, treg);
                 treg = lookup(min(t1 + 2, nkt - 1));
             }
             const int gn = g1 < nsteps ? g1 : g;
