@@ -236,10 +236,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int kq, pair;
     if (p.pair_major && per_tile % kXcds == 0) {
         const int tiles = gridDim.x / per_tile;
+        const int x = blockIdx.x % kXcds;  // this XCD
         const int k = blockIdx.x / kXcds;  // index on this XCD
-        const int pl = k / tiles;
+        int pl = k / tiles;
         kq = k - pl * tiles;
-        pair = blockIdx.x % kXcds + kXcds * pl;
+        // Longest first: the XCD's pairs x + 8 i are taken in the order of
+        // their sequences' context lengths, longest first (ties by i), so
+        // that the last items to start are short ones. Every wave ranks the
+        // (at most 64) pairs in its lanes itself.
+        const int nx = per_tile / kXcds;
+        if (nx <= 64) {
+            const int li = lane < nx ? p.context_lens[(x + kXcds * lane) / p.num_kv_heads] : -1;
+            int r = 0;
+            for (int i2 = 0; i2 < nx; ++i2) {
+                const int l2 = __builtin_amdgcn_readlane(li, i2);
+                r += (l2 > li) || (l2 == li && i2 < lane);
+            }
+            const unsigned long long hit = __ballot(lane < nx && r == pl);
+            if (hit != 0) pl = __builtin_ctzll(hit);
+        }
+        pair = x + kXcds * pl;
     } else {
         kq = blockIdx.x / per_tile;
         pair = blockIdx.x - kq * per_tile;
