@@ -185,3 +185,38 @@ def test_full_size_workload_sampled_rows(name):
                               pos[rows] + 1, w.scale, w.block_size, oracle.BF16)
     stats = compare_attention(out[torch.from_numpy(rows).to(DEV)], ref, name)
     log(f"[prefill] {name}: {len(rows)} sampled rows {stats}")
+
+
+def _pair_major_case(name):
+    """Batches whose K/V rows exceed the bound for the pair-major item order
+    (each XCD takes whole (sequence, KV head) pairs, longest context first)."""
+    rng = np.random.default_rng(21)
+    if name == "ties":        # every sequence the same length: the rank falls back to the pair index
+        return P.make(name, [1112] * 32, [512] * 32, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                      seed=21)
+    if name == "kv4":         # four KV heads: an XCD's pairs mix sequences and heads
+        return P.make(name, rng.integers(2100, 3001, size=32), [256] * 32, num_heads=16, num_kv_heads=4,
+                      head_dim=128, block_size=16, seed=22)
+    # 72 sequences x 8 KV heads: 72 pairs per XCD, more than one wave ranks
+    return P.make(name, rng.integers(500, 901, size=72), [64] * 72, num_heads=32, num_kv_heads=8, head_dim=128,
+                  block_size=32, seed=23)
+
+
+@pytest.mark.parametrize("name", ["ties", "kv4", "many"])
+def test_pair_major_orders_sampled_rows(name):
+    w = _pair_major_case(name)
+    assert w.num_seqs * w.num_kv_heads * int(w.context_lens.max()) * w.head_dim * 2 * 2 > 128 * 2 ** 20
+    v = P.make_values(w, device=DEV)
+    out = _run(w, v)
+    assert torch.isfinite(out.float()).all(), "non-finite output"
+    rng = np.random.default_rng(6)
+    qs = w.query_start
+    pos = w.positions()
+    seq_of = np.repeat(np.arange(w.num_seqs), w.query_lens)
+    rows = set(qs[:-1].tolist()) | set((qs[1:] - 1).tolist())
+    rows |= set(rng.choice(w.num_tokens, size=32, replace=False).tolist())
+    rows = np.array(sorted(rows))
+    ref = oracle.paged_decode(host_bits(v["q"])[rows], host_bits(v["k_cache"]), host_bits(v["v_cache"]),
+                              w.block_tables[seq_of[rows]], pos[rows] + 1, w.scale, w.block_size, oracle.BF16)
+    stats = compare_attention(out[torch.from_numpy(rows).to(DEV)], ref, name)
+    log(f"[prefill] pair-major {name}: {len(rows)} sampled rows {stats}")
