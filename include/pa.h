@@ -12,7 +12,9 @@
  *   pa_append_block_tables  record each sequence's newest block in its
  *                   device block-table row after a decode append.
  *   pa_append_block_tables_host  the same, taking the step's lengths and
- *                   slots from host memory in the launch arguments.
+ *                   slots from host memory in the launch arguments;
+ *   pa_write_cache_append_host  that append and the step's cache write in
+ *                   one launch.
  *
  * Pages the operations are defined by (cited below by short name):
  *   [aiqz]     aiqz.cc/article/paged-attention-mechanism.html (PagedAttention
@@ -388,6 +390,28 @@ pa_status_t pa_append_block_tables_host(int32_t* block_tables, int max_blocks_pe
                                         const int32_t* host_context_lens, const int32_t* host_slot_mapping,
                                         int32_t* context_lens_out, int32_t* slot_mapping_out, int num_seqs,
                                         int block_size, void* stream);
+
+/*
+ * A decode step's table append and cache write in one launch (per 448
+ * sequences): the same result as
+ *     pa_append_block_tables_host(block_tables, max_blocks_per_seq, host_context_lens, host_slot_mapping,
+ *                                 context_lens_out, slot_mapping_out, num_seqs, block_size, stream)
+ * followed by
+ *     pa_write_cache(k, v, k_cache, v_cache, slot_mapping_out, num_seqs, num_kv_heads, head_dim,
+ *                    block_size, num_blocks, dtype, stream)
+ * ([aiqz] 块表映射机制 and 前缀共享机制: the newest token's block enters its
+ * table row, the token is written into its slot). k, v are
+ * [num_seqs][num_kv_heads][head_dim], row i sequence i's newest token. The
+ * host arrays are read during the call and travel in the launch arguments
+ * (the write takes its slots from there), so the caller may reuse them as
+ * soon as the call returns. Argument rules and errors as those two calls'.
+ */
+pa_status_t pa_write_cache_append_host(const void* k, const void* v, void* k_cache, void* v_cache,
+                                       int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* host_context_lens, const int32_t* host_slot_mapping,
+                                       int32_t* context_lens_out, int32_t* slot_mapping_out, int num_seqs,
+                                       int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                       pa_dtype_t dtype, void* stream);
 
 pa_status_t pa_write_cache_layers(const void* k, const void* v, void* k_cache, void* v_cache,
                                   const int32_t* slot_mapping, int num_tokens, int num_layers,

@@ -405,6 +405,34 @@ def append_block_tables_host(block_tables, context_lens, slot_mapping, context_l
                                                  _stream(block_tables)))
 
 
+def write_cache_append_host(k, v, k_cache, v_cache, block_tables, context_lens, slot_mapping, context_lens_out,
+                            slot_mapping_out):
+    """``append_block_tables_host`` then ``write_cache`` of row i of ``k``/``v``
+    ([num_seqs, num_kv_heads, head_dim]) into slot ``slot_mapping[i]``, in one
+    launch per 448 sequences (``pa_write_cache_append_host``). The lengths and
+    slots are host int32 arrays carried in the launch arguments."""
+    nb, hkv, bs, d = _check_caches(k_cache, v_cache)
+    _dev_tensor(k, "k", dtype=k_cache.dtype, ndim=3)
+    _dev_tensor(v, "v", dtype=k_cache.dtype, ndim=3)
+    _dev_tensor(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev_tensor(context_lens_out, "context_lens_out", dtype=torch.int32, ndim=1)
+    _dev_tensor(slot_mapping_out, "slot_mapping_out", dtype=torch.int32, ndim=1)
+    lens = _host_int32(context_lens, "context_lens")
+    slots = _host_int32(slot_mapping, "slot_mapping")
+    n = block_tables.shape[0]
+    if lens.shape[0] != n or slots.shape[0] != n or context_lens_out.shape[0] != n or slot_mapping_out.shape[0] != n:
+        raise ValueError("one context length and one slot per table row")
+    if tuple(k.shape) != (n, hkv, d) or tuple(v.shape) != (n, hkv, d):
+        raise ValueError("k and v must be [num_seqs, num_kv_heads, head_dim]")
+    if debug_enabled():
+        check_slot_mapping(slots, nb, bs)
+    _check(library().pa_write_cache_append_host(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                                block_tables.data_ptr(), block_tables.shape[1], lens.ctypes.data,
+                                                slots.ctypes.data, context_lens_out.data_ptr(),
+                                                slot_mapping_out.data_ptr(), n, hkv, d, bs, nb,
+                                                _DTYPES[k_cache.dtype], _stream(k_cache)))
+
+
 def alloc_cache_layers(num_layers: int, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
                        dtype=torch.bfloat16, device="cuda"):
     """Uninitialised (k_cache, v_cache) of ``num_layers`` layers in one

@@ -33,7 +33,7 @@ EXPORTED = (
     "pa_decode_workspace_size", "pa_decode_plan", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
     "pa_decode_noalloc",
     "pa_prefill", "pa_write_cache", "pa_copy_blocks", "pa_write_cache_layers", "pa_copy_blocks_layers",
-    "pa_append_block_tables", "pa_append_block_tables_host",
+    "pa_append_block_tables", "pa_append_block_tables_host", "pa_write_cache_append_host",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_prefill", "pa_bm_share", "pa_bm_append", "pa_bm_free",
     "pa_bm_block_tables", "pa_bm_num_free", "pa_bm_blocks_in_use", "pa_bm_refcount", "pa_bm_seq_tokens",
     "pa_bm_blocks_without_sharing", "pa_bm_check", "pa_probe_read_tiles",
@@ -93,6 +93,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.pa_append_block_tables.argtypes = [_vp, _i, _vp, _vp, _i, _i, _vp]
         lib.pa_append_block_tables_host.restype = _i
         lib.pa_append_block_tables_host.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _vp]
+        lib.pa_write_cache_append_host.restype = _i
+        lib.pa_write_cache_append_host.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                                                   _i, _i, _vp]
         lib.pa_copy_blocks.restype = _i
         lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
         _i64 = ctypes.c_int64

@@ -650,4 +650,37 @@ pa_status_t pa_append_block_tables_host(int32_t* block_tables, int max_blocks_pe
     return PA_OK;
 }
 
+pa_status_t pa_write_cache_append_host(const void* k, const void* v, void* k_cache, void* v_cache,
+                                       int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* host_context_lens, const int32_t* host_slot_mapping,
+                                       int32_t* context_lens_out, int32_t* slot_mapping_out, int num_seqs,
+                                       int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                       pa_dtype_t dtype, void* stream) {
+    if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size (num_seqs=%d max_blocks_per_seq=%d num_kv_heads=%d "
+                    "head_dim=%d block_size=%d num_blocks=%d)", num_seqs, max_blocks_per_seq, num_kv_heads, head_dim,
+                    block_size, num_blocks);
+    if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    const int row_bytes = head_dim * elem_bytes(dtype);
+    if (row_bytes % 16 != 0)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim * element size = %d bytes is not a multiple of 16", row_bytes);
+    if (row_bytes > 32 * 1024)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim * element size = %d bytes is more than 32768", row_bytes);
+    if (!is_pow2(block_size) || block_size < 4 || block_size > 256)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a power of two in [4, 256]", block_size);
+    if (num_seqs == 0) return PA_OK;
+    if (!k || !v || !k_cache || !v_cache || !block_tables || !host_context_lens || !host_slot_mapping ||
+        !context_lens_out || !slot_mapping_out)
+        return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PA_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
+    hipError_t e = pa::launch_write_stage(k, v, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                                          host_context_lens, host_slot_mapping, context_lens_out, slot_mapping_out,
+                                          num_seqs, num_kv_heads, head_dim, elem_bytes(dtype), block_size,
+                                          num_blocks, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "table append and cache write kernel launch");
+    return PA_OK;
+}
+
 }  // extern "C"

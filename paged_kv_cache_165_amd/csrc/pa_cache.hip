@@ -51,14 +51,11 @@ __host__ __device__ constexpr int write_lds_row(int head_dim, int elem_bytes) {
 // token (and end any run).
 
 template <typename EW>
-__global__ __launch_bounds__(256) void pa_write_kernel(const u32x4* __restrict__ k,
-                                                       const u32x4* __restrict__ v,
-                                                       u32x4* __restrict__ kc,
-                                                       EW* __restrict__ vc,
-                                                       const int32_t* __restrict__ slots,
-                                                       int num_tokens, int num_kv_heads, int head_dim,
-                                                       int row16, int log2_bs, int log2_vt, int log2_chunk,
-                                                       int log2_win, long long pool_slots) {
+__device__ __forceinline__ void write_tokens(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                             u32x4* __restrict__ kc, EW* __restrict__ vc,
+                                             const int32_t* __restrict__ slots, int num_tokens, int num_kv_heads,
+                                             int head_dim, int row16, int log2_bs, int log2_vt, int log2_chunk,
+                                             int log2_win, long long pool_slots) {
     constexpr int E = sizeof(EW);
     {
         // this workgroup's layer: pool_slots is also the cache's layer
@@ -158,6 +155,19 @@ __global__ __launch_bounds__(256) void pa_write_kernel(const u32x4* __restrict__
     }
 }
 
+template <typename EW>
+__global__ __launch_bounds__(256) void pa_write_kernel(const u32x4* __restrict__ k,
+                                                       const u32x4* __restrict__ v,
+                                                       u32x4* __restrict__ kc,
+                                                       EW* __restrict__ vc,
+                                                       const int32_t* __restrict__ slots,
+                                                       int num_tokens, int num_kv_heads, int head_dim,
+                                                       int row16, int log2_bs, int log2_vt, int log2_chunk,
+                                                       int log2_win, long long pool_slots) {
+    write_tokens<EW>(k, v, kc, vc, slots, num_tokens, num_kv_heads, head_dim, row16, log2_bs, log2_vt, log2_chunk,
+                     log2_win, pool_slots);
+}
+
 // grid (pairs, 2, layers): y = 0 copies K, y = 1 copies V, z is the layer
 // (its caches start z * num_blocks * block16 vectors in). A block is
 // contiguous ([Hkv][B][D]), so the copy is one linear run of block16 vectors.
@@ -240,6 +250,45 @@ __global__ __launch_bounds__(kStageSeqs) void pa_stage_append_kernel(StageArgs a
     a.tables[static_cast<size_t>(i) * a.max_blocks + col] = slot >> a.log2_bs;
 }
 
+// The table append of pa_stage_append_kernel and the cache write of the
+// step's new tokens in one launch: the lengths and slots travel in the
+// launch arguments, and the write reads its slots from there too (no slot
+// load from memory). Workgroup (x, 0) also does the append for its chunk of
+// sequences; every workgroup then writes as pa_write_kernel does.
+struct WriteGeom {
+    const u32x4* k;
+    const u32x4* v;
+    u32x4* kc;
+    void* vc;
+    long long pool_slots;
+    int num_kv_heads;
+    int head_dim;
+    int row16;
+    int log2_vt;
+    int log2_chunk;
+    int log2_win;
+};
+static_assert(sizeof(StageArgs) + sizeof(WriteGeom) <= 4000, "kernel arguments are limited to 4 KB");
+
+template <typename EW>
+__global__ __launch_bounds__(256) void pa_write_stage_kernel(StageArgs a, WriteGeom g) {
+    if (blockIdx.y == 0 && threadIdx.x < (1u << g.log2_chunk)) {
+        const int i = (blockIdx.x << g.log2_chunk) + threadIdx.x;
+        if (i < a.num_seqs) {
+            const int L = a.lens[i];
+            const int slot = a.slots[i];
+            a.lens_out[i] = L;
+            a.slots_out[i] = slot;
+            if (L > 0 && slot >= 0) {
+                const int col = (L - 1) >> a.log2_bs;
+                if (col < a.max_blocks) a.tables[static_cast<size_t>(i) * a.max_blocks + col] = slot >> a.log2_bs;
+            }
+        }
+    }
+    write_tokens<EW>(g.k, g.v, g.kc, static_cast<EW*>(g.vc), a.slots, a.num_seqs, g.num_kv_heads, g.head_dim,
+                     g.row16, a.log2_bs, g.log2_vt, g.log2_chunk, g.log2_win, g.pool_slots);
+}
+
 hipError_t launch_stage_append(int32_t* tables, int max_blocks, const int32_t* host_lens,
                                const int32_t* host_slots, int32_t* lens_out, int32_t* slots_out, int num_seqs,
                                int block_size, hipStream_t stream) {
@@ -293,6 +342,55 @@ hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void*
                          static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
                          static_cast<u32x4*>(k_cache), static_cast<uint32_t*>(v_cache), slots, num_tokens,
                          num_kv_heads, head_dim, row16, log2_bs, log2_vt, log2_chunk, log2_win, pool_slots);
+}
+
+hipError_t launch_write_stage(const void* k, const void* v, void* k_cache, void* v_cache, int32_t* tables,
+                              int max_blocks, const int32_t* host_lens, const int32_t* host_slots, int32_t* lens_out,
+                              int32_t* slots_out, int num_seqs, int num_kv_heads, int head_dim, int elem_bytes,
+                              int block_size, int num_blocks, hipStream_t stream) {
+    const int row16 = head_dim * elem_bytes / 16;
+    const int ld = write_lds_row(head_dim, elem_bytes);
+    // the write's geometry, as launch_write_cache chooses it
+    int log2_chunk = 4, log2_win = 5;
+    if ((static_cast<size_t>(1) << log2_win) * ld * elem_bytes > 64 * 1024) {
+        while (log2_chunk > 0 && (static_cast<size_t>(1) << log2_chunk) * ld * elem_bytes > 32 * 1024) --log2_chunk;
+        log2_win = log2_chunk;
+    }
+    const size_t smem = (static_cast<size_t>(1) << log2_win) * ld * elem_bytes;
+    if (smem > 64 * 1024) return hipErrorInvalidConfiguration;
+    const int log2_bs = ilog2(block_size);
+    WriteGeom g;
+    g.kc = static_cast<u32x4*>(k_cache);
+    g.vc = v_cache;
+    g.pool_slots = static_cast<long long>(num_blocks) * block_size;
+    g.num_kv_heads = num_kv_heads;
+    g.head_dim = head_dim;
+    g.row16 = row16;
+    g.log2_vt = ilog2(v_tile_tokens(block_size));
+    g.log2_chunk = log2_chunk;
+    g.log2_win = log2_win;
+    for (int i0 = 0; i0 < num_seqs; i0 += kStageSeqs) {
+        StageArgs a;
+        const int n = std::min(kStageSeqs, num_seqs - i0);
+        a.tables = tables + static_cast<size_t>(i0) * max_blocks;
+        a.lens_out = lens_out + i0;
+        a.slots_out = slots_out + i0;
+        a.max_blocks = max_blocks;
+        a.num_seqs = n;
+        a.log2_bs = log2_bs;
+        std::memcpy(a.lens, host_lens + i0, sizeof(int32_t) * n);
+        std::memcpy(a.slots, host_slots + i0, sizeof(int32_t) * n);
+        const size_t row0 = static_cast<size_t>(i0) * num_kv_heads * row16;
+        g.k = static_cast<const u32x4*>(k) + row0;
+        g.v = static_cast<const u32x4*>(v) + row0;
+        const dim3 grid(static_cast<unsigned>((n + (1 << log2_chunk) - 1) >> log2_chunk),
+                        static_cast<unsigned>(num_kv_heads), 1);
+        const hipError_t e = elem_bytes == 2
+                                 ? launch_kernel(pa_write_stage_kernel<uint16_t>, grid, dim3(256), smem, stream, a, g)
+                                 : launch_kernel(pa_write_stage_kernel<uint32_t>, grid, dim3(256), smem, stream, a, g);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,

@@ -167,6 +167,12 @@ constexpr int kStageSeqs = 448;
 hipError_t launch_stage_append(int32_t* tables, int max_blocks, const int32_t* host_lens,
                                const int32_t* host_slots, int32_t* lens_out, int32_t* slots_out, int num_seqs,
                                int block_size, hipStream_t stream);
+// launch_stage_append followed by launch_write_cache of the step's one token
+// per sequence, in one launch per kStageSeqs sequences
+hipError_t launch_write_stage(const void* k, const void* v, void* k_cache, void* v_cache, int32_t* tables,
+                              int max_blocks, const int32_t* host_lens, const int32_t* host_slots, int32_t* lens_out,
+                              int32_t* slots_out, int num_seqs, int num_kv_heads, int head_dim, int elem_bytes,
+                              int block_size, int num_blocks, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
                               int num_layers, size_t block_bytes, int num_blocks, hipStream_t stream);
 

@@ -34,13 +34,17 @@ from .blocks import BlockManager
 class Step:
     """What a decode step shares across a model's layers: the device slot
     mapping, lengths and block tables of its sequences and the host views of
-    its slots and copy pairs (valid until the step after next)."""
+    its slots and copy pairs (valid until the step after next). ``stage``
+    holds the host lengths and slots while the table append that stores them
+    to the device is still to be launched (with the step's first cache write,
+    in one launch)."""
 
-    __slots__ = ("n", "slots", "pairs", "d_slots", "d_lens", "d_tables", "max_ctx")
+    __slots__ = ("n", "slots", "pairs", "d_slots", "d_lens", "d_tables", "max_ctx", "stage")
 
-    def __init__(self, n, slots, pairs, d_slots, d_lens, d_tables, max_ctx):
+    def __init__(self, n, slots, pairs, d_slots, d_lens, d_tables, max_ctx, stage=None):
         self.n, self.slots, self.pairs = n, slots, pairs
         self.d_slots, self.d_lens, self.d_tables, self.max_ctx = d_slots, d_lens, d_tables, max_ctx
+        self.stage = stage
 
 
 class PagedDecoder:
@@ -85,6 +89,7 @@ class PagedDecoder:
         self._dtables = None  # device block tables [cap, max_blocks] of the rows in self._rows
         self._rows = None     # int64 sequence ids of those rows, or None once any table may differ
         self._lens = None     # host copy of the rows' context lengths
+        self._pending = None  # a begun step whose table append waits for its first cache write
 
     # -- host -> device -----------------------------------------------------
     def _dev(self, a: np.ndarray) -> torch.Tensor:
@@ -185,6 +190,7 @@ class PagedDecoder:
         attention follow per layer in ``decode_layer``."""
         s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
         n = len(s)
+        self._flush_stage()
         st = self._staging_for(n)
         host, dev = st["host"], st["dev"]
         h = host.numpy()
@@ -225,8 +231,11 @@ class PagedDecoder:
         d_slots, d_lens = dev[:n], dev[n:2 * n]
         d_pairs = dev[2 * n:2 * n + 2 * npairs].view(npairs, 2)
         d_tables = self._dtables[:n]
+        stage = None
         if same_rows:
-            self._pa.append_block_tables_host(d_tables, lens, slots, d_lens, d_slots, self.block_size)
+            # the table append goes with the step's first cache write
+            # (decode_layer), in one launch
+            stage = (lens, slots)
         else:
             d_tables.copy_(dev[4 * n:4 * n + n * self.max_blocks].view(n, self.max_blocks))
             self._rows = s.copy()
@@ -234,7 +243,19 @@ class PagedDecoder:
             copy = self._pa.copy_blocks_layers if self.num_layers > 1 else self._pa.copy_blocks
             copy(self.k_cache, self.v_cache, d_pairs)
         max_ctx = int(lens.max()) if n else 0
-        return Step(n, slots, pairs[:npairs], d_slots, d_lens, d_tables, max_ctx)
+        step = Step(n, slots, pairs[:npairs], d_slots, d_lens, d_tables, max_ctx, stage)
+        self._pending = step if stage is not None else None
+        return step
+
+    def _flush_stage(self) -> None:
+        """Launch a begun step's table append on its own if no cache write
+        took it."""
+        step, self._pending = self._pending, None
+        if step is not None and step.stage is not None:
+            lens, slots = step.stage
+            step.stage = None
+            self._pa.append_block_tables_host(step.d_tables, lens, slots, step.d_lens, step.d_slots,
+                                              self.block_size)
 
     def decode_layer(self, step: Step, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      scale: float, out: torch.Tensor = None) -> torch.Tensor:
@@ -243,7 +264,13 @@ class PagedDecoder:
         decode: attention of ``q`` [n, Hq, D] over each sequence's tokens,
         the new one included. Layers may run in any order, each once."""
         kc, vc = self.layer_caches(layer)
-        self._pa.write_cache(k, v, kc, vc, step.d_slots)
+        if step.stage is not None:
+            lens, slots = step.stage
+            step.stage = None
+            self._pending = None
+            self._pa.write_cache_append_host(k, v, kc, vc, step.d_tables, lens, slots, step.d_lens, step.d_slots)
+        else:
+            self._pa.write_cache(k, v, kc, vc, step.d_slots)
         if out is None:
             out = torch.empty_like(q)
         self._pa.decode(out, q, kc, vc, step.d_tables, step.d_lens, scale,

@@ -192,6 +192,55 @@ def test_append_block_tables_host_matches_device_call(n):
     assert not (changed & ~expect).any()
 
 
+WRITE_STAGE = [(1, torch.bfloat16, 128, 16), (300, torch.bfloat16, 128, 16), (449, torch.float32, 64, 4),
+               (1000, torch.bfloat16, 256, 64), (512, torch.float16, 128, 32)]
+
+
+@pytest.mark.parametrize("n,dt,d,bs", WRITE_STAGE, ids=[f"n{n}-{str(dt)[6:]}-D{d}-B{bs}" for n, dt, d, bs in WRITE_STAGE])
+def test_write_cache_append_host_matches_two_calls(n, dt, d, bs):
+    """pa_write_cache_append_host gives the tables, device lengths and slots
+    of pa_append_block_tables_host and the caches of pa_write_cache from the
+    same host lengths and slots, bit for bit, and the caches of the oracle's
+    write; batches over 448 sequences take several launches. Slots are
+    distinct (a random sample of the pool), some skipped (-1); rows with no
+    token or a column past the table width keep their table entries."""
+    import paged_kv_cache_165_amd as pa
+    rng = np.random.default_rng(n + d + bs)
+    hkv, maxb = 2, 9
+    nb = max(64, (2 * n) // bs + 8)
+    lens = rng.integers(0, maxb * bs + 20, size=n).astype(np.int32)
+    slots = rng.choice(nb * bs, size=n, replace=False).astype(np.int32)
+    slots[rng.random(n) < 0.1] = -1
+    tab0 = rng.integers(0, nb, size=(n, maxb)).astype(np.int32)
+    g = torch.Generator(device=DEV).manual_seed(n + d)
+    k = _rand(g, (n, hkv, d), dt)
+    v = _rand(g, (n, hkv, d), dt)
+    kc0, vc0 = pa.alloc_cache(nb, hkv, bs, d, dtype=dt, device=DEV)
+    kc0.copy_(_rand(g, kc0.shape, dt))
+    vc0.copy_(_rand(g, vc0.shape, dt))
+    outs = []
+    for fused in (False, True):
+        kc, vc = kc0.clone(), vc0.clone()
+        tab = torch.from_numpy(tab0).to(DEV)
+        lens_out = torch.full((n,), -9, dtype=torch.int32, device=DEV)
+        slots_out = torch.full((n,), -9, dtype=torch.int32, device=DEV)
+        host_lens, host_slots = lens.copy(), slots.copy()
+        if fused:
+            pa.write_cache_append_host(k, v, kc, vc, tab, host_lens, host_slots, lens_out, slots_out)
+        else:
+            pa.append_block_tables_host(tab, host_lens, host_slots, lens_out, slots_out, bs)
+            pa.write_cache(k, v, kc, vc, slots_out)
+        host_lens[:] = 0          # the call has read them: reusing the arrays changes nothing
+        host_slots[:] = -1
+        torch.cuda.synchronize()
+        outs.append((tab, lens_out, slots_out, kc, vc))
+    for a, b in zip(outs[0], outs[1]):
+        assert raw_equal(b, host_bits(a))
+    kc_o, vc_o = oracle.write_cache(host_bits(k), host_bits(v), host_bits(kc0), host_bits(vc0), slots, bs)
+    assert raw_equal(outs[1][3], kc_o) and raw_equal(outs[1][4], vc_o)
+    assert np.array_equal(outs[1][1].cpu().numpy(), lens) and np.array_equal(outs[1][2].cpu().numpy(), slots)
+
+
 def test_multi_layer_steps_match_oracle_per_layer():
     """Three layers sharing one block table per sequence: prompts written
     into every layer in one launch, forks sharing partly filled blocks (the
