@@ -192,6 +192,49 @@ def test_append_block_tables_host_matches_device_call(n):
     assert not (changed & ~expect).any()
 
 
+def test_engine_step_without_decode_still_appends_tables():
+    """A step whose table append waits for its first cache write, begun and
+    never decoded: the next begin_step launches that append on its own (the
+    begun step's device lengths and slots are stored), and the next step's
+    decode, whose own append goes with its write, leaves the device tables and
+    lengths equal to the manager's and matches the oracle (the skipped step's
+    token keeps whatever its slot held, on the device and in the mirror
+    alike)."""
+    from paged_kv_cache_165_amd.engine import PagedDecoder
+    dtype, bs, hq, hkv, d = torch.bfloat16, 16, 8, 2, 64
+    g = torch.Generator(device=DEV).manual_seed(77)
+    rng = np.random.default_rng(77)
+    nb = 64
+    eng = PagedDecoder(nb, bs, hq, hkv, d, max_blocks_per_seq=12, dtype=dtype, free_order=rng.permutation(nb))
+    eng.k_cache.copy_(_rand(g, eng.k_cache.shape, dtype))
+    eng.v_cache.copy_(_rand(g, eng.v_cache.shape, dtype))
+    seqs = [0, 1, 2]
+    for i, n in zip(seqs, (5, 14, 31)):
+        eng.prefill(i, _rand(g, (n, hkv, d), dtype), _rand(g, (n, hkv, d), dtype))
+    scale = 0.125
+    q, k, v = (_rand(g, (3, hq, d), dtype), _rand(g, (3, hkv, d), dtype), _rand(g, (3, hkv, d), dtype))
+    eng.step(seqs, q, k, v, scale)             # sets up the rows: the next steps reuse them
+    skipped = eng.begin_step(seqs)             # begun, never decoded
+    skipped_lens = skipped.slots.copy(), eng.tables(seqs)[1]
+    step = eng.begin_step(seqs)                # launches the skipped step's append first
+    torch.cuda.synchronize()
+    assert np.array_equal(skipped.d_slots.cpu().numpy(), skipped_lens[0])
+    assert np.array_equal(skipped.d_lens.cpu().numpy(), skipped_lens[1])
+    kc_h, vc_h = host_bits(eng.k_cache), host_bits(eng.v_cache)
+    q, k, v = (_rand(g, (3, hq, d), dtype), _rand(g, (3, hkv, d), dtype), _rand(g, (3, hkv, d), dtype))
+    out = eng.decode_layer(step, 0, q, k, v, scale)
+    torch.cuda.synchronize()
+    tables, lens = eng.tables(seqs)
+    dev_tab = step.d_tables.cpu().numpy()
+    for r in range(3):
+        nblk = -(-int(lens[r]) // bs)
+        assert np.array_equal(dev_tab[r, :nblk], tables[r, :nblk]), r
+    assert np.array_equal(step.d_lens.cpu().numpy(), lens)
+    kc_h, vc_h = oracle.write_cache(host_bits(k), host_bits(v), kc_h, vc_h, step.slots[:3].copy(), bs)
+    ref = oracle.paged_decode(host_bits(q), kc_h, vc_h, tables, lens, scale, bs, ORACLE_DTYPE[dtype])
+    compare_attention(out, ref, "step after an undecoded step")
+
+
 WRITE_STAGE = [(1, torch.bfloat16, 128, 16), (300, torch.bfloat16, 128, 16), (449, torch.float32, 64, 4),
                (1000, torch.bfloat16, 256, 64), (512, torch.float16, 128, 32)]
 
