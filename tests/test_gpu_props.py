@@ -238,6 +238,35 @@ def test_largest_batch():
     compare_attention(out, run_oracle(c, 0.125), "8192 seqs")
 
 
+def test_shape_beyond_the_lds_is_refused_before_launch():
+    """A valid shape whose launch plan does not fit the compute unit's LDS
+    (8192 sequences, 16 query heads per KV head, head_dim 256: the stream
+    split's schedule and query blocks) is refused with PA_ERR_UNSUPPORTED on
+    the host, naming the LDS, and nothing is launched: the output keeps its
+    contents. The same shape with fewer sequences runs."""
+    import paged_kv_cache_165_amd as pa
+    from paged_kv_cache_165_amd import _lib
+    s, hkv, g, d, bs = 8192, 2, 16, 256, 16
+    with pytest.raises(pa.PaError):
+        pa.decode_plan(s, hkv * g, hkv, d, 1, bs, 0, torch.bfloat16)
+    q = torch.zeros(s, hkv * g, d, dtype=torch.bfloat16, device=DEV)
+    kc, vc = pa.alloc_cache(s, hkv, bs, d, dtype=torch.bfloat16, device=DEV)
+    kc.zero_()
+    vc.zero_()
+    tables = torch.arange(s, dtype=torch.int32, device=DEV).view(s, 1)
+    lens = torch.ones(s, dtype=torch.int32, device=DEV)
+    out = torch.full_like(q, 7.0)
+    with pytest.raises(pa.PaError) as err:
+        pa.decode(out, q, kc, vc, tables, lens, 0.0625, max_context_len=1)
+    assert err.value.status == _lib.PA_ERR_UNSUPPORTED and "LDS" in str(err.value)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    n = 1024
+    pa.decode(out[:n], q[:n], kc, vc, tables[:n], lens[:n], 0.0625, max_context_len=1)
+    torch.cuda.synchronize()
+    assert bool((out[:n] == 0).all()) and bool((out[n:] == 7.0).all())
+
+
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 def test_one_pair_split_over_every_wave(dt):
     """One (sequence, KV head) pair of 65,536 tokens: the stream split gives
