@@ -310,24 +310,33 @@ hipError_t launch_stage_append(int32_t* tables, int max_blocks, const int32_t* h
     return hipSuccess;
 }
 
+// The write's chunking: run mode is 16 entries per workgroup, with V
+// staging for up to 31 tokens (the chunk and the rest of its last run) when
+// 32 rows fit in 64 KB of LDS. Otherwise plain chunks of 16 entries, fewer
+// for rows so wide that 16 would not fit in 32 KB. Returns false if no
+// chunk fits.
+static bool write_geometry(int head_dim, int elem_bytes, int* log2_chunk, int* log2_win, size_t* smem) {
+    const int ld = write_lds_row(head_dim, elem_bytes);
+    int c = 4, w = 5;
+    if ((static_cast<size_t>(1) << w) * ld * elem_bytes > 64 * 1024) {
+        while (c > 0 && (static_cast<size_t>(1) << c) * ld * elem_bytes > 32 * 1024) --c;
+        w = c;
+    }
+    *log2_chunk = c;
+    *log2_win = w;
+    *smem = (static_cast<size_t>(1) << w) * ld * elem_bytes;
+    return *smem <= 64 * 1024;
+}
+
 hipError_t launch_write_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                               const int32_t* slots, int num_tokens, int num_layers, int num_kv_heads,
                               int head_dim, int elem_bytes, int block_size, int num_blocks,
                               hipStream_t stream) {
     if (num_tokens == 0 || num_layers == 0) return hipSuccess;
     const int row16 = head_dim * elem_bytes / 16;
-    const int ld = write_lds_row(head_dim, elem_bytes);
-    // Run mode: 16 entries per workgroup, V staging for up to 31 tokens (the
-    // chunk and the rest of its last run) when 32 rows fit in 64 KB of LDS.
-    // Otherwise plain chunks of 16 entries, fewer for rows so wide that 16
-    // would not fit in 32 KB.
-    int log2_chunk = 4, log2_win = 5;
-    if ((static_cast<size_t>(1) << log2_win) * ld * elem_bytes > 64 * 1024) {
-        while (log2_chunk > 0 && (static_cast<size_t>(1) << log2_chunk) * ld * elem_bytes > 32 * 1024) --log2_chunk;
-        log2_win = log2_chunk;
-    }
-    const size_t smem = (static_cast<size_t>(1) << log2_win) * ld * elem_bytes;
-    if (smem > 64 * 1024) return hipErrorInvalidConfiguration;
+    int log2_chunk = 0, log2_win = 0;
+    size_t smem = 0;
+    if (!write_geometry(head_dim, elem_bytes, &log2_chunk, &log2_win, &smem)) return hipErrorInvalidConfiguration;
     const int log2_bs = ilog2(block_size);
     const int log2_vt = ilog2(v_tile_tokens(block_size));
     const long long pool_slots = static_cast<long long>(num_blocks) * block_size;
@@ -349,15 +358,9 @@ hipError_t launch_write_stage(const void* k, const void* v, void* k_cache, void*
                               int32_t* slots_out, int num_seqs, int num_kv_heads, int head_dim, int elem_bytes,
                               int block_size, int num_blocks, hipStream_t stream) {
     const int row16 = head_dim * elem_bytes / 16;
-    const int ld = write_lds_row(head_dim, elem_bytes);
-    // the write's geometry, as launch_write_cache chooses it
-    int log2_chunk = 4, log2_win = 5;
-    if ((static_cast<size_t>(1) << log2_win) * ld * elem_bytes > 64 * 1024) {
-        while (log2_chunk > 0 && (static_cast<size_t>(1) << log2_chunk) * ld * elem_bytes > 32 * 1024) --log2_chunk;
-        log2_win = log2_chunk;
-    }
-    const size_t smem = (static_cast<size_t>(1) << log2_win) * ld * elem_bytes;
-    if (smem > 64 * 1024) return hipErrorInvalidConfiguration;
+    int log2_chunk = 0, log2_win = 0;
+    size_t smem = 0;
+    if (!write_geometry(head_dim, elem_bytes, &log2_chunk, &log2_win, &smem)) return hipErrorInvalidConfiguration;
     const int log2_bs = ilog2(block_size);
     WriteGeom g;
     g.kc = static_cast<u32x4*>(k_cache);
