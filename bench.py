@@ -27,15 +27,17 @@ METRIC = "paged decode attention: KV GB/s read (% of HBM peak), seqs/sec"
 HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_165_amd", "csrc", "pa_decode.hip")
+PREFILL_SOURCE = os.path.join(ROOT, "paged_kv_cache_165_amd", "csrc", "pa_prefill.hip")
+PREFILL_KERNELS = ("pa_prefill_mfma", "pa_prefill_f32")
 PARTITION_KERNELS = ("pa_decode_stream", "pa_decode_mfma", "pa_decode_valu")
 PLAN_KERNELS = {"valu": "pa_decode_valu", "mfma": "pa_decode_mfma", "mfma_wave": "pa_decode_mfma_wave",
                 "mfma_stream": "pa_decode_stream"}
 CALIBRATION_KERNEL = "neg_kernel"  # torch's elementwise negate: reads N bytes, writes N bytes
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(path: str = KERNEL_SOURCE) -> str:
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -129,21 +131,29 @@ def resolved_partition(w) -> int:
                                                          w.max_context_len, w.block_size, dt)
 
 
-def summarize_counters(fetch_csv, write_csv, out_json, workload, calib_mb, partition_size=0):
+def summarize_counters(fetch_csv, write_csv, out_json, workload, calib_mb, partition_size=0, prefill=None):
     """Scale per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the partition
-    kernel by what the same counters read for a copy of known size. The
-    record keeps the kernel source hash and the partition size the counters
-    were taken with; the bench reports them only while both still hold."""
+    kernel (with ``prefill``: of the prefill kernel, recorded under the
+    prefill workload's name) by what the same counters read for a copy of
+    known size. The record keeps the kernel source hash and (decode) the
+    partition size the counters were taken with; the bench reports them only
+    while both still hold."""
     import workloads as W
-    w = W.build(workload)
-    if partition_size:
-        w.partition_size = partition_size
+    kernels, source = PARTITION_KERNELS, KERNEL_SOURCE
+    if prefill:
+        from workloads import prefill as P
+        w = P.BUILDERS[prefill]()
+        workload, kernels, source = w.name, PREFILL_KERNELS, PREFILL_SOURCE
+    else:
+        w = W.build(workload)
+        if partition_size:
+            w.partition_size = partition_size
     calib_bytes = calib_mb * (1 << 20)
     res = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path, counter)
         cal = [v for n, v in rows if CALIBRATION_KERNEL in n]
-        part = [v for n, v in rows if any(k in n for k in PARTITION_KERNELS)]
+        part = [v for n, v in rows if any(k in n for k in kernels)]
         if not cal or not part:
             raise SystemExit(f"{path}: no {counter} rows for the calibration copy or the partition kernel")
         scale = calib_bytes / (sum(cal) / len(cal) * 1024.0)
@@ -159,8 +169,8 @@ def summarize_counters(fetch_csv, write_csv, out_json, workload, calib_mb, parti
         "read_bytes": round(res["FETCH_SIZE"]["partition_bytes"]),
         "write_bytes": round(res["WRITE_SIZE"]["partition_bytes"]),
         "fetch_scale": res["FETCH_SIZE"]["scale"], "write_scale": res["WRITE_SIZE"]["scale"],
-        "calibration_mb": calib_mb, "kernel_source_sha256_16": kernel_source_hash(),
-        "partition_size": resolved_partition(w), "counters": res,
+        "calibration_mb": calib_mb, "kernel_source_sha256_16": kernel_source_hash(source),
+        "partition_size": None if prefill else resolved_partition(w), "counters": res,
     }
     with open(out_json, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
@@ -520,6 +530,24 @@ def prefill_bench(args, dev):
     kb.record()
     torch.cuda.synchronize()
     k_us = 1e3 * ka.elapsed_time(kb) / args.steps
+    if args.copy_calibration_mb:
+        # the copy of known size the counter summary scales by
+        n = args.copy_calibration_mb * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    traffic = None  # counter bytes, valid only for the kernel source they were taken on
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                tj = json.load(f).get(w.name)
+            if tj and tj.get("kernel_source_sha256_16") == kernel_source_hash(PREFILL_SOURCE):
+                traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
     flops = w.flops()
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (k_us * 1e-6) / 1e12
@@ -542,7 +570,8 @@ def prefill_bench(args, dev):
         "tokens_per_s": round(w.num_tokens / (ms_step * 1e-3), 1),
         "roofline": {"bound": "mfma", "kernel": "pa_prefill (pa_prefill_mfma)", "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "traffic_gbs": round(traffic / (k_us * 1e-6) / 1e9, 2) if traffic else None,
                      "kernel_us_mean": round(k_us, 2),
                      "kernel_timing": f"{args.steps} back-to-back launches between two HIP events on the launch stream"},
         "cpu_baseline": cpu,
@@ -553,7 +582,7 @@ def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.traffic_json,
-                           args.workload, args.copy_calibration_mb, args.partition_size or 0)
+                           args.workload, args.copy_calibration_mb, args.partition_size or 0, args.prefill)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this library has no multi-GPU path "
