@@ -572,9 +572,11 @@ pa_status_t pa_prefill(void* out, const void* q, const void* k_cache, const void
     // The K/V rows the batch attends to, at most: when they cannot stay in
     // half of MI355X's 256 MB last-level cache, the query tiles of one
     // (sequence, KV head) pair are kept together on one XCD so that they
-    // share its L2 (measured: 503 against 589 us on 32 chunks of 512 tokens
-    // after histories of up to 3072; whole 2048-token prompts, whose 67 MB
-    // stay cached, run about 3 % faster tile-major).
+    // share its L2 (measured: 455-459 against 562 us on 32 chunks of 512
+    // tokens after histories of up to 3072; whole 2048-token prompts, whose
+    // 67 MB stay in the last-level cache, run within noise of each other in
+    // both orders, tile-major fetching about three times their K/V and
+    // queries past the L2).
     const double kv_bound = static_cast<double>(num_seqs) * num_kv_heads * max_context_len * head_dim *
                             elem_bytes(dtype) * 2.0;
     p.pair_major = kv_bound > 128.0 * (1 << 20) ? 1 : 0;
