@@ -254,6 +254,46 @@ def test_append_block_tables_host_rejects_before_launch(args, status, msg):
 
 
 
+# (k, v, k_cache, v_cache, block_tables, max_blocks, host_lens, host_slots, lens_out, slots_out,
+#  num_seqs, num_kv_heads, head_dim, block_size, num_blocks, dtype)
+_WS = (16, 32, 48, 64, 80, 4, 96, 112, 128, 144, 2, 2, 128, 16, 10, 1)
+
+
+def _ws(**kw):
+    names = ("k", "v", "kc", "vc", "tab", "maxb", "lens", "slots", "lens_out", "slots_out", "n", "hkv", "d", "bs",
+             "nb", "dt")
+    a = dict(zip(names, _WS))
+    a.update(kw)
+    return tuple(a[n] for n in names)
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    (_ws(n=-1), 1, b"zero size"),
+    (_ws(maxb=0), 1, b"zero size"),
+    (_ws(d=0), 1, b"zero size"),
+    (_ws(nb=0), 1, b"zero size"),
+    (_ws(dt=7), 1, b"unknown dtype"),
+    (_ws(d=4), 2, b"multiple of 16"),
+    (_ws(d=16384, dt=0), 2, b"more than 32768"),
+    (_ws(bs=12), 2, b"power of two"),
+    (_ws(bs=2), 2, b"power of two"),
+    (_ws(bs=512), 2, b"power of two"),
+    (_ws(k=0), 1, b"null pointer"),
+    (_ws(tab=0), 1, b"null pointer"),
+    (_ws(lens=0), 1, b"null pointer"),
+    (_ws(slots_out=0), 1, b"null pointer"),
+    (_ws(v=40), 1, b"aligned"),
+    (_ws(kc=8), 1, b"aligned"),
+])
+def test_write_cache_append_host_rejects_before_launch(args, status, msg):
+    """The append-and-write call checks its arguments before anything is
+    launched; the pointer values here are never dereferenced."""
+    lib, _ = _lib()
+    assert lib.pa_write_cache_append_host(*args, None) == status
+    assert msg in lib.pa_last_error()
+    assert lib.pa_write_cache_append_host(*_ws(k=0, v=0, kc=0, vc=0, tab=0, n=0), None) == 0  # empty batch
+
+
 def test_headers_and_library_usable_from_plain_c(tmp_path):
     """include/pa.h and include/pa_blocks.h compile as strict C99 (and as
     C++17), and a C program linked against libpa.so drives the host-side
