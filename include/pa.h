@@ -59,7 +59,10 @@
  * memset, copy or synchronization), so a caller may record them into a HIP
  * graph and replay it. Make one call of each kind and shape on the device
  * before capturing: a call whose cache entries are missing fills them through
- * host queries of the runtime; later calls of the same shape make none.
+ * host queries of the runtime; later calls of the same shape make none. The
+ * calls that take host arrays (pa_append_block_tables_host,
+ * pa_write_cache_append_host) carry their values in the launch arguments,
+ * so a captured call replays the values it was captured with.
  */
 #ifndef PA_H
 #define PA_H
