@@ -1515,7 +1515,7 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
     // every run spans at least 8 cost units, so that each owns a tile
     const long long wmax = static_cast<long long>(gridDim.x) * kWaves;
     run.weff = static_cast<int>(min(wmax, max(1ll, run.total / 8)));
-    run.w = blockIdx.x * kWaves + wave;
+    run.w = xcd_run_id<kWaves>(run.weff, wave);  // (a bijection onto 0 .. gridDim.x * kWaves - 1)
     if (run.w >= run.weff) {
         stream_list_end(p, run.w, true, lane);
         return;

@@ -111,4 +111,24 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Which of a grid's W = gridDim.x * WPG contiguous runs of a stream wave
+// `wave` of this workgroup takes, when only the first `active` runs hold
+// work. Workgroup ids go to MI355X's eight XCDs in turn; each XCD takes one
+// contiguous stretch of the active runs (its eighth), so that neighbouring
+// work -- the KV heads of one sequence, sequences that share blocks -- is
+// read through that XCD's L2. The waves an XCD has beyond its stretch take
+// the ids from `active` on, so the grid's ids are still 0 .. W - 1, each
+// once. A grid that is not a multiple of eight keeps the plain order.
+template <int WPG>
+__device__ __forceinline__ int xcd_run_id(int active, int wave) {
+    constexpr int kXcds = 8;
+    const int b = static_cast<int>(blockIdx.x);
+    if (gridDim.x % kXcds != 0) return b * WPG + wave;
+    const int per = static_cast<int>(gridDim.x) / kXcds * WPG;  // waves per XCD
+    const int x = b % kXcds;                                     // this XCD
+    const int l = b / kXcds * WPG + wave;                        // wave index on it
+    const int r0 = x * active / kXcds, r1 = (x + 1) * active / kXcds;
+    return l < r1 - r0 ? r0 + l : active + x * per - r0 + (l - (r1 - r0));
+}
+
 }  // namespace pa

@@ -11,7 +11,8 @@
 namespace pa {
 namespace {
 
-// One wave per contiguous run of the tile list; U tile pairs loading at once,
+// One wave per contiguous run of the tile list, the runs dealt to the XCDs as
+// the decode's stream split deals its runs; U tile pairs loading at once,
 // each CH KB of K and CH KB of V as 16-byte nontemporal lane loads (one 1 KB
 // row of the wave per load instruction), folded into a checksum after all U
 // have arrived. Past the run's end a group repeats the run's last tile.
@@ -21,7 +22,7 @@ __global__ __launch_bounds__(256) void pa_probe_tiles_kernel(const char* __restr
                                                              int num_cache_tiles, u32x4* __restrict__ sink) {
     const int lane = threadIdx.x & 63;
     const int W = gridDim.x * 4;
-    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * 4 + (threadIdx.x >> 6));
+    const int w = __builtin_amdgcn_readfirstlane(xcd_run_id<4>(W, static_cast<int>(threadIdx.x >> 6)));
     const int lo = static_cast<int>(static_cast<long long>(n) * w / W);
     const int hi = static_cast<int>(static_cast<long long>(n) * (w + 1) / W);
     u32x4 acc = {0u, 0u, 0u, 0u};
