@@ -93,7 +93,8 @@ typedef enum pa_status {
 
 /* The decode partition kernels (see pa_decode_plan). */
 typedef enum pa_decode_kernel {
-    PA_DECODE_VALU = 0,      /* vector ALU; one item per workgroup (float32, or one query head per KV head) */
+    PA_DECODE_VALU = 0,      /* vector ALU; one item per workgroup (float32, or one query head per KV head
+                                outside the stream split) */
     PA_DECODE_MFMA = 1,      /* matrix cores; one item per workgroup (partitions of more than 128 blocks) */
     PA_DECODE_MFMA_WAVE = 2,  /* matrix cores; one item per wave (partitions of at most 128 blocks,
                                  blocks of fewer than 16 tokens) */
@@ -124,9 +125,10 @@ const char* pa_last_error(void);
  * partition_size = 0, a function of the batch's shape only (host code, no
  * device query). With items = num_seqs * num_kv_heads *
  * ceil(max_context_len / size):
- *   - bfloat16 / float16 with 2 or more query heads per KV head (one wave
- *     reduces an item): min(2048, 128 * block_size), halved while
- *     items < 2048 (two per wave of MI355X's 256 compute units);
+ *   - bfloat16 / float16 with 2 or more query heads per KV head, or with
+ *     blocks of 16 or more tokens (one wave reduces an item, or the stream
+ *     split): min(2048, 128 * block_size), halved while items < 2048 (two
+ *     per wave of MI355X's 256 compute units);
  *   - otherwise (a workgroup reduces an item): 256 * block_size, halved
  *     while items < 512;
  * in both cases not below 512 tokens. Long partitions cost the fewest item
@@ -206,9 +208,9 @@ pa_status_t pa_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int he
  * clamped to max_context_len tokens. Table entries outside [0, num_blocks)
  * are clamped into that range (wrong values, no fault). q/out must not alias.
  *
- * Work: with 16-bit elements, grouped query heads, blocks of 16 or more
- * tokens and partitions of at most 128 blocks (pa_decode_plan names the
- * kernel), the batch's 16-key tiles form one stream that a persistent grid
+ * Work: with 16-bit elements, blocks of 16 or more tokens and partitions of
+ * at most 128 blocks (pa_decode_plan names the kernel), the batch's 16-key
+ * tiles form one stream that a persistent grid
  * divides evenly among its waves; a wave merges the partitions of its
  * stretch of a (sequence, KV head) pair itself, and only pairs split between
  * waves leave records for the merge. The division depends on the batch and

@@ -17,16 +17,20 @@
 namespace {
 
 // Shape of the default split.
-// Workgroup items (float32, or one query head per KV head): at most 256
-// blocks, and at least 512 items per launch (two per compute unit of
+// Workgroup items (float32, or one query head per KV head with blocks of
+// fewer than 16 tokens): at most 256 blocks, and at least 512 items per
+// launch (two per compute unit of
 // MI355X). The default stops at 256 blocks although an item can stage 512:
 // on a skewed batch (lognormal lengths up to 8192) the largest items then
 // take most of a launch and the static deal cannot even them out (measured
 // on MI355X: 285 us against 255 us at 256 blocks for 256 sequences of 8 KV
 // heads, and 562 against 465 us for 8 sequences of 32k-131k tokens).
-// Wave items (16-bit grouped heads): one wave reduces an item alone, four
+// Wave items (16-bit grouped heads) and the stream split (16-bit, blocks
+// of 16 or more tokens, any group): one wave reduces an item alone, four
 // times slower than a workgroup, so items stay at 2048 tokens or less (and
-// within the wave's table slice), at least 2048 of them (two per wave).
+// within the wave's table slice), at least 2048 of them (two per wave); the
+// stream split needs partitions within that slice and is indifferent to
+// their size.
 // Neither goes below 512 tokens, the shortest partition worth its item
 // switch and merge.
 constexpr int kAutoMaxBlocks = 256;
@@ -149,7 +153,8 @@ pa_status_t noalloc_scratch(void** out) {
 // block_size.
 int auto_partition(int num_seqs, int num_heads, int num_kv_heads, int max_context_len, int block_size,
                    pa_dtype_t dtype) {
-    const bool wave = pa::decode_uses_mfma(dtype, num_heads / num_kv_heads);
+    const bool wave = pa::decode_uses_mfma(dtype, num_heads / num_kv_heads) ||
+                      pa::decode_stream_shape(dtype, block_size);
     int part = wave ? std::min(kWaveMaxPartition, pa::kWaveSlice * block_size) : kAutoMaxBlocks * block_size;
     const long long target = wave ? kWaveTargetItems : kTargetItems;
     while (part > kMinAutoPartition) {

@@ -1473,7 +1473,7 @@ __device__ __forceinline__ void stream_list_end(const DecodeParams& p, int w, bo
 template <int DT, int D, int G>
 __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
     static_assert(DT == PA_BF16 || DT == PA_F16, "MFMA path is for 16-bit elements");
-    static_assert(G == 2 || G == 4 || G == 8 || G == 16, "group size");
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
     constexpr int E = 2;
     constexpr int NK = D / 32;
     constexpr int NV = D / 16;
@@ -2069,6 +2069,18 @@ hipError_t launch_mfma(const DecodeParams& p, const DeviceInfo& dv, hipStream_t 
     return run_planned(kern, p, pl, dv, stream);
 }
 
+// One query head per KV head on the stream split (16-bit elements, blocks of
+// 16 or more tokens): the MFMA tiles then carry one distinct column, but the
+// kernel is bound by the K/V stream, not by its products.
+template <int DT, int D, int G>
+hipError_t launch_stream_only(const DecodeParams& p, const DeviceInfo& dv, hipStream_t stream) {
+    DecodePlan pl;
+    if (plan_decode(static_cast<pa_dtype_t>(DT), D, G, p.num_seqs, p.part >> p.log2_bs, true, dv.lds_per_cu,
+                    dv.lds_per_wg, kMfmaWgPerCu, &pl) != PA_OK || pl.kernel != PA_DECODE_MFMA_STREAM)
+        return hipErrorInvalidConfiguration;
+    return run_planned(pa_decode_stream<DT, D, G>, p, pl, dv, stream);
+}
+
 template <int DT, int D>
 hipError_t launch_d(const DecodeParams& p, const DeviceInfo& dv, hipStream_t stream) {
     if constexpr (DT == PA_F32) {
@@ -2080,7 +2092,7 @@ hipError_t launch_d(const DecodeParams& p, const DeviceInfo& dv, hipStream_t str
         }
     } else {
         switch (p.group) {
-            case 1: return launch_valu<DT, D, 1>(p, dv, stream);
+            case 1: return p.stream ? launch_stream_only<DT, D, 1>(p, dv, stream) : launch_valu<DT, D, 1>(p, dv, stream);
             case 2: return launch_mfma<DT, D, 2>(p, dv, stream);
             case 4: return launch_mfma<DT, D, 4>(p, dv, stream);
             case 8: return launch_mfma<DT, D, 8>(p, dv, stream);
@@ -2171,8 +2183,10 @@ bool decode_wave_items(pa_dtype_t dt, int group, int part_blocks) {
     return decode_uses_mfma(dt, group) && part_blocks <= kWaveSlice;
 }
 
+bool decode_stream_shape(pa_dtype_t dt, int block_size) { return dt != PA_F32 && block_size >= 16; }
+
 bool decode_stream(pa_dtype_t dt, int group, int block_size, int part, int num_seqs, int num_kv_heads, int max_ctx) {
-    if (!decode_uses_mfma(dt, group) || block_size < 16 || part / block_size > kWaveSlice) return false;
+    if (group < 1 || !decode_stream_shape(dt, block_size) || part / block_size > kWaveSlice) return false;
     // cost positions are int32 in the kernel
     const long long tiles = max_ctx > 0 ? (static_cast<long long>(max_ctx) + 15) / 16 : 1;
     const long long cost = static_cast<long long>(num_seqs) * num_kv_heads * (kStreamTileCost * tiles + kStreamPairCost);

@@ -71,7 +71,8 @@ def _expected(dt, d, g, s, part_blocks, max_wg, block_size=16, kv_heads=2, max_c
     """Kernel, LDS bytes, ring slots and residency the plan must give, or
     None when nothing fits."""
     mfma = dt != F32 and g >= 2
-    stream = (mfma and block_size >= 16 and part_blocks <= WAVE_SLICE and
+    # the stream split: 16-bit elements, any group, blocks of 16 or more tokens
+    stream = (dt != F32 and block_size >= 16 and part_blocks <= WAVE_SLICE and
               s * kv_heads * (4 * max(1, -(-max_ctx // 16)) + 3) < 2 ** 31 - 1)
     if stream:   # the stream split's records differ: no other kernel stands in
         cands = [STREAM]
@@ -169,9 +170,17 @@ def test_plan_follows_the_default_partition_and_the_device_lds():
     # partitions over 128 blocks run one item per workgroup
     assert lib.pa_decode_plan(64, 32, 8, 128, 8192, 16, 4096, BF16, LDS, LDS, 1, ctypes.byref(plan)) == 0
     assert plan.kernel == MFMA
-    # one query head per KV head, and float32, run the VALU kernel
+    # one query head per KV head: the stream split at 2048-token partitions
+    # with blocks of 16 or more tokens, the VALU kernel with smaller blocks,
+    # with partitions over 128 blocks, and for float32
     assert lib.pa_decode_plan(64, 32, 32, 128, 4096, 16, 0, BF16, LDS, LDS, 2, ctypes.byref(plan)) == 0
+    assert plan.kernel == STREAM and plan.partition_size == 2048 and plan.workgroups_per_cu == 1
+    assert lib.pa_decode_plan(64, 32, 32, 128, 4096, 8, 0, BF16, LDS, LDS, 2, ctypes.byref(plan)) == 0
+    assert plan.kernel == VALU and plan.workgroups_per_cu == 2 and plan.partition_size == 2048
+    assert lib.pa_decode_plan(64, 32, 32, 128, 4096, 16, 4096, BF16, LDS, LDS, 2, ctypes.byref(plan)) == 0
     assert plan.kernel == VALU and plan.workgroups_per_cu == 2
+    assert lib.pa_decode_plan(64, 32, 32, 128, 4096, 16, 0, F32, LDS, LDS, 2, ctypes.byref(plan)) == 0
+    assert plan.kernel == VALU and plan.partition_size == 4096
 
 
 def test_plan_rejects_bad_arguments():

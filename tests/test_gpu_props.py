@@ -146,7 +146,9 @@ def test_block_sizes(bs, g):
 @pytest.mark.parametrize("dt,d", [(torch.float32, 128), (torch.float32, 256), (torch.bfloat16, 256),
                                   (torch.bfloat16, 64), (torch.float16, 64)])
 def test_block_sizes_wide_rows(bs, dt, d):
-    """Row geometries of the VALU kernel other than 256-byte rows. float32
+    """Row geometries other than 256-byte rows with one query head per KV
+    head: the VALU kernel for float32 and for 16-bit elements in blocks of 8,
+    the stream split for 16-bit elements in blocks of 16 or more. float32
     head_dim 256 takes blocks of at least 16 tokens: a smaller block is
     rejected with PA_ERR_UNSUPPORTED before anything is launched."""
     c = make_case([5, 100, 700], 4, 4, d, bs, dt, seed=bs + d)
