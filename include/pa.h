@@ -96,10 +96,11 @@ typedef enum pa_decode_kernel {
     PA_DECODE_VALU = 0,      /* vector ALU; one item per workgroup (float32, or one query head per KV head
                                 outside the stream split) */
     PA_DECODE_MFMA = 1,      /* matrix cores; one item per workgroup (partitions of more than 128 blocks) */
-    PA_DECODE_MFMA_WAVE = 2,  /* matrix cores; one item per wave (partitions of at most 128 blocks,
-                                 blocks of fewer than 16 tokens) */
-    PA_DECODE_MFMA_STREAM = 3 /* matrix cores; the batch's tiles split evenly over the waves (partitions of
-                                 at most 128 blocks, blocks of 16 tokens or more) */
+    PA_DECODE_MFMA_WAVE = 2,  /* matrix cores; one item per wave (partitions of at most 128 blocks, 2 or
+                                 more query heads per KV head, when the stream split's cost positions
+                                 could pass 2^31: see pa_decode) */
+    PA_DECODE_MFMA_STREAM = 3 /* matrix cores; the batch's tiles split evenly over the waves (16-bit
+                                 elements, partitions of at most 128 blocks) */
 } pa_decode_kernel_t;
 
 /* How pa_decode launches its partition kernel for one shape. */
@@ -125,11 +126,10 @@ const char* pa_last_error(void);
  * partition_size = 0, a function of the batch's shape only (host code, no
  * device query). With items = num_seqs * num_kv_heads *
  * ceil(max_context_len / size):
- *   - bfloat16 / float16 with 2 or more query heads per KV head, or with
- *     blocks of 16 or more tokens (one wave reduces an item, or the stream
- *     split): min(2048, 128 * block_size), halved while items < 2048 (two
- *     per wave of MI355X's 256 compute units);
- *   - otherwise (a workgroup reduces an item): 256 * block_size, halved
+ *   - bfloat16 / float16 (the stream split, or one wave per item):
+ *     min(2048, 128 * block_size), halved while items < 2048 (two per wave
+ *     of MI355X's 256 compute units);
+ *   - float32 (a workgroup reduces an item): 256 * block_size, halved
  *     while items < 512;
  * in both cases not below 512 tokens. Long partitions cost the fewest item
  * switches and merges; the item count keeps every compute unit fed.
@@ -208,17 +208,19 @@ pa_status_t pa_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int he
  * clamped to max_context_len tokens. Table entries outside [0, num_blocks)
  * are clamped into that range (wrong values, no fault). q/out must not alias.
  *
- * Work: with 16-bit elements, blocks of 16 or more tokens and partitions of
- * at most 128 blocks (pa_decode_plan names the kernel), the batch's 16-key
- * tiles form one stream that a persistent grid
- * divides evenly among its waves; a wave merges the partitions of its
- * stretch of a (sequence, KV head) pair itself, and only pairs split between
- * waves leave records for the merge. The division depends on the batch and
- * on the device's compute-unit count: results repeat bit for bit on one
- * device and differ in rounding only between devices. Otherwise the work is
- * split into items of (sequence, KV head, partition) that a persistent grid
- * processes largest first; an item's result does not depend on which
- * workgroup (or wave) ran it.
+ * Work: with 16-bit elements and partitions of at most 128 blocks
+ * (pa_decode_plan names the kernel), the batch's 16-key tiles form one
+ * stream that a persistent grid divides evenly among its waves; a wave
+ * merges the partitions of its stretch of a (sequence, KV head) pair
+ * itself, and only pairs split between waves leave records for the merge.
+ * The division depends on the batch and on the device's compute-unit count:
+ * results repeat bit for bit on one device and differ in rounding only
+ * between devices. The stream's cost positions are 32-bit: a batch with
+ * num_seqs * num_kv_heads * (4 * ceil(max_context_len / 16) + 3) >= 2^31 - 1
+ * runs the item kernels instead. Otherwise the work is split into items of
+ * (sequence, KV head, partition) that a persistent grid processes largest
+ * first; an item's result does not depend on which workgroup (or wave) ran
+ * it.
  */
 pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens, float scale,

@@ -17,16 +17,15 @@
 namespace {
 
 // Shape of the default split.
-// Workgroup items (float32, or one query head per KV head with blocks of
-// fewer than 16 tokens): at most 256 blocks, and at least 512 items per
+// Workgroup items (float32): at most 256 blocks, and at least 512 items per
 // launch (two per compute unit of
 // MI355X). The default stops at 256 blocks although an item can stage 512:
 // on a skewed batch (lognormal lengths up to 8192) the largest items then
 // take most of a launch and the static deal cannot even them out (measured
 // on MI355X: 285 us against 255 us at 256 blocks for 256 sequences of 8 KV
 // heads, and 562 against 465 us for 8 sequences of 32k-131k tokens).
-// Wave items (16-bit grouped heads) and the stream split (16-bit, blocks
-// of 16 or more tokens, any group): one wave reduces an item alone, four
+// 16-bit elements (the stream split, or one item per wave where its cost
+// positions would not fit 31 bits): one wave reduces an item alone, four
 // times slower than a workgroup, so items stay at 2048 tokens or less (and
 // within the wave's table slice), at least 2048 of them (two per wave); the
 // stream split needs partitions within that slice and is indifferent to

@@ -1470,7 +1470,7 @@ __device__ __forceinline__ void stream_list_end(const DecodeParams& p, int w, bo
         *reinterpret_cast<int4*>(p.ws_meta + 4 * static_cast<size_t>(x)) = make_int4(0, 0, 0, 0);
 }
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, bool BIGB>
 __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
     static_assert(DT == PA_BF16 || DT == PA_F16, "MFMA path is for 16-bit elements");
     static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
@@ -1534,25 +1534,48 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
     };
     auto clamp_pid = [&](int pid) { return pid < 0 ? 0 : (pid >= p.num_blocks ? p.num_blocks - 1 : pid); };
 
-    // K/V loads of one 16-token tile: the tile lies in one block (blocks of
-    // 16 tokens or more) and one 16-token V tile, so the bases are scalar
-    auto load_with = [&](const Piece& x, int tile, int pk, Buf& b) {
+    // K/V loads of one 16-token tile. Blocks of 16 tokens or more: the tile
+    // lies in one block and one 16-token V tile, so the bases are scalar.
+    // Smaller blocks: a lane's K row (key tt0 + r16) and its four V keys
+    // (tt0 + 4j ..) each lie in one block, whose ids pk and pv it holds.
+    auto load_with = [&](const Piece& x, int tile, int pk, int pv, Buf& b) {
         const int tt0 = x.t0 + 16 * tile;
         const int krow = min(tt0 + r16, x.t1 - 1);
         const int vtok = min(tt0 + 4 * j, last4_of(x));
-        const int pid = __builtin_amdgcn_readfirstlane(pk);
-        const size_t tile_el = (static_cast<size_t>(pid) * hkv + x.kv) * blk_el;
-        const char* kt = kbase + tile_el * E;
-        const char* vtp = vbase + (tile_el + static_cast<size_t>((tt0 & (bs - 1)) >> 4) * D * 16) * E;
-        const uint32_t ko = static_cast<uint32_t>(((krow & (bs - 1)) * D + 8 * j) * E);
-        const uint32_t vo = static_cast<uint32_t>(((vtok & 15) + 16 * r16) * E);
+        if constexpr (BIGB) {
+            const int pid = __builtin_amdgcn_readfirstlane(pk);
+            const size_t tile_el = (static_cast<size_t>(pid) * hkv + x.kv) * blk_el;
+            const char* kt = kbase + tile_el * E;
+            const char* vtp = vbase + (tile_el + static_cast<size_t>((tt0 & (bs - 1)) >> 4) * D * 16) * E;
+            const uint32_t ko = static_cast<uint32_t>(((krow & (bs - 1)) * D + 8 * j) * E);
+            const uint32_t vo = static_cast<uint32_t>(((vtok & 15) + 16 * r16) * E);
 #pragma unroll
-        for (int c = 0; c < NK; ++c) b.k[c] = nt_load<u32x4>(kt, ko + 64 * c);
+            for (int c = 0; c < NK; ++c) b.k[c] = nt_load<u32x4>(kt, ko + 64 * c);
 #pragma unroll
-        for (int v = 0; v < NV; ++v) b.v[v] = nt_load<u32x2>(vtp, vo + 512 * v);
+            for (int v = 0; v < NV; ++v) b.v[v] = nt_load<u32x2>(vtp, vo + 512 * v);
+        } else {
+            const int vt = 1 << p.log2_vt;
+            const size_t kel = (static_cast<size_t>(pk) * hkv + x.kv) * blk_el +
+                               static_cast<size_t>(krow & (bs - 1)) * D + 8 * j;
+#pragma unroll
+            for (int c = 0; c < NK; ++c) b.k[c] = nt_load<u32x4>(kbase, (kel + 32 * c) * E);
+            const int voff = vtok & (bs - 1);
+            const size_t vel = (static_cast<size_t>(pv) * hkv + x.kv) * blk_el +
+                               static_cast<size_t>(voff >> p.log2_vt) * D * vt + (voff & (vt - 1)) +
+                               static_cast<size_t>(r16) * vt;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                b.v[v] = nt_load<u32x2>(vbase, (vel + static_cast<size_t>(16 * v) * vt) * E);
+        }
     };
-    auto tile_block = [&](const Piece& x, const int* tb, int tile) {
-        return tb[(min(x.t0 + 16 * tile, x.t1 - 1) >> p.log2_bs) - x.b0];
+    auto tile_blocks = [&](const Piece& x, const int* tb, int tile, int& pk, int& pv) {
+        const int tt0 = x.t0 + 16 * tile;
+        if constexpr (BIGB) {
+            pk = pv = tb[(min(tt0, x.t1 - 1) >> p.log2_bs) - x.b0];
+        } else {
+            pk = tb[(min(tt0 + r16, x.t1 - 1) >> p.log2_bs) - x.b0];
+            pv = tb[(min(tt0 + 4 * j, last4_of(x)) >> p.log2_bs) - x.b0];
+        }
     };
     auto stage_slice = [&](const Piece& x, int* tb) {
         const int* trow = p.block_tables + static_cast<size_t>(x.s) * p.max_blocks + x.b0;
@@ -1579,9 +1602,9 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
     for (int w = lane; w < QW; w += 64) qs[w] = qwords[q_word0(cur) + w];
     Buf A, B;
     {
-        int pk = 0;
-        if (ntiles_of(cur) > 0) pk = tile_block(cur, tbl, 0);
-        load_with(cur, 0, pk, A);
+        int pk = 0, pv = 0;
+        if (ntiles_of(cur) > 0) tile_blocks(cur, tbl, 0, pk, pv);
+        load_with(cur, 0, pk, pv, A);
     }
 
     // the segment's running result: the merged partitions so far (max in
@@ -1595,7 +1618,14 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
         // raw loads of the next piece's metadata, consumed at the end
         const int* trow = p.block_tables + static_cast<size_t>(nxt.s) * p.max_blocks + nxt.b0;
         const int* safe = p.context_lens;
-        const int pk_raw = *(next_tile ? trow : safe);
+        int pk_raw, pv_raw;
+        if constexpr (BIGB) {
+            pk_raw = *(next_tile ? trow : safe);
+            pv_raw = pk_raw;
+        } else {
+            pk_raw = *(next_tile ? trow + ((min(nxt.t0 + r16, nxt.t1 - 1) >> p.log2_bs) - nxt.b0) : safe);
+            pv_raw = *(next_tile ? trow + ((min(nxt.t0 + 4 * j, last4_of(nxt)) >> p.log2_bs) - nxt.b0) : safe);
+        }
         int tbl_raw[TPL];
 #pragma unroll
         for (int i = 0; i < TPL; ++i)
@@ -1664,12 +1694,16 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
                 acc[v] = mfma_pv<DT>(a, pb, acc[v]);
             }
         };
-        auto load_tile = [&](int tile, Buf& b) { load_with(cur, tile, tile_block(cur, tbl, tile), b); };
+        auto load_tile = [&](int tile, Buf& b) {
+            int pk, pv;
+            tile_blocks(cur, tbl, tile, pk, pv);
+            load_with(cur, tile, pk, pv, b);
+        };
         auto load_next = [&](Buf& b) {
-            int pk = pk_raw;
-            asm volatile("" : "+v"(pk));
-            if (next_tile) load_with(nxt, 0, clamp_pid(pk), b);
-            else load_with(cur, 0, 0, b);
+            int pk = pk_raw, pv = pv_raw;
+            asm volatile("" : "+v"(pk), "+v"(pv));
+            if (next_tile) load_with(nxt, 0, clamp_pid(pk), clamp_pid(pv), b);
+            else load_with(cur, 0, 0, 0, b);
         };
         // the piece's tiles, two deep
         int t = 0;
@@ -1695,7 +1729,7 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
         load_next(A);
-        asm volatile("" ::"v"(pk_raw));
+        asm volatile("" ::"v"(pk_raw), "v"(pv_raw));
 
         // the partition (piece) joins the segment by the log-sum-exp rule:
         // both sides are rescaled to the larger max (m_run is the same on
@@ -2061,7 +2095,7 @@ hipError_t launch_mfma(const DecodeParams& p, const DeviceInfo& dv, hipStream_t 
     const bool big = (1 << p.log2_bs) >= 16;
     void (*kern)(DecodeParams);
     if (pl.kernel == PA_DECODE_MFMA_STREAM)
-        kern = pa_decode_stream<DT, D, G>;
+        kern = big ? pa_decode_stream<DT, D, G, true> : pa_decode_stream<DT, D, G, false>;
     else if (pl.kernel == PA_DECODE_MFMA_WAVE)
         kern = big ? pa_decode_mfma_wave<DT, D, G, true> : pa_decode_mfma_wave<DT, D, G, false>;
     else
@@ -2069,16 +2103,18 @@ hipError_t launch_mfma(const DecodeParams& p, const DeviceInfo& dv, hipStream_t 
     return run_planned(kern, p, pl, dv, stream);
 }
 
-// One query head per KV head on the stream split (16-bit elements, blocks of
-// 16 or more tokens): the MFMA tiles then carry one distinct column, but the
-// kernel is bound by the K/V stream, not by its products.
+// One query head per KV head on the stream split (16-bit elements): the MFMA
+// tiles then carry one distinct column, but the kernel is bound by the K/V
+// stream, not by its products.
 template <int DT, int D, int G>
 hipError_t launch_stream_only(const DecodeParams& p, const DeviceInfo& dv, hipStream_t stream) {
     DecodePlan pl;
     if (plan_decode(static_cast<pa_dtype_t>(DT), D, G, p.num_seqs, p.part >> p.log2_bs, true, dv.lds_per_cu,
                     dv.lds_per_wg, kMfmaWgPerCu, &pl) != PA_OK || pl.kernel != PA_DECODE_MFMA_STREAM)
         return hipErrorInvalidConfiguration;
-    return run_planned(pa_decode_stream<DT, D, G>, p, pl, dv, stream);
+    const bool big = (1 << p.log2_bs) >= 16;
+    return run_planned(big ? pa_decode_stream<DT, D, G, true> : pa_decode_stream<DT, D, G, false>, p, pl, dv,
+                       stream);
 }
 
 template <int DT, int D>
@@ -2183,7 +2219,7 @@ bool decode_wave_items(pa_dtype_t dt, int group, int part_blocks) {
     return decode_uses_mfma(dt, group) && part_blocks <= kWaveSlice;
 }
 
-bool decode_stream_shape(pa_dtype_t dt, int block_size) { return dt != PA_F32 && block_size >= 16; }
+bool decode_stream_shape(pa_dtype_t dt, int block_size) { return dt != PA_F32 && block_size >= 4; }
 
 bool decode_stream(pa_dtype_t dt, int group, int block_size, int part, int num_seqs, int num_kv_heads, int max_ctx) {
     if (group < 1 || !decode_stream_shape(dt, block_size) || part / block_size > kWaveSlice) return false;

@@ -144,8 +144,8 @@ hipError_t launch_decode_merge(const DecodeParams& p, pa_dtype_t dt, int head_di
 bool decode_supported(pa_dtype_t dt, int head_dim, int group);
 // Whether a shape runs the stream kernel, which splits the batch's tiles
 // evenly over the grid's waves (its workspace layout differs): 16-bit
-// elements, any group, blocks of 16 or more tokens (decode_stream_shape),
-// partitions of at most a wave's table slice and cost positions in 31 bits.
+// elements, any group and block size (decode_stream_shape), partitions of at
+// most a wave's table slice and cost positions in 31 bits.
 bool decode_stream_shape(pa_dtype_t dt, int block_size);
 bool decode_stream(pa_dtype_t dt, int group, int block_size, int part, int num_seqs, int num_kv_heads, int max_ctx);
 bool decode_uses_mfma(pa_dtype_t dt, int group);

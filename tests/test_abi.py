@@ -57,14 +57,16 @@ def test_status_strings_and_workspace_size():
     assert dp(8, 8, 8, 131072, 32, F32) == 8192       # 64 pairs x 16 partitions = 1024 items
     assert dp(1, 8, 8, 131072, 16, F32) == 2048       # 8 pairs: halve until 8 x 64 = 512 items
     assert dp(4, 4, 4, 256, 16, F32) == 512           # tiny batch: floor of 512 tokens
-    assert dp(64, 8, 8, 1000, 4, BF16) == 1024        # 256 blocks of 4; 512 pairs suffice
-    assert dp(32, 8, 8, 1000, 4, F16) == 512          # 256 pairs: halved once
-    assert dp(2, 1, 1, 4096, 256, BF16) == 512
-    # wave items and the stream split (16-bit with grouped heads, or with
-    # blocks of 16 or more tokens): min(2048, 128 blocks), halved while < 2048 items
+    assert dp(64, 8, 8, 1000, 4, F32) == 1024         # 256 blocks of 4; 512 pairs suffice
+    assert dp(32, 8, 8, 1000, 4, F32) == 512          # 256 pairs: halved once
+    assert dp(2, 1, 1, 4096, 256, F32) == 512
+    # 16-bit elements (the stream split, or wave items): min(2048, 128
+    # blocks), halved while < 2048 items
     assert dp(256, 32, 8, 8192, 16, BF16) == 2048     # 2048 pairs x 4 partitions
     assert dp(64, 32, 32, 4096, 16, BF16) == 2048     # one query head per KV head: 2048 pairs x 2
     assert dp(8, 8, 8, 131072, 32, BF16) == 2048      # 64 pairs x 64 partitions
+    assert dp(64, 8, 8, 1000, 4, BF16) == 512         # 128 blocks of 4, 512 pairs: the floor
+    assert dp(2, 1, 1, 4096, 256, BF16) == 512        # 2 pairs: halve to the floor
     assert dp(8, 64, 8, 131072, 32, BF16) == 2048     # 64 pairs x 64 partitions
     assert dp(1, 64, 8, 131072, 32, F16) == 512       # 8 pairs: halve to the floor
     assert dp(256, 32, 8, 1000, 8, BF16) == 1024      # 128 blocks of 8
@@ -76,7 +78,7 @@ def test_status_strings_and_workspace_size():
     # single partition: no workspace needed (item kernels)
     assert lib.pa_decode_workspace_size(4, 8, 8, 128, 512, 16, 0, F32) == 0
     assert lib.pa_decode_workspace_size(4, 8, 8, 128, 1024, 16, 1024, F32) == 0
-    assert lib.pa_decode_workspace_size(4, 8, 8, 128, 512, 8, 0, BF16) == 0
+    assert lib.pa_decode_workspace_size(4, 8, 8, 128, 512, 8, 0, F32) == 0
     # records of (m, l, o[D]) floats, each region 256-byte aligned
     recs = 4 * 8 * 3
     a = lambda x: (x + 255) // 256 * 256
@@ -93,12 +95,16 @@ def test_status_strings_and_workspace_size():
     assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 512, BF16) == stream
     assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 0, BF16) == stream
     assert lib.pa_decode_workspace_size(4, 8, 2, 128, 500, 16, 512, BF16) == stream
-    # one query head per KV head runs it too (16-bit, blocks of 16 or more)
+    # one query head per KV head runs it too, and so do blocks of 8
     x1 = 2 * 1024 * 1
     assert lib.pa_decode_workspace_size(4, 8, 8, 128, 512, 16, 0, BF16) == \
         a(1024 * 16) + 2 * a(x1 * 4) + a(x1 * 128 * 4)
-    # blocks of 8 keep the one-item-per-wave kernel and its records
-    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 8, 512, BF16) == expect
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 8, 512, BF16) == stream
+    # a batch whose stream cost positions could pass 2^31 (1024 x 8 pairs of
+    # up to 2^20 tokens) keeps the one-item-per-wave kernel and its records
+    big = 1024 * 32 * 64
+    assert lib.pa_decode_workspace_size(1024, 32, 8, 128, 2 ** 20, 128, 16384, BF16) == \
+        a(big * 4) * 2 + a(big * 128 * 4)
     assert lib.pa_decode_workspace_size(-1, 8, 8, 128, 1100, 16, 0, BF16) == 0
     assert lib.pa_decode_workspace_size(4, 8, 8, 128, 1100, 16, 0, 9) == 0
 

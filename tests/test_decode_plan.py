@@ -71,8 +71,8 @@ def _expected(dt, d, g, s, part_blocks, max_wg, block_size=16, kv_heads=2, max_c
     """Kernel, LDS bytes, ring slots and residency the plan must give, or
     None when nothing fits."""
     mfma = dt != F32 and g >= 2
-    # the stream split: 16-bit elements, any group, blocks of 16 or more tokens
-    stream = (dt != F32 and block_size >= 16 and part_blocks <= WAVE_SLICE and
+    # the stream split: 16-bit elements, any group and block size
+    stream = (dt != F32 and part_blocks <= WAVE_SLICE and
               s * kv_heads * (4 * max(1, -(-max_ctx // 16)) + 3) < 2 ** 31 - 1)
     if stream:   # the stream split's records differ: no other kernel stands in
         cands = [STREAM]
@@ -142,7 +142,7 @@ def test_every_accepted_plan_fits_and_the_rest_is_refused(dt, d, g):
 def test_block_size_and_cost_bound_choose_the_kernel():
     lib, L = _lib()
     plan = L.DecodePlan()
-    for bs, part, kernel in [(16, 2048, STREAM), (32, 4096, STREAM), (8, 1024, WAVE), (4, 512, WAVE),
+    for bs, part, kernel in [(16, 2048, STREAM), (32, 4096, STREAM), (8, 1024, STREAM), (4, 512, STREAM),
                              (16, 4096, MFMA)]:  # 256 blocks: more than a wave's table slice
         assert lib.pa_decode_plan(64, 32, 8, 128, 8192, bs, part, BF16, LDS, LDS, 1, ctypes.byref(plan)) == 0
         assert plan.kernel == kernel, (bs, part)
@@ -157,9 +157,9 @@ def test_plan_follows_the_default_partition_and_the_device_lds():
     # the GQA batch-256 shape: 2048-token partitions, the stream split
     assert lib.pa_decode_plan(256, 32, 8, 128, 8192, 16, 0, BF16, LDS, LDS, 1, ctypes.byref(plan)) == 0
     assert plan.kernel == STREAM and plan.partition_size == 2048
-    # blocks of 8 tokens: one item per wave
+    # blocks of 8 tokens: the stream split at 1024-token partitions
     assert lib.pa_decode_plan(256, 32, 8, 128, 8192, 8, 0, BF16, LDS, LDS, 1, ctypes.byref(plan)) == 0
-    assert plan.kernel == WAVE
+    assert plan.kernel == STREAM and plan.partition_size == 1024
     # a smaller LDS holds fewer ring slots, and a too small one refuses
     assert lib.pa_decode_plan(256, 32, 8, 128, 8192, 16, 0, BF16, 65536, 65536, 1, ctypes.byref(plan)) == 0
     small = plan.ring_slots
@@ -170,13 +170,12 @@ def test_plan_follows_the_default_partition_and_the_device_lds():
     # partitions over 128 blocks run one item per workgroup
     assert lib.pa_decode_plan(64, 32, 8, 128, 8192, 16, 4096, BF16, LDS, LDS, 1, ctypes.byref(plan)) == 0
     assert plan.kernel == MFMA
-    # one query head per KV head: the stream split at 2048-token partitions
-    # with blocks of 16 or more tokens, the VALU kernel with smaller blocks,
-    # with partitions over 128 blocks, and for float32
+    # one query head per KV head: the stream split (here at 2048 and 1024
+    # tokens), the VALU kernel with partitions over 128 blocks and for float32
     assert lib.pa_decode_plan(64, 32, 32, 128, 4096, 16, 0, BF16, LDS, LDS, 2, ctypes.byref(plan)) == 0
     assert plan.kernel == STREAM and plan.partition_size == 2048 and plan.workgroups_per_cu == 1
     assert lib.pa_decode_plan(64, 32, 32, 128, 4096, 8, 0, BF16, LDS, LDS, 2, ctypes.byref(plan)) == 0
-    assert plan.kernel == VALU and plan.workgroups_per_cu == 2 and plan.partition_size == 2048
+    assert plan.kernel == STREAM and plan.partition_size == 1024
     assert lib.pa_decode_plan(64, 32, 32, 128, 4096, 16, 4096, BF16, LDS, LDS, 2, ctypes.byref(plan)) == 0
     assert plan.kernel == VALU and plan.workgroups_per_cu == 2
     assert lib.pa_decode_plan(64, 32, 32, 128, 4096, 16, 0, F32, LDS, LDS, 2, ctypes.byref(plan)) == 0

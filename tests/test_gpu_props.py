@@ -121,15 +121,35 @@ def test_full_table_slice_partitions(dt, g):
 
 @pytest.mark.parametrize("bs", [4, 8, 16, 32])
 @pytest.mark.parametrize("dt,g", [(torch.bfloat16, 4), (torch.float16, 8)])
-def test_wave_and_workgroup_mfma_kernels(dt, g, bs):
-    """16-bit grouped heads run one item per wave when a partition spans at
+def test_stream_and_workgroup_mfma_kernels(dt, g, bs):
+    """16-bit grouped heads run the stream split when a partition spans at
     most 128 blocks and one item per workgroup above that: both, at every
     small block size, and the library's default split."""
     lens = [1, 5, 16, 31, 700, 2049, 5000]
     c = make_case(lens, 2 * g, 2, 128, bs, dt, seed=40 + bs + g)
     ref = run_oracle(c, 0.08)
-    for part, kind in ((128 * bs, "wave"), (256 * bs, "workgroup"), (0, "default")):
+    for part, kind in ((128 * bs, "stream"), (256 * bs, "workgroup"), (0, "default")):
         compare_attention(run_gpu(c, 0.08, part=part), ref, f"{dt} g{g} bs{bs} part {part} ({kind})")
+
+
+def test_wave_items_past_the_stream_cost_bound():
+    """The stream split keeps its cost positions in 32 bits, so a batch that
+    could pass 2^31 runs one item per wave instead. The bound is taken on
+    max_context_len, so 1024 short sequences of 8 KV heads declared up to
+    2^20 tokens reach it (blocks of 128 keep the table at 8192 entries per
+    sequence; table entries past each context are never read)."""
+    pa = _pa()
+    n, hkv, g, bs, mc, part = 1024, 8, 4, 128, 2 ** 20, 16384
+    assert n * hkv * (4 * (mc // 16) + 3) >= 2 ** 31 - 1
+    plan = pa.decode_plan(n, hkv * g, hkv, 128, mc, bs, part, torch.bfloat16)
+    assert plan["kernel"] == "mfma_wave", plan
+    lens = np.random.default_rng(77).integers(0, bs + 1, size=n)
+    lens[:3] = [0, 1, bs]
+    c = make_case(lens, hkv * g, hkv, 128, bs, torch.bfloat16, seed=77)
+    wide = np.zeros((n, mc // bs), np.int32)
+    wide[:, :c["tables"].shape[1]] = c["tables"]
+    out = run_gpu(c, 0.09, part=part, max_ctx=mc, tables=wide)
+    compare_attention(out, run_oracle(c, 0.09), "wave items past the stream cost bound")
 
 
 @pytest.mark.parametrize("bs", [4, 8, 16, 32, 64, 128, 256])
@@ -147,10 +167,9 @@ def test_block_sizes(bs, g):
                                   (torch.bfloat16, 64), (torch.float16, 64)])
 def test_block_sizes_wide_rows(bs, dt, d):
     """Row geometries other than 256-byte rows with one query head per KV
-    head: the VALU kernel for float32 and for 16-bit elements in blocks of 8,
-    the stream split for 16-bit elements in blocks of 16 or more. float32
-    head_dim 256 takes blocks of at least 16 tokens: a smaller block is
-    rejected with PA_ERR_UNSUPPORTED before anything is launched."""
+    head: the VALU kernel for float32, the stream split for 16-bit elements.
+    float32 head_dim 256 takes blocks of at least 16 tokens: a smaller block
+    is rejected with PA_ERR_UNSUPPORTED before anything is launched."""
     c = make_case([5, 100, 700], 4, 4, d, bs, dt, seed=bs + d)
     if dt == torch.float32 and d == 256 and bs < 16:
         pa = _pa()

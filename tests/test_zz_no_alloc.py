@@ -47,7 +47,7 @@ def test_noalloc_matches_decode_with_workspace_on_two_calls():
     pa.write_cache(k_new, v_new, kc, vc, torch.from_numpy(w.writes[0].slots).to(DEV))
     tables = torch.from_numpy(w.block_tables).to(DEV)
     lens = torch.from_numpy(w.context_lens).to(DEV)
-    # call 1: the whole batch (records of 256 x 32 heads x 4 partitions)
+    # call 1: the whole batch (the stream split: a tail and a head record per wave)
     # call 2: its first 48 sequences, shorter contexts, a shorter partition
     lens2_h = np.minimum(w.context_lens[:48], 3000).astype(np.int32)
     cases = [(q, tables, lens, w.max_context_len, 0),
@@ -72,11 +72,11 @@ def test_noalloc_matches_decode_with_workspace_on_two_calls():
 
 
 def test_noalloc_refuses_records_beyond_its_scratch():
-    """64 sequences x 32 heads x 256 partitions of 512 tokens in blocks of 8
-    (the one-item-per-wave kernel, which keeps a record per partition) need
-    272 MB of records: refused on the host. (Every buffer is real and every
-    context empty, so nothing could be read out of bounds even if a launch
-    happened.)"""
+    """64 sequences x 32 heads x 64 partitions of 2048 tokens in blocks of 8
+    (256 blocks per partition: the one-item-per-workgroup kernel, which keeps
+    a record per partition) need 68 MB of records: refused on the host.
+    (Every buffer is real and every context empty, so nothing could be read
+    out of bounds even if a launch happened.)"""
     lib, L = _lib()
     import paged_kv_cache_165_amd as pa
     s, hq, hkv, d, bs, max_ctx = 64, 32, 8, 128, 8, 131072
@@ -85,9 +85,10 @@ def test_noalloc_refuses_records_beyond_its_scratch():
     out = torch.empty_like(q)
     tables = torch.zeros(s, max_ctx // bs, dtype=torch.int32, device=DEV)
     lens = torch.zeros(s, dtype=torch.int32, device=DEV)
-    assert pa.workspace_size(s, hq, hkv, d, max_ctx, bs, 512, torch.bfloat16) > L.NOALLOC_SCRATCH_BYTES
+    assert pa.decode_plan(s, hq, hkv, d, max_ctx, bs, 2048, torch.bfloat16)["kernel"] == "mfma"
+    assert pa.workspace_size(s, hq, hkv, d, max_ctx, bs, 2048, torch.bfloat16) > L.NOALLOC_SCRATCH_BYTES
     st = lib.pa_decode_noalloc(out.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), tables.data_ptr(),
                                lens.data_ptr(), ctypes.c_float(0.1), bs, s, hq, hkv, d, 4, tables.shape[1], max_ctx,
-                               512, 1, _stream())
+                               2048, 1, _stream())
     assert st == L.PA_ERR_UNSUPPORTED
     assert b"static scratch" in lib.pa_last_error()
