@@ -24,21 +24,24 @@
 // while the current one is reduced (cf-1.com 5.1 and 6.2: prefetch the next
 // physical block).
 //
-// Two inner loops, three kernels:
-//  * pa_decode_valu (one query head per KV head, and float32): q.k is a
-//    per-lane partial dot product finished by a DPP butterfly over the lanes
-//    that hold one K row; each lane keeps an online softmax over its rows and
-//    accumulates P.V with FMAs.
-//  * pa_decode_mfma (bfloat16/float16 with 2..16 query heads per KV head):
-//    the heads sharing a KV head form a real small dense product. Per 16-token
+// Two inner loops, four kernels:
+//  * pa_decode_valu (float32, and one query head per KV head where the
+//    stream split below does not run): q.k is a per-lane partial dot product
+//    finished by a DPP butterfly over the lanes that hold one K row; each
+//    lane keeps an online softmax over its rows and accumulates P.V with FMAs.
+//  * the MFMA tile code (bfloat16/float16): the heads sharing a KV head form
+//    a small dense product (one distinct column with one head). Per 16-token
 //    tile, S^T = K Q^T is D/32 v_mfma_f32_16x16x32 (K rows as A, the group's
 //    query rows as B columns), and O^T += V^T P^T is D/16 v_mfma_f32_16x16x16
 //    whose B operand is exactly the lane layout of S^T after exp2, so P never
 //    leaves registers. The softmax max is rescaled lazily (only when a tile's
-//    max exceeds the running max by more than 2^8). pa_decode_mfma_wave runs
-//    the same tile code with one item per wave, for partitions of at most
-//    kWaveSlice blocks; pa_decode_mfma shares an item among the workgroup's
-//    waves, for longer partitions.
+//    max exceeds the running max by more than 2^8). pa_decode_stream deals
+//    the batch's 16-key tiles evenly over a persistent grid's waves, each
+//    merging the partitions of its stretch in registers (partitions of at
+//    most kWaveSlice blocks, any group and block size); pa_decode_mfma_wave
+//    runs the same tile code with one item per wave where the stream's
+//    32-bit cost positions could overflow; pa_decode_mfma shares an item
+//    among the workgroup's waves, for longer partitions.
 // Lanes, then (workgroup items) waves through LDS, are merged by the
 // log-sum-exp rule.
 // A sequence that fits one partition is written straight to `out`; longer

@@ -49,8 +49,7 @@ def test_status_strings_and_workspace_size():
     assert lib.pa_status_string(3) == b"workspace missing or too small"
     dp = lib.pa_default_partition_size
     F32, BF16, F16 = 0, 1, 2
-    # workgroup items (float32, or one query head per KV head with blocks of
-    # fewer than 16 tokens): 256 blocks, halved while the batch has < 512
+    # workgroup items (float32): 256 blocks, halved while the batch has < 512
     # items, not below 512 tokens
     assert dp(64, 32, 32, 4096, 16, F32) == 4096      # 2048 pairs, one partition each
     assert dp(256, 8, 8, 8192, 16, F32) == 4096
@@ -86,7 +85,7 @@ def test_status_strings_and_workspace_size():
     assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 512, F32) == expect
     # the default resolves as pa_default_partition_size does: 4 x 2 pairs, 1100 tokens -> 512
     assert lib.pa_decode_workspace_size(4, 8, 2, 128, 1100, 16, 0, F32) == expect
-    # grouped 16-bit heads with blocks of 16 or more run the stream split: no
+    # 16-bit elements run the stream split: no
     # per-partition records; per wave of the grid's 1024, a tail and a head
     # record of every query head of a group and four ints naming the pair
     # of the tail record, whatever the batch and the partition
