@@ -181,12 +181,14 @@ def test_block_sizes_wide_rows(bs, dt, d):
     compare_attention(out, run_oracle(c, 0.1), f"{dt} D{d} bs {bs}")
 
 
-def test_permutation_invariance_bitwise():
+@pytest.mark.parametrize("bs,hq,hkv", [(16, 32, 8), (8, 32, 8), (4, 8, 8)])
+def test_permutation_invariance_bitwise(bs, hq, hkv):
     """Moving every block to another physical id (tables rewritten to match)
     gives bit-identical outputs: the reduction order depends only on logical
-    positions."""
+    positions. Blocks of 16 (wave-uniform bases), of 8 and 4 (each lane's own
+    block ids; one query head per KV head at 4)."""
     lens = [5, 400, 1030, 3000]
-    c = make_case(lens, 32, 8, 128, 16, torch.bfloat16, seed=7)
+    c = make_case(lens, hq, hkv, 128, bs, torch.bfloat16, seed=7 + bs)
     base = run_gpu(c, 0.09)
     nb = c["kc"].shape[0]
     perm = np.random.default_rng(8).permutation(nb)
