@@ -632,13 +632,16 @@ def main():
     ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_context_len,
                             w.block_size, w.partition_size, q.dtype, device=dev)
     dargs = (out, q, kc, vc, tables, lens, w.scale, w.max_context_len, w.partition_size, ws)
+    # a batch whose tables share blocks tells the library so (pa_decode_ex,
+    # PA_DECODE_SHARED_BLOCKS): the same results, tiles kept in the L2
+    hint = {"shared_blocks": True} if w.refcount_max > 1 else {}
 
     def step():
         if len(w.cow_pairs):
             pa.copy_blocks(kc, vc, pairs)
         for sl, (k, v) in zip(slots, vals["writes"]):
             pa.write_cache(k, v, kc, vc, sl)
-        pa.decode_partitions(*dargs)
+        pa.decode_partitions(*dargs, **hint)
         pa.decode_merge(*dargs)
 
     progress(f"warmup {args.warmup} steps, at least {WARMUP_MIN_S} s")
@@ -660,7 +663,7 @@ def main():
     ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ka.record()
     for _ in range(args.steps):
-        pa.decode_partitions(*dargs)
+        pa.decode_partitions(*dargs, **hint)
     kb.record()
     torch.cuda.synchronize()
     part_us = 1e3 * ka.elapsed_time(kb) / args.steps
@@ -705,8 +708,8 @@ def main():
     # pa_decode (partition kernel + merge) and the partition kernel alone.
     calls = max(50, args.steps)
     per_call = {"calls": calls, "warmup": 10,
-                "decode_us": per_call_us(lambda: pa.decode(*dargs), calls),
-                "partition_us": per_call_us(lambda: pa.decode_partitions(*dargs), calls),
+                "decode_us": per_call_us(lambda: pa.decode(*dargs, **hint), calls),
+                "partition_us": per_call_us(lambda: pa.decode_partitions(*dargs, **hint), calls),
                 "timing": "each call between two HIP events on the launch stream (an event pair adds a few us "
                           "of queue time around the kernel)"}
     progress(f"per call: decode {per_call['decode_us']}, partition kernel {per_call['partition_us']}")
@@ -780,7 +783,7 @@ def main():
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "partition_size": resolved_partition(w), "ctx": w.ctx_recipe, "tokens": int(w.context_lens.sum()), "tail_waste": round(W.tail_waste(w), 5),
-                   "kv_bytes": kv, "seed": w.seed,
+                   "kv_bytes": kv, "seed": w.seed, "decode_flags": "shared_blocks" if hint else "none",
                    "parallelism": "none (1 GPU)" if args.tp == 1 else
                    f"one GPU's shard of a {args.tp}-way split by KV head (no exchange needed)"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),

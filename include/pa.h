@@ -3,7 +3,8 @@
  *
  * Device operations, each enqueued on the caller's HIP stream:
  *   pa_decode       single-query attention of every sequence over its KV
- *                   cache, read through its block table;
+ *                   cache, read through its block table (pa_decode_ex: with
+ *                   a hint that the batch shares blocks);
  *   pa_prefill      attention of several new tokens per sequence, each over
  *                   the cached tokens up to its own position;
  *   pa_write_cache  write each new token's K and V rows into the slot given by
@@ -74,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 9
+#define PA_ABI_VERSION 10
 
 typedef enum pa_dtype {
     PA_F32 = 0,  /* IEEE binary32 */
@@ -254,6 +255,34 @@ pa_status_t pa_decode_merge(void* out, const void* q, const void* k_cache, const
                             int max_blocks_per_seq, int max_context_len, int partition_size,
                             pa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * pa_decode and pa_decode_partitions with flags; flags = 0 is the plain
+ * call. PA_DECODE_SHARED_BLOCKS tells the library that some physical blocks
+ * appear in several sequences' tables (prefix sharing, [aiqz] section
+ * 前缀共享机制): the stream split then reads K/V tiles of blocks of 16 or
+ * more tokens with ordinary loads, which the L2 keeps for the other
+ * sequences that list the same blocks, instead of nontemporal (streaming)
+ * loads. Results are bit for bit those of the plain call; only the load
+ * policy changes. Without sharing the hint is slower (streaming loads suit a
+ * batch read once), so pass it only for batches that share. The item
+ * kernels ignore it. Unknown flag bits return PA_ERR_INVALID_ARG before any
+ * launch.
+ */
+#define PA_DECODE_SHARED_BLOCKS 1u
+pa_status_t pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, float scale,
+                         int block_size, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                         int num_blocks, int max_blocks_per_seq, int max_context_len,
+                         int partition_size, pa_dtype_t dtype, void* workspace,
+                         size_t workspace_bytes, unsigned flags, void* stream);
+pa_status_t pa_decode_partitions_ex(void* out, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, float scale, int block_size,
+                                    int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                    int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                    int partition_size, pa_dtype_t dtype, void* workspace,
+                                    size_t workspace_bytes, unsigned flags, void* stream);
 
 /*
  * pa_decode for callers that cannot allocate: code under HIP graph capture,

@@ -230,15 +230,21 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
 
 
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len=None,
-           partition_size=0, workspace=None):
+           partition_size=0, workspace=None, shared_blocks=False):
     """Paged decode attention into ``out`` (see ``pa_decode`` in include/pa.h).
 
     ``max_context_len`` should be passed by callers that know it; when None it
-    is read from the device, which synchronizes the stream.
+    is read from the device, which synchronizes the stream. ``shared_blocks``
+    is the hint that some physical blocks appear in several tables
+    (``pa_decode_ex`` with PA_DECODE_SHARED_BLOCKS): the same results, read
+    through the L2 for the other sharers.
     """
     args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                         max_context_len, partition_size, workspace)
-    _check(library().pa_decode(*args))
+    if shared_blocks:
+        _check(library().pa_decode_ex(*args[:-1], _lib.PA_DECODE_SHARED_BLOCKS, args[-1]))
+    else:
+        _check(library().pa_decode(*args))
     return out
 
 
@@ -273,11 +279,15 @@ def decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, 
 
 
 def decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                      max_context_len, partition_size=0, workspace=None):
-    """First stage of ``decode`` (partition kernel) on the current stream."""
+                      max_context_len, partition_size=0, workspace=None, shared_blocks=False):
+    """First stage of ``decode`` (partition kernel) on the current stream;
+    ``shared_blocks`` as in ``decode``."""
     args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                         max_context_len, partition_size, workspace)
-    _check(library().pa_decode_partitions(*args))
+    if shared_blocks:
+        _check(library().pa_decode_partitions_ex(*args[:-1], _lib.PA_DECODE_SHARED_BLOCKS, args[-1]))
+    else:
+        _check(library().pa_decode_partitions(*args))
 
 
 def decode_merge(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,

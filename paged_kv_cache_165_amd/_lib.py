@@ -18,7 +18,8 @@ PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 PA_OK = 0
 PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_BLOCKS = 1, 2, 3, 4, 5
 PA_DECODE_VALU, PA_DECODE_MFMA, PA_DECODE_MFMA_WAVE, PA_DECODE_MFMA_STREAM = 0, 1, 2, 3
-ABI_VERSION = 9
+PA_DECODE_SHARED_BLOCKS = 1  # pa_decode_ex flag
+ABI_VERSION = 10
 NOALLOC_SCRATCH_BYTES = 32 << 20  # PA_NOALLOC_SCRATCH_BYTES
 
 
@@ -31,7 +32,7 @@ class DecodePlan(ctypes.Structure):
 EXPORTED = (
     "pa_abi_version", "pa_status_string", "pa_last_error", "pa_default_partition_size",
     "pa_decode_workspace_size", "pa_decode_plan", "pa_decode", "pa_decode_partitions", "pa_decode_merge",
-    "pa_decode_noalloc",
+    "pa_decode_ex", "pa_decode_partitions_ex", "pa_decode_noalloc",
     "pa_prefill", "pa_write_cache", "pa_copy_blocks", "pa_write_cache_layers", "pa_copy_blocks_layers",
     "pa_append_block_tables", "pa_append_block_tables_host", "pa_write_cache_append_host",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_prefill", "pa_bm_share", "pa_bm_append", "pa_bm_free",
@@ -78,6 +79,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             f = getattr(lib, name)
             f.restype = _i
             f.argtypes = _DECODE_ARGS
+        for name in ("pa_decode_ex", "pa_decode_partitions_ex"):
+            f = getattr(lib, name)
+            f.restype = _i
+            f.argtypes = _DECODE_ARGS[:19] + [ctypes.c_uint, _vp]
         lib.pa_decode_noalloc.restype = _i
         lib.pa_decode_noalloc.argtypes = _DECODE_ARGS[:17] + [_vp]
         lib.pa_prefill.restype = _i

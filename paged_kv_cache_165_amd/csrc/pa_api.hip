@@ -290,6 +290,7 @@ pa_status_t prepare_decode(void* out, const void* q, const void* k_cache, const 
     p->ws_xl = stream && ws.total ? reinterpret_cast<float*>(wsb + ws.xl_off) : nullptr;
     p->ws_xo = stream && ws.total ? reinterpret_cast<float*>(wsb + ws.xo_off) : nullptr;
     p->stream = stream ? 1 : 0;
+    p->keep_tiles = 0;
     p->scale_log2 = scale * 1.4426950408889634f;
     p->num_seqs = num_seqs;
     p->num_heads = num_heads;
@@ -432,15 +433,28 @@ pa_status_t pa_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int he
         num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len, partition_size,  \
         dtype, workspace, workspace_bytes
 
-pa_status_t pa_decode_partitions(void* out, const void* q, const void* k_cache,
-                                 const void* v_cache, const int32_t* block_tables,
-                                 const int32_t* context_lens, float scale, int block_size,
-                                 int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                                 int num_blocks, int max_blocks_per_seq, int max_context_len,
-                                 int partition_size, pa_dtype_t dtype, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+namespace {
+
+pa_status_t apply_decode_flags(unsigned flags, pa::DecodeParams* p) {
+    if (flags & ~static_cast<unsigned>(PA_DECODE_SHARED_BLOCKS))
+        return fail(PA_ERR_INVALID_ARG, "unknown decode flags 0x%x", flags & ~static_cast<unsigned>(PA_DECODE_SHARED_BLOCKS));
+    p->keep_tiles = (flags & PA_DECODE_SHARED_BLOCKS) ? 1 : 0;
+    return PA_OK;
+}
+
+}  // namespace
+
+pa_status_t pa_decode_partitions_ex(void* out, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, float scale, int block_size,
+                                    int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                    int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                    int partition_size, pa_dtype_t dtype, void* workspace,
+                                    size_t workspace_bytes, unsigned flags, void* stream) {
     pa::DecodeParams p;
     pa_status_t st = prepare_decode(PA_DECODE_ARGS, &p);
+    if (st != PA_OK) return st;
+    st = apply_decode_flags(flags, &p);
     if (st != PA_OK) return st;
     if (num_seqs == 0) return PA_OK;
     pa::DeviceInfo dv;
@@ -451,6 +465,16 @@ pa_status_t pa_decode_partitions(void* out, const void* q, const void* k_cache,
         return lds_fail(num_seqs, head_dim, num_heads / num_kv_heads, dv.lds_per_cu, dv.lds_per_wg);
     if (e != hipSuccess) return hip_fail(e, "decode partition kernel launch");
     return PA_OK;
+}
+
+pa_status_t pa_decode_partitions(void* out, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, float scale, int block_size,
+                                 int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                 int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                 int partition_size, pa_dtype_t dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return pa_decode_partitions_ex(PA_DECODE_ARGS, 0u, stream);
 }
 
 pa_status_t pa_decode_merge(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -469,14 +493,16 @@ pa_status_t pa_decode_merge(void* out, const void* q, const void* k_cache, const
     return PA_OK;
 }
 
-pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* block_tables, const int32_t* context_lens, float scale,
-                      int block_size, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                      int num_blocks, int max_blocks_per_seq, int max_context_len,
-                      int partition_size, pa_dtype_t dtype, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+pa_status_t pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, float scale,
+                         int block_size, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                         int num_blocks, int max_blocks_per_seq, int max_context_len,
+                         int partition_size, pa_dtype_t dtype, void* workspace,
+                         size_t workspace_bytes, unsigned flags, void* stream) {
     pa::DecodeParams p;
     pa_status_t st = prepare_decode(PA_DECODE_ARGS, &p);
+    if (st != PA_OK) return st;
+    st = apply_decode_flags(flags, &p);
     if (st != PA_OK) return st;
     if (num_seqs == 0) return PA_OK;
     pa::DeviceInfo dv;
@@ -490,6 +516,15 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void*
     e = pa::launch_decode_merge(p, dtype, head_dim, s);
     if (e != hipSuccess) return hip_fail(e, "decode merge kernel launch");
     return PA_OK;
+}
+
+pa_status_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int block_size, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                      int num_blocks, int max_blocks_per_seq, int max_context_len,
+                      int partition_size, pa_dtype_t dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    return pa_decode_ex(PA_DECODE_ARGS, 0u, stream);
 }
 
 pa_status_t pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,

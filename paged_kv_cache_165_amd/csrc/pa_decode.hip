@@ -1473,7 +1473,11 @@ __device__ __forceinline__ void stream_list_end(const DecodeParams& p, int w, bo
         *reinterpret_cast<int4*>(p.ws_meta + 4 * static_cast<size_t>(x)) = make_int4(0, 0, 0, 0);
 }
 
-template <int DT, int D, int G, bool BIGB>
+// KEEP: K/V tiles are read with ordinary loads instead of nontemporal ones,
+// so that the L2 keeps them for the other sequences that list the same
+// blocks (a caller's hint that the batch shares blocks; blocks of 16 or more
+// tokens). Streaming loads are faster when nothing is shared.
+template <int DT, int D, int G, bool BIGB, bool KEEP = false>
 __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
     static_assert(DT == PA_BF16 || DT == PA_F16, "MFMA path is for 16-bit elements");
     static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
@@ -1552,10 +1556,17 @@ __global__ __launch_bounds__(kThreads) void pa_decode_stream(DecodeParams p) {
             const char* vtp = vbase + (tile_el + static_cast<size_t>((tt0 & (bs - 1)) >> 4) * D * 16) * E;
             const uint32_t ko = static_cast<uint32_t>(((krow & (bs - 1)) * D + 8 * j) * E);
             const uint32_t vo = static_cast<uint32_t>(((vtok & 15) + 16 * r16) * E);
+            if constexpr (KEEP) {
 #pragma unroll
-            for (int c = 0; c < NK; ++c) b.k[c] = nt_load<u32x4>(kt, ko + 64 * c);
+                for (int c = 0; c < NK; ++c) b.k[c] = *reinterpret_cast<const u32x4*>(kt + ko + 64 * c);
 #pragma unroll
-            for (int v = 0; v < NV; ++v) b.v[v] = nt_load<u32x2>(vtp, vo + 512 * v);
+                for (int v = 0; v < NV; ++v) b.v[v] = *reinterpret_cast<const u32x2*>(vtp + vo + 512 * v);
+            } else {
+#pragma unroll
+                for (int c = 0; c < NK; ++c) b.k[c] = nt_load<u32x4>(kt, ko + 64 * c);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) b.v[v] = nt_load<u32x2>(vtp, vo + 512 * v);
+            }
         } else {
             const int vt = 1 << p.log2_vt;
             const size_t kel = (static_cast<size_t>(pk) * hkv + x.kv) * blk_el +
@@ -2098,7 +2109,8 @@ hipError_t launch_mfma(const DecodeParams& p, const DeviceInfo& dv, hipStream_t 
     const bool big = (1 << p.log2_bs) >= 16;
     void (*kern)(DecodeParams);
     if (pl.kernel == PA_DECODE_MFMA_STREAM)
-        kern = big ? pa_decode_stream<DT, D, G, true> : pa_decode_stream<DT, D, G, false>;
+        kern = !big ? pa_decode_stream<DT, D, G, false>
+                    : (p.keep_tiles ? pa_decode_stream<DT, D, G, true, true> : pa_decode_stream<DT, D, G, true>);
     else if (pl.kernel == PA_DECODE_MFMA_WAVE)
         kern = big ? pa_decode_mfma_wave<DT, D, G, true> : pa_decode_mfma_wave<DT, D, G, false>;
     else
@@ -2116,8 +2128,10 @@ hipError_t launch_stream_only(const DecodeParams& p, const DeviceInfo& dv, hipSt
                     dv.lds_per_wg, kMfmaWgPerCu, &pl) != PA_OK || pl.kernel != PA_DECODE_MFMA_STREAM)
         return hipErrorInvalidConfiguration;
     const bool big = (1 << p.log2_bs) >= 16;
-    return run_planned(big ? pa_decode_stream<DT, D, G, true> : pa_decode_stream<DT, D, G, false>, p, pl, dv,
-                       stream);
+    void (*kern)(DecodeParams) = !big ? pa_decode_stream<DT, D, G, false>
+                                      : (p.keep_tiles ? pa_decode_stream<DT, D, G, true, true>
+                                                      : pa_decode_stream<DT, D, G, true>);
+    return run_planned(kern, p, pl, dv, stream);
 }
 
 template <int DT, int D>

@@ -56,6 +56,8 @@ struct DecodeParams {
     int log2_bs;        // block size = 1 << log2_bs
     int log2_vt;        // tokens per transposed V tile = min(block size, 16)
     int ring_slots;     // item results a workgroup buffers in LDS before storing them
+    int keep_tiles;     // 1: the stream kernel reads K/V tiles with ordinary loads, which the L2 keeps for
+                        //   other readers of shared blocks; 0: nontemporal (streaming) loads
 };
 
 // Everything one prefill launch needs. Pointers are device pointers.

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(L.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 9
+    assert lib.pa_abi_version() == 10
 
 
 def test_status_strings_and_workspace_size():
@@ -140,6 +140,22 @@ def test_decode_rejects_before_launch(over, status, msg):
     lib, _ = _lib()
     assert _decode(lib, **over) == status
     assert msg in lib.pa_last_error()
+
+
+@pytest.mark.parametrize("name", ["pa_decode_ex", "pa_decode_partitions_ex"])
+@pytest.mark.parametrize("flags", [2, 0x80000000, 3])
+def test_decode_ex_rejects_unknown_flags_before_launch(name, flags):
+    """Only PA_DECODE_SHARED_BLOCKS is defined: any other bit is refused
+    after the shape checks and before a launch (the pointers here are never
+    dereferenced), and so is a malformed shape whatever the flags."""
+    lib, L = _lib()
+    f = getattr(lib, name)
+    a = (16, 32, 48, 64, 80, 96, 0.1, 16, 2, 8, 2, 128, 10, 4, 64, 0, 1, 128, 1 << 30)
+    assert f(*a, flags, None) == L.PA_ERR_INVALID_ARG
+    assert b"unknown decode flags" in lib.pa_last_error()
+    bad = a[:9] + (7,) + a[10:]      # 7 query heads over 2 KV heads
+    assert f(*bad, L.PA_DECODE_SHARED_BLOCKS, None) == L.PA_ERR_INVALID_ARG
+    assert b"multiple of num_kv_heads" in lib.pa_last_error()
 
 
 def test_decode_empty_batch_is_noop():

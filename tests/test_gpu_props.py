@@ -199,6 +199,33 @@ def test_permutation_invariance_bitwise(bs, hq, hkv):
     assert torch.equal(base.view(torch.int16), out2.view(torch.int16))
 
 
+@pytest.mark.parametrize("bs,g", [(16, 4), (32, 1), (8, 4)])
+def test_shared_blocks_hint_changes_nothing_but_the_loads(bs, g):
+    """decode with the shared-blocks hint (pa_decode_ex) equals the plain
+    call bit for bit, on sequences whose tables share a prefix (four samples
+    of each of three prompts) and on blocks of 8, where the hint is ignored."""
+    pa = _pa()
+    hkv = 4
+    lens = [900, 1300, 700, 2000, 1000, 800]
+    c = make_case(lens, hkv * g, hkv, 128, bs, torch.bfloat16, seed=31 + bs + g, trap_nan=False)
+    tables = c["tables"].copy()
+    share = 512 // bs
+    for i in range(len(lens)):                  # sequence i shares its first 512 tokens with sequence i % 2
+        tables[i, :share] = c["tables"][i % 2, :share]
+    q = c["q"]
+    t_d = torch.from_numpy(tables).to(DEV)
+    l_d = torch.from_numpy(c["lens"]).to(DEV)
+    mc = int(c["lens"].max())
+    plain = torch.empty_like(q)
+    hinted = torch.empty_like(q)
+    pa.decode(plain, q, c["kc"], c["vc"], t_d, l_d, 0.08, max_context_len=mc)
+    pa.decode(hinted, q, c["kc"], c["vc"], t_d, l_d, 0.08, max_context_len=mc, shared_blocks=True)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), hinted.view(torch.int16))
+    c2 = dict(c, tables=tables)
+    compare_attention(hinted, run_oracle(c2, 0.08), f"shared-blocks hint bs {bs} g {g}")
+
+
 def test_shared_blocks_equal_copied_blocks_bitwise():
     """Sequences whose tables share prefix blocks (reference count 3) and a
     sequence reading copies of those blocks made by pa_copy_blocks give the
