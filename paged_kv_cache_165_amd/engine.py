@@ -90,6 +90,7 @@ class PagedDecoder:
         self._rows = None     # int64 sequence ids of those rows, or None once any table may differ
         self._lens = None     # host copy of the rows' context lengths
         self._pending = None  # a begun step whose table append waits for its first cache write
+        self._shared = False  # a fork has happened: tables may list the same blocks (decode hint)
 
     # -- host -> device -----------------------------------------------------
     def _dev(self, a: np.ndarray) -> torch.Tensor:
@@ -153,6 +154,7 @@ class PagedDecoder:
         ``parent``'s blocks."""
         n = self.blocks.seq_tokens(parent) if num_tokens is None else int(num_tokens)
         self.blocks.share(child, parent, n)
+        self._shared = self._shared or n > 0
         self._rows = None
 
     def free(self, seq: int) -> None:
@@ -275,7 +277,7 @@ class PagedDecoder:
             out = torch.empty_like(q)
         self._pa.decode(out, q, kc, vc, step.d_tables, step.d_lens, scale,
                         max_context_len=step.max_ctx, partition_size=self.partition_size,
-                        workspace=self._workspace_for(step.n, step.max_ctx))
+                        workspace=self._workspace_for(step.n, step.max_ctx), shared_blocks=self._shared)
         return out
 
     def step(self, seqs, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
